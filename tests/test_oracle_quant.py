@@ -1,0 +1,102 @@
+"""Pins of the oracle's block-uniform and KIVI-style quantizers.
+
+"Codec-Gauge" (arXiv HTML, evaluation-protocol paragraph): block-uniform
+uses one range per T_b x d_l block; the KIVI-style path uses per-channel key
+ranges and per-token value ranges; both use the same bit settings.  Group
+size 32 and a 128-token full-precision tail come from the KIVI-style workload
+this build measures.  Pins: brute-force optimal level, exact endpoints,
+half-step error bound, independent min/max grouping, LSB-first packing.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from fixed_rate_compression_amd import synth
+
+
+def _check_group(vals, codes, mn, scale, bits):
+    L = (1 << bits) - 1
+    vals = np.asarray(vals, np.float32)
+    assert mn == vals.min()
+    if vals.max() == vals.min():
+        assert scale == 0 and np.all(codes == 0)
+        return
+    assert scale == np.float32(np.float32(vals.max() - vals.min()) / np.float32(L))
+    for x, q in zip(vals, codes):
+        xhat = np.float32(mn + np.float32(np.float32(q) * scale))
+        # brute force over all levels, exact arithmetic
+        dist = [abs(Fraction(float(x)) - (Fraction(float(mn)) + k * Fraction(float(scale))))
+                for k in range(L + 1)]
+        best = min(dist)
+        # optimal up to the fp32 rounding of (x - mn) * inv
+        assert dist[q] - best <= Fraction(float(scale)) * Fraction(1, 2 ** 18) + Fraction(2) ** -140
+        assert abs(float(xhat) - float(x)) <= float(scale) * (0.5 + 2 ** -18) + 2 * np.spacing(np.float32(abs(x) + abs(mn)))
+    assert codes[np.argmin(vals)] == 0
+    assert codes[np.argmax(vals)] == L
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
+def test_block_uniform_bruteforce(bits):
+    Bt, d, T = 4, 8, 16
+    x = (np.random.default_rng(bits).standard_normal((T, d)) * 3).astype(np.float32)
+    payload, meta = oracle.bu_encode_field(x, Bt, bits)
+    assert payload.size == T * d * bits // 8 and meta.shape == (T // Bt, 2)
+    codes = oracle.unpack_codes(payload, T * d, bits).reshape(T // Bt, Bt * d)
+    for m in range(T // Bt):
+        _check_group(x[m * Bt:(m + 1) * Bt].reshape(-1), codes[m], meta[m, 0], meta[m, 1], bits)
+    y = oracle.bu_decode_field(payload, meta, T, d, Bt, bits)
+    for m in range(T // Bt):
+        blk = slice(m * Bt, (m + 1) * Bt)
+        assert np.min(y[blk]) == np.min(x[blk])                  # x_hat(mn) = mn
+        assert np.max(np.abs(y[blk] - x[blk])) <= meta[m, 1] * 0.5001 + 1e-6
+
+
+def test_constant_block_and_packing_order():
+    # codes 0..15 in token-major order pack as LSB-first nibbles 0x10, 0x32, ...
+    d, Bt, bits = 16, 1, 4
+    x = np.arange(16, dtype=np.float32)[None, :]
+    payload, meta = oracle.bu_encode_field(x, Bt, bits)
+    assert list(payload) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    assert meta[0, 0] == 0.0 and meta[0, 1] == 1.0
+    c = np.full((2, 16), 2.5, np.float32)
+    p2, m2 = oracle.bu_encode_field(c, 2, 3)
+    assert np.all(p2 == 0) and m2[0, 0] == 2.5 and m2[0, 1] == 0.0
+    assert np.array_equal(oracle.bu_decode_field(p2, m2, 2, 16, 2, 3), c)
+
+
+def test_tiny_range_does_not_overflow():
+    x = np.array([[1e-45, 0.0, 1e-45, 0.0]], np.float32)
+    payload, meta = oracle.bu_encode_field(x, 1, 4)
+    y = oracle.bu_decode_field(payload, meta, 1, 4, 1, 4)
+    assert np.all(np.isfinite(y)) and np.max(np.abs(y - x)) <= 1e-45
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_kivi_grouping_and_tail(kind, bits):
+    T, d, group, residual = 192, 128, 32, 128
+    x = synth.kv_field_cpu(3, kind, T, d, 0.95, 4)
+    payload, meta, tail = oracle.kivi_encode_field(x, kind, group, bits, residual)
+    Tq = T - residual
+    assert np.array_equal(tail, x[Tq:])
+    codes = oracle.unpack_codes(payload, Tq * d, bits).reshape(Tq, d)
+    # metadata: 8 bytes per `group` quantized values
+    assert meta.nbytes == 8 * Tq * d // group
+    if kind == 0:      # keys: one range per channel per 32 tokens
+        mm = meta.reshape(Tq // group, d, 2)
+        for tg in range(Tq // group):
+            for c in range(0, d, 7):
+                vals = x[tg * group:(tg + 1) * group, c]
+                _check_group(vals, codes[tg * group:(tg + 1) * group, c], mm[tg, c, 0], mm[tg, c, 1], bits)
+        assert np.array_equal(mm[..., 0], x[:Tq].reshape(Tq // group, group, d).min(axis=1))
+    else:              # values: one range per token per 32 channels
+        mm = meta.reshape(Tq, d // group, 2)
+        for t in range(0, Tq, 5):
+            for cg in range(d // group):
+                vals = x[t, cg * group:(cg + 1) * group]
+                _check_group(vals, codes[t, cg * group:(cg + 1) * group], mm[t, cg, 0], mm[t, cg, 1], bits)
+        assert np.array_equal(mm[..., 0], x[:Tq].reshape(Tq, d // group, group).min(axis=2))
+    y = oracle.kivi_decode_field(payload, meta, tail, T, d, kind, group, bits, residual)
+    assert np.array_equal(y[Tq:], x[Tq:])

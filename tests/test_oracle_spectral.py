@@ -1,0 +1,116 @@
+"""Pins of the oracle's token-channel DCT statistics and gradient.
+
+"Codec-Gauge" (arXiv HTML, frequency-objective paragraphs): orthonormal 2D
+DCT of each T_b x d_l block of X' = G X; energy E = U^2; spectral centroid
+over a normalized radius; smooth log-amplitude rate proxy with tau = 0.04;
+the gauge and DCT are energy preserving.  Pins: scipy's independent DCT,
+Parseval, closed-form blocks, gauge invariance of the energy, and central
+finite differences of the whole objective w.r.t. A.
+"""
+import numpy as np
+import pytest
+import scipy.fft
+
+import oracle
+from oracle import spectral
+from fixed_rate_compression_amd import synth
+
+
+@pytest.mark.parametrize("N", [4, 16, 128])
+def test_dct_matrix_matches_scipy(N):
+    C = spectral.dct_matrix(N)
+    ref = scipy.fft.dct(np.eye(N), type=2, norm="ortho", axis=0)
+    assert np.max(np.abs(C - ref)) < 1e-14
+    assert np.max(np.abs(C @ C.T - np.eye(N))) < 1e-13
+
+
+def test_block_dct_matches_scipy_dctn_and_parseval():
+    x = synth.kv_field_cpu(5, 0, 64, 128, 0.95, 4).astype(np.float64)
+    blocks = x.reshape(4, 16, 128)
+    U = spectral.dct_matrix(16)[None] @ blocks @ spectral.dct_matrix(128).T[None]
+    for b in range(4):
+        ref = scipy.fft.dctn(blocks[b], type=2, norm="ortho")
+        assert np.max(np.abs(U[b] - ref)) < 1e-12 * np.max(np.abs(ref))
+    st = oracle.dct_stats_field(x, None, 0, grad=False)
+    assert abs(st["sum_E"] - np.sum(x * x)) < 1e-12 * np.sum(x * x)
+
+
+def test_radius_endpoints():
+    r = spectral.radius_matrix(16, 128)
+    assert r[0, 0] == 0.0 and abs(r[15, 127] - 1.0) < 1e-15
+    assert np.all((r >= 0) & (r <= 1.0 + 1e-15))
+
+
+def test_constant_block_centroid_zero():
+    x = np.full((32, 128), 1.7)
+    st = oracle.dct_stats_field(x, None, 0, grad=False)
+    assert np.all(np.abs(st["L_block"]) < 1e-14)
+
+
+@pytest.mark.parametrize("uv", [(0, 5), (3, 0), (7, 100), (15, 127)])
+def test_single_basis_image_centroid_is_its_radius(uv):
+    u, v = uv
+    Ct, Cd = spectral.dct_matrix(16), spectral.dct_matrix(128)
+    blk = 2.5 * np.outer(Ct[u], Cd[v])          # inverse DCT of a unit impulse
+    st = oracle.dct_stats_field(blk, None, 0, grad=False)
+    r = spectral.radius_matrix(16, 128)[u, v]
+    assert abs(st["L_block"][0] - r) < 1e-12
+
+
+def test_zero_field():
+    st = oracle.dct_stats_field(np.zeros((16, 128)), None, 0, grad=True)
+    assert st["L_rate"] == 0.0 and st["L_freq"] == 0.0 and st["L"] == 0.0
+
+
+def test_rate_proxy_closed_form():
+    # one DC-only block with U00 = c: L_rate = log(1 + |c|/tau) / (16*128)
+    c, tau = 3.0, 0.04
+    blk = np.full((16, 128), c / np.sqrt(16 * 128))
+    st = oracle.dct_stats_field(blk, None, 0, grad=False, tau=tau)
+    # (the other coefficients are DCT round-off, ~1e-17 each)
+    assert abs(st["L_rate"] - np.log1p(c / tau) / (16 * 128)) < 1e-11 * st["L_rate"]
+
+
+def test_centroid_range_and_gauge_energy_invariance():
+    rng = np.random.default_rng(2)
+    x = synth.kv_field_cpu(6, 0, 128, 128, 0.95, 4).astype(np.float64)
+    A = 0.1 * rng.standard_normal((8, 16, 16))
+    s0 = oracle.dct_stats_field(x, None, 0, grad=False)
+    s1 = oracle.dct_stats_field(x, A, 16, grad=False)
+    assert 0.0 <= s1["L_freq"] <= 1.0 and 0.0 <= s0["L_freq"] <= 1.0
+    assert abs(s0["sum_E"] - s1["sum_E"]) < 1e-11 * s0["sum_E"]
+    assert s0["L_freq"] != s1["L_freq"]
+
+
+def test_gradient_finite_differences():
+    rng = np.random.default_rng(3)
+    g, d, Tb, T = 4, 8, 4, 16
+    x = rng.standard_normal((T, d)) * np.exp(rng.standard_normal(d))
+    A = 0.2 * rng.standard_normal((d // g, g, g))
+    st = oracle.dct_stats_field(x, A, g, Tb=Tb, grad=True)
+    dA = st["dA"]
+    h = 1e-6
+    fd = np.zeros_like(A)
+    for idx in np.ndindex(*A.shape):
+        Ap = A.copy(); Ap[idx] += h
+        Am = A.copy(); Am[idx] -= h
+        fd[idx] = (oracle.dct_stats_field(x, Ap, g, Tb=Tb, grad=False)["L"] -
+                   oracle.dct_stats_field(x, Am, g, Tb=Tb, grad=False)["L"]) / (2 * h)
+    assert np.max(np.abs(dA - fd)) <= 1e-6 * np.max(np.abs(fd))
+    assert np.max(np.abs(dA + np.swapaxes(dA, -1, -2))) < 1e-15
+
+
+def test_gradient_wrt_gauge_finite_differences():
+    # dG alone (before the exp chain rule): perturb G entries directly
+    rng = np.random.default_rng(4)
+    g, d, Tb, T = 4, 8, 4, 8
+    x = rng.standard_normal((T, d))
+    G = oracle.gauge_from_skew(0.3 * rng.standard_normal((d // g, g, g)))
+    st = oracle.dct_stats_field(x, np.zeros((d // g, g, g)), g, Tb=Tb, grad=True, G=G)
+    h = 1e-6
+    for idx in [(0, 0, 0), (1, 2, 3), (0, 3, 1)]:
+        Gp = G.copy(); Gp[idx] += h
+        Gm = G.copy(); Gm[idx] -= h
+        fd = (oracle.dct_stats_field(x, None, g, Tb=Tb, grad=False, G=Gp)["L"] -
+              oracle.dct_stats_field(x, None, g, Tb=Tb, grad=False, G=Gm)["L"]) / (2 * h)
+        assert abs(st["dG"][idx] - fd) <= 1e-6 * max(1e-3, abs(fd))
