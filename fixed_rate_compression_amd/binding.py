@@ -1,0 +1,217 @@
+"""Thin ctypes binding of libcodecgauge.so (include/codec_gauge.h).
+
+Argument marshalling only: the functions keep the C names, take torch CUDA
+tensors (or numpy arrays for host arguments), pass raw pointers plus the
+current HIP stream, and raise on a negative return code.  All computation
+happens in the HIP library; if it is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libcodecgauge.so")
+
+CG_OK = 0
+CG_E_INVAL, CG_E_SHAPE, CG_E_UNSUPPORTED, CG_E_SIZE, CG_E_HIP, CG_E_INTERNAL = -1, -2, -3, -4, -5, -6
+CG_DTYPE_F32, CG_DTYPE_BF16 = 0, 1
+CG_BACKEND_NONE, CG_BACKEND_ZFP, CG_BACKEND_BLOCK_UNIFORM, CG_BACKEND_KIVI = 0, 1, 2, 3
+CG_HEADER_BYTES = 64
+
+EXPORTED = ["cg_encoded_bytes", "cg_encode", "cg_decode", "cg_roundtrip", "cg_gauge_fit_stats",
+            "cg_stats_workspace_bytes", "cg_gauge_from_skew", "cg_gauge_apply", "cg_write_header",
+            "cg_last_error"]
+
+
+class CgShape(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("kv", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("tokens", ctypes.c_int64),
+                ("token_capacity", ctypes.c_int64), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class CgGauge(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int32), ("G", ctypes.c_void_p)]
+
+
+class CgCodec(ctypes.Structure):
+    _fields_ = [("backend", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("block_tokens", ctypes.c_int32), ("residual_tokens", ctypes.c_int32)]
+
+
+class CgStats(ctypes.Structure):
+    _fields_ = [("L_freq", ctypes.c_double), ("L_rate", ctypes.c_double), ("L", ctypes.c_double),
+                ("sum_E", ctypes.c_double)]
+
+
+class CodecGaugeError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        # torch loads its bundled HIP runtime under the name "libamdhip64.so";
+        # importing it first lets this library's libamdhip64.so.7 dependency
+        # resolve (by soname) to that same runtime instead of a second copy
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+        SP, GP, CP = ctypes.POINTER(CgShape), ctypes.POINTER(CgGauge), ctypes.POINTER(CgCodec)
+        U64P = ctypes.POINTER(ctypes.c_uint64)
+        sig = {
+            "cg_encoded_bytes": [SP, CP, U64P, U64P, U64P],
+            "cg_encode": [SP, P, GP, CP, I64, I64, P, U64, P, U64, P],
+            "cg_decode": [SP, P, U64, P, U64, GP, CP, I64, I64, P, P],
+            "cg_roundtrip": [SP, P, GP, CP, P, U64, P, U64, P, P],
+            "cg_gauge_fit_stats": [SP, P, I32, P, I32, ctypes.c_float, ctypes.c_float,
+                                   ctypes.c_float, P, ctypes.c_size_t, P, P, P],
+            "cg_stats_workspace_bytes": [SP, I32, I32, ctypes.POINTER(ctypes.c_size_t)],
+            "cg_gauge_from_skew": [I64, I32, P, P],
+            "cg_gauge_apply": [SP, P, GP, I32, P, P],
+            "cg_write_header": [SP, CP, I32, I32, P, U64],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.cg_last_error.argtypes = []
+        L.cg_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(fn, rc):
+    if rc != CG_OK:
+        raise CodecGaugeError(fn, rc, lib().cg_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        assert t.flags["C_CONTIGUOUS"]
+        return t.ctypes.data
+    assert t.is_contiguous(), "tensors must be contiguous"
+    return t.data_ptr()
+
+
+def _nbytes(t):
+    if t is None:
+        return 0
+    if isinstance(t, np.ndarray):
+        return t.nbytes
+    return t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_shape(layers, kv, batch, heads, tokens, token_capacity=None, head_dim=128,
+               dtype=CG_DTYPE_BF16) -> CgShape:
+    return CgShape(layers, kv, batch, heads, tokens,
+                   tokens if token_capacity is None else token_capacity, head_dim, dtype)
+
+
+def make_gauge(group: int, G=None) -> CgGauge:
+    gg = CgGauge(group, _ptr(G) if G is not None else None)
+    gg._keep = G      # the struct holds a raw pointer: keep the tensor alive with it
+    return gg
+
+
+def make_codec(backend, bits=4, block_tokens=0, residual_tokens=0) -> CgCodec:
+    return CgCodec(backend, bits, block_tokens, residual_tokens)
+
+
+def cg_encoded_bytes(shape: CgShape, codec: CgCodec):
+    p, m, h = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    _check("cg_encoded_bytes", lib().cg_encoded_bytes(ctypes.byref(shape), ctypes.byref(codec),
+                                                      ctypes.byref(p), ctypes.byref(m),
+                                                      ctypes.byref(h)))
+    return p.value, m.value, h.value
+
+
+def cg_encode(shape, kv, gauge, codec, t0, nt, payload, meta=None, stream=None):
+    _check("cg_encode", lib().cg_encode(ctypes.byref(shape), _ptr(kv), ctypes.byref(gauge),
+                                        ctypes.byref(codec), t0, nt, _ptr(payload),
+                                        _nbytes(payload), _ptr(meta), _nbytes(meta),
+                                        _stream(stream)))
+
+
+def cg_decode(shape, payload, meta, gauge, codec, t0, nt, kv_out, stream=None):
+    _check("cg_decode", lib().cg_decode(ctypes.byref(shape), _ptr(payload), _nbytes(payload),
+                                        _ptr(meta), _nbytes(meta), ctypes.byref(gauge),
+                                        ctypes.byref(codec), t0, nt, _ptr(kv_out),
+                                        _stream(stream)))
+
+
+def cg_roundtrip(shape, kv_in, gauge, codec, payload, meta, kv_out, stream=None):
+    _check("cg_roundtrip", lib().cg_roundtrip(ctypes.byref(shape), _ptr(kv_in),
+                                              ctypes.byref(gauge), ctypes.byref(codec),
+                                              _ptr(payload), _nbytes(payload), _ptr(meta),
+                                              _nbytes(meta), _ptr(kv_out), _stream(stream)))
+
+
+def cg_gauge_apply(shape, kv, gauge, direction, out, stream=None):
+    _check("cg_gauge_apply", lib().cg_gauge_apply(ctypes.byref(shape), _ptr(kv),
+                                                  ctypes.byref(gauge), direction, _ptr(out),
+                                                  _stream(stream)))
+
+
+def cg_gauge_from_skew(A: np.ndarray) -> np.ndarray:
+    """A fp64 [n, g, g] (host) -> G = exp(A - A^T) fp32 [n, g, g] (host)."""
+    A = np.ascontiguousarray(A, np.float64)
+    n, g, _ = A.shape
+    G = np.empty((n, g, g), np.float32)
+    _check("cg_gauge_from_skew", lib().cg_gauge_from_skew(n, g, A.ctypes.data, G.ctypes.data))
+    return G
+
+
+def cg_stats_workspace_bytes(shape, g, T_b):
+    b = ctypes.c_size_t()
+    _check("cg_stats_workspace_bytes", lib().cg_stats_workspace_bytes(ctypes.byref(shape), g, T_b,
+                                                                      ctypes.byref(b)))
+    return b.value
+
+
+def cg_gauge_fit_stats(shape, kv, g, A_host: np.ndarray, T_b, tau, lambda_f, lambda_r, workspace,
+                       grad=True, stream=None):
+    """Returns (stats structured array [n_fields], dA fp64 or None)."""
+    nf = shape.layers * shape.kv * shape.batch * shape.heads
+    out = (CgStats * nf)()
+    A = np.ascontiguousarray(A_host, np.float64)
+    dA = np.zeros((nf, shape.head_dim // g, g, g), np.float64) if grad else None
+    _check("cg_gauge_fit_stats", lib().cg_gauge_fit_stats(
+        ctypes.byref(shape), _ptr(kv), g, A.ctypes.data, T_b, tau, lambda_f, lambda_r,
+        _ptr(workspace), _nbytes(workspace), ctypes.cast(out, ctypes.c_void_p),
+        dA.ctypes.data if grad else None, _stream(stream)))
+    stats = np.array([(o.L_freq, o.L_rate, o.L, o.sum_E) for o in out],
+                     dtype=[("L_freq", "f8"), ("L_rate", "f8"), ("L", "f8"), ("sum_E", "f8")])
+    return stats, dA
+
+
+def cg_write_header(shape, codec, layer, kv) -> bytes:
+    buf = ctypes.create_string_buffer(CG_HEADER_BYTES)
+    _check("cg_write_header", lib().cg_write_header(ctypes.byref(shape), ctypes.byref(codec),
+                                                    layer, kv, buf, CG_HEADER_BYTES))
+    return buf.raw
+
+
+def cg_last_error() -> str:
+    return lib().cg_last_error().decode()

@@ -1,0 +1,33 @@
+// Internal launch interface between the C ABI (codec_gauge_api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cgk {
+
+constexpr int TILE_T = 64;  // tokens per workgroup tile of the rows kernels
+
+// geometry of a rows launch over every field: one workgroup per
+// (field, 64-token tile) of rows [t0, t0 + nt)
+struct TileArgs {
+  int64_t tcap;   // token_capacity (row stride of a field)
+  int64_t t0;     // first row
+  int64_t nt;     // number of rows
+  int64_t grid;   // fields * tiles
+  int32_t tiles;  // tiles per field = ceil(nt / 64)
+  int32_t batch;  // B (gauges are shared across the batch)
+  int32_t heads;  // H
+  int32_t pad;
+};
+
+bool zfp_rate_built(int R);
+hipError_t zfp_encode_launch(int R, bool bf16, int g, const void *kv, const float *gauges,
+                             uint8_t *payload, const TileArgs &a, hipStream_t s);
+hipError_t zfp_decode_launch(int R, bool bf16, int g, const uint8_t *payload, const float *gauges,
+                             void *out, const TileArgs &a, hipStream_t s);
+hipError_t gauge_rows_launch(bool src_bf16, bool dst_bf16, bool inverse, int g, const void *src,
+                             const float *gauges, void *dst, const TileArgs &a, hipStream_t s);
+
+}  // namespace cgk

@@ -1,0 +1,23 @@
+// cg_gauge_apply for the dense (g = 128) gauge: the quantizers' MFMA routine
+// on the same 64-token tiles and 16-tile workgroup chunks.
+#include "quant_launch.hpp"
+
+namespace cgq {
+
+hipError_t gauge128_rows_launch(bool bf16, bool inverse, const void *kv, const float *gauges,
+                                float *out, int64_t tcap, int64_t tokens, int64_t fields, int batch,
+                                int heads, hipStream_t s) {
+  QuantArgs q = make_args(tcap, tokens, 0, tokens, fields, batch, heads, 0, 0, 0, 0, 1);
+  const QK a = make_qk(q, tiles_per_chunk(128));
+  const dim3 grid((unsigned)(fields * a.chunks)), block(NT);
+  if (bf16) {
+    if (inverse) hipLaunchKernelGGL((k_gauge128_rows<true, true>), grid, block, 0, s, kv, gauges, out, a);
+    else hipLaunchKernelGGL((k_gauge128_rows<true, false>), grid, block, 0, s, kv, gauges, out, a);
+  } else {
+    if (inverse) hipLaunchKernelGGL((k_gauge128_rows<false, true>), grid, block, 0, s, kv, gauges, out, a);
+    else hipLaunchKernelGGL((k_gauge128_rows<false, false>), grid, block, 0, s, kv, gauges, out, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cgq

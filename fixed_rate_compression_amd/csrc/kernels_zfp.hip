@@ -1,0 +1,101 @@
+// Dispatch of the fused zfp-style kernels (zfp_kernels.hpp) and of the
+// gauge-only rows kernel.  Each rate's kernels are instantiated in their own
+// translation unit (zfp_r<R>.hip) so the library builds in parallel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cg_launch.hpp"
+#include "cg_tile.hpp"
+
+namespace cgk {
+
+template <int R>
+hipError_t zfp_launch_rate(bool encode, bool bf16, int g, const void *src, const float *gauges,
+                           void *dst, const TileArgs &a, hipStream_t s);
+
+#define CG_ZFP_RATES(X) X(2) X(3) X(4) X(6) X(8)
+
+bool zfp_rate_built(int R) {
+  switch (R) {
+#define CASE(r) case r: return true;
+    CG_ZFP_RATES(CASE)
+#undef CASE
+  }
+  return false;
+}
+
+static hipError_t zfp_launch(int R, bool encode, bool bf16, int g, const void *src,
+                             const float *gauges, void *dst, const TileArgs &a, hipStream_t s) {
+  if (g != 0 && g != 16 && g != 32) return hipErrorInvalidValue;
+  switch (R) {
+#define CASE(r) case r: return zfp_launch_rate<r>(encode, bf16, g, src, gauges, dst, a, s);
+    CG_ZFP_RATES(CASE)
+#undef CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t zfp_encode_launch(int R, bool bf16, int g, const void *kv, const float *gauges,
+                             uint8_t *payload, const TileArgs &a, hipStream_t s) {
+  return zfp_launch(R, true, bf16, g, kv, gauges, payload, a, s);
+}
+
+hipError_t zfp_decode_launch(int R, bool bf16, int g, const uint8_t *payload, const float *gauges,
+                             void *out, const TileArgs &a, hipStream_t s) {
+  return zfp_launch(R, false, bf16, g, payload, gauges, out, a, s);
+}
+
+// Gauge-only rows kernel: storage (or fp32) rows -> gauge / inverse gauge ->
+// storage (or fp32) rows.  Backs the NONE backend and cg_gauge_apply.
+template <bool SRC_BF16, bool DST_BF16, int G, bool INV>
+__global__ __launch_bounds__(NT) void k_gauge_rows(const void *__restrict__ src,
+                                                   const float *__restrict__ gauges,
+                                                   void *__restrict__ dst, TileArgs a) {
+  __shared__ float xs[TILE_T * PITCH];
+  const int64_t field = (int64_t)blockIdx.x / a.tiles;
+  const int tile = (int)((int64_t)blockIdx.x % a.tiles);
+  const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
+  const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+  const int64_t row0 = field * a.tcap + tb;
+  load_tile<SRC_BF16>((const uint8_t *)src + (size_t)row0 * D * (SRC_BF16 ? 2 : 4), nrows, xs);
+  __syncthreads();
+  if constexpr (G != 0) {
+    gauge_tile<G, INV>(xs, nrows, gauges + gauge_index(field, a.batch, a.heads) * D * G);
+    __syncthreads();
+  }
+  store_tile<DST_BF16>((uint8_t *)dst + (size_t)row0 * D * (DST_BF16 ? 2 : 4), nrows, xs);
+}
+
+template <bool SB, bool DB, bool INV>
+static hipError_t gauge_rows_g(int g, const void *src, const float *gauges, void *dst,
+                               const TileArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)a.grid), block(NT);
+  switch (g) {
+    case 0:
+      hipLaunchKernelGGL((k_gauge_rows<SB, DB, 0, INV>), grid, block, 0, s, src, gauges, dst, a);
+      return hipGetLastError();
+    case 16:
+      hipLaunchKernelGGL((k_gauge_rows<SB, DB, 16, INV>), grid, block, 0, s, src, gauges, dst, a);
+      return hipGetLastError();
+    case 32:
+      hipLaunchKernelGGL((k_gauge_rows<SB, DB, 32, INV>), grid, block, 0, s, src, gauges, dst, a);
+      return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t gauge_rows_launch(bool src_bf16, bool dst_bf16, bool inverse, int g, const void *src,
+                             const float *gauges, void *dst, const TileArgs &a, hipStream_t s) {
+  if (inverse) {
+    if (src_bf16) return dst_bf16 ? gauge_rows_g<true, true, true>(g, src, gauges, dst, a, s)
+                                  : gauge_rows_g<true, false, true>(g, src, gauges, dst, a, s);
+    return dst_bf16 ? gauge_rows_g<false, true, true>(g, src, gauges, dst, a, s)
+                    : gauge_rows_g<false, false, true>(g, src, gauges, dst, a, s);
+  }
+  if (src_bf16) return dst_bf16 ? gauge_rows_g<true, true, false>(g, src, gauges, dst, a, s)
+                                : gauge_rows_g<true, false, false>(g, src, gauges, dst, a, s);
+  return dst_bf16 ? gauge_rows_g<false, true, false>(g, src, gauges, dst, a, s)
+                  : gauge_rows_g<false, false, false>(g, src, gauges, dst, a, s);
+}
+
+}  // namespace cgk

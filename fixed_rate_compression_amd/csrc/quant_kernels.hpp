@@ -1,0 +1,513 @@
+// Fused gauge + block-uniform / KIVI-style quantizers, and their decoders
+// ("Codec-Gauge", arXiv HTML, evaluation-protocol paragraph: block-uniform
+// uses one range per T_b x d_l block; the KIVI-style path uses per-channel
+// key and per-token value ranges; both run on the gauged cache with the same
+// bit settings, and decoding applies the inverse gauge).
+//
+// Quantizer (one range [mn, mx] per group, L = 2^bits - 1):
+//   scale = (mx - mn) / L, inv = L / (mx - mn)    (correctly rounded fp32)
+//   q     = clamp(rint((x - mn) * inv), 0, L)     (ties to even, no FMA)
+//   x_hat = mn + q * scale                        (multiply, then add)
+//   mx == mn, or inv not finite: scale = 0, every q = 0.
+// Codes are packed LSB first in token-major value order (value (t, c) of a
+// field at bit (t * 128 + c) * bits of its code region).
+//
+// Work layout: a workgroup (256 threads) processes 64-token tiles of one
+// field (a chunk of consecutive tiles when the dense MFMA gauge is used, so
+// its 64 KB matrix is loaded once).  After the gauge, thread i owns the 32
+// values (row i/4, channels 32 (i%4) .. +31): exactly `bits` 32-bit words of
+// codes, stored with one vector store, so a wave writes a contiguous span.
+#pragma once
+
+#include <float.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cg_quant.hpp"
+#include "cg_tile.hpp"
+#include "gauge128.hpp"
+
+namespace cgq {
+
+using namespace cgk;
+
+struct QK {
+  int64_t tcap, tokens, t0, nt;
+  int64_t chunks;           // workgroups per field
+  int32_t tiles_per_chunk;  // 64-token tiles per workgroup
+  int32_t batch, heads, kv;
+  int32_t block;            // block-uniform: tokens per range block
+  int32_t residual;         // KIVI: tail rows kept in the storage format
+};
+
+struct Range {
+  float mn, scale, inv;
+  bool zero;
+};
+
+__device__ __forceinline__ Range make_range(float mn, float mx, int L) {
+  Range r;
+  r.mn = mn;
+  const float diff = mx - mn;
+  r.inv = diff > 0.0f ? (float)L / diff : 0.0f;
+  r.zero = (mx == mn) || !(r.inv <= FLT_MAX);
+  r.scale = r.zero ? 0.0f : diff / (float)L;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t quant1(float x, const Range &r, int L) {
+  if (r.zero) return 0u;
+  const float s = x - r.mn;
+  const float p = s * r.inv;
+  int q = (int)rintf(p);
+  q = q < 0 ? 0 : (q > L ? L : q);
+  return (uint32_t)q;
+}
+
+__device__ __forceinline__ float dequant1(uint32_t q, float mn, float scale) {
+  const float p = (float)q * scale;
+  return mn + p;
+}
+
+template <int BITS>
+__device__ __forceinline__ void pack32(const uint32_t (&q)[32], uint32_t (&w)[BITS]) {
+#pragma unroll
+  for (int d = 0; d < BITS; d++) w[d] = 0;
+#pragma unroll
+  for (int k = 0; k < 32; k++) {
+    const int pos = k * BITS;
+    w[pos >> 5] |= q[k] << (pos & 31);
+    if ((pos & 31) + BITS > 32) w[(pos >> 5) + 1] |= q[k] >> (32 - (pos & 31));
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void unpack32(const uint32_t (&w)[BITS], uint32_t (&q)[32]) {
+  constexpr uint32_t M = (1u << BITS) - 1u;
+#pragma unroll
+  for (int k = 0; k < 32; k++) {
+    const int pos = k * BITS;
+    uint32_t v = w[pos >> 5] >> (pos & 31);
+    if ((pos & 31) + BITS > 32) v |= w[(pos >> 5) + 1] << (32 - (pos & 31));
+    q[k] = v & M;
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_words(uint8_t *p, const uint32_t (&w)[BITS]) {
+  if constexpr (BITS == 4) {
+    *(uint4 *)p = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (BITS == 8) {
+    ((uint4 *)p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    ((uint4 *)p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else if constexpr (BITS == 2) {
+    *(uint2 *)p = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int d = 0; d < BITS; d++) ((uint32_t *)p)[d] = w[d];
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[BITS]) {
+  if constexpr (BITS == 4) {
+    const uint4 u = *(const uint4 *)p;
+    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+  } else if constexpr (BITS == 8) {
+    const uint4 u = ((const uint4 *)p)[0], v = ((const uint4 *)p)[1];
+    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    w[4] = v.x; w[5] = v.y; w[6] = v.z; w[7] = v.w;
+  } else if constexpr (BITS == 2) {
+    const uint2 u = *(const uint2 *)p;
+    w[0] = u.x; w[1] = u.y;
+  } else {
+#pragma unroll
+    for (int d = 0; d < BITS; d++) w[d] = ((const uint32_t *)p)[d];
+  }
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// the 32 tile values owned by this thread (row t, channels 32 j .. 32 j + 31)
+__device__ __forceinline__ void read32(const float *xs, int t, int j, float (&v)[32]) {
+  const float *s = xs + t * PITCH + 32 * j;
+#pragma unroll
+  for (int k = 0; k < 32; k += 4) {
+    const float4 q = *(const float4 *)(s + k);
+    v[k] = q.x; v[k + 1] = q.y; v[k + 2] = q.z; v[k + 3] = q.w;
+  }
+}
+
+__device__ __forceinline__ void write32(float *xs, int t, int j, const float (&v)[32]) {
+  float *d = xs + t * PITCH + 32 * j;
+#pragma unroll
+  for (int k = 0; k < 32; k += 4) *(float4 *)(d + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+}
+
+__device__ __forceinline__ void zero_rows(float *xs, int from) {
+  for (int i = threadIdx.x; i < (TILE_T - from) * 32; i += NT)
+    *(float4 *)(xs + (from + (i >> 5)) * PITCH + (i & 31) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// gauge stage of a tile; DIR false = forward, true = inverse; EXACT: values
+// are bf16 numbers (dense gauge takes two passes instead of three)
+template <int G, bool INV, bool EXACT>
+__device__ __forceinline__ void gauge_stage(float *xs, int nrows, const float *Gf, const G128Frags &fr) {
+  if constexpr (G == 16 || G == 32) {
+    gauge_tile<G, INV>(xs, nrows, Gf);
+    __syncthreads();
+  } else if constexpr (G == 128) {
+    gauge128_tile<EXACT>(xs, fr);
+  }
+}
+
+// storage-format row segment of 32 values <-> fp32
+template <bool BF16>
+__device__ __forceinline__ void store32_storage(uint8_t *p, const float (&v)[32]) {
+  if (BF16) {
+    uint4 *d = (uint4 *)p;
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+      d[k] = make_uint4(pack_bf16x2(v[8 * k], v[8 * k + 1]), pack_bf16x2(v[8 * k + 2], v[8 * k + 3]),
+                        pack_bf16x2(v[8 * k + 4], v[8 * k + 5]), pack_bf16x2(v[8 * k + 6], v[8 * k + 7]));
+  } else {
+    float4 *d = (float4 *)p;
+#pragma unroll
+    for (int k = 0; k < 8; k++) d[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load32_storage(const uint8_t *p, float (&v)[32]) {
+  if (BF16) {
+    const uint4 *s = (const uint4 *)p;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint4 r = s[k];
+      v[8 * k] = bf16lo(r.x); v[8 * k + 1] = bf16hi(r.x);
+      v[8 * k + 2] = bf16lo(r.y); v[8 * k + 3] = bf16hi(r.y);
+      v[8 * k + 4] = bf16lo(r.z); v[8 * k + 5] = bf16hi(r.z);
+      v[8 * k + 6] = bf16lo(r.w); v[8 * k + 7] = bf16hi(r.w);
+    }
+  } else {
+    const float4 *s = (const float4 *)p;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const float4 r = s[k];
+      v[4 * k] = r.x; v[4 * k + 1] = r.y; v[4 * k + 2] = r.z; v[4 * k + 3] = r.w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// block-uniform
+// ---------------------------------------------------------------------------
+
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
+                                                  const float *__restrict__ gauges,
+                                                  uint8_t *__restrict__ payload,
+                                                  float *__restrict__ meta, QK a) {
+  __shared__ float xs[TILE_T * PITCH];
+  __shared__ float red[8];
+  constexpr int L = (1 << BITS) - 1;
+  const int64_t f = (int64_t)blockIdx.x / a.chunks;
+  const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
+  const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
+  const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
+  G128Frags fr;
+  if constexpr (G == 128) load_g128<false>(Gf, fr);
+  const int BT = a.block;
+  const int64_t nblk_f = a.tcap / BT;
+  const int t = threadIdx.x >> 2, j = threadIdx.x & 3, w = threadIdx.x >> 6;
+  for (int64_t tile = chunk * a.tiles_per_chunk;
+       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+    const int64_t tb = a.t0 + tile * TILE_T;
+    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+    load_tile<BF16>((const uint8_t *)kv + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4), nrows, xs);
+    if (G == 128 && nrows < TILE_T) zero_rows(xs, nrows);
+    __syncthreads();
+    gauge_stage<G, false, BF16>(xs, nrows, Gf, fr);
+    const bool active = t < nrows;
+    float v[32];
+    float mn = INFINITY, mx = -INFINITY;
+    if (active) {
+      read32(xs, t, j, v);
+#pragma unroll
+      for (int k = 0; k < 32; k++) {
+        mn = fminf(mn, v[k]);
+        mx = fmaxf(mx, v[k]);
+      }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if ((threadIdx.x & 63) == 0) {
+      red[2 * w] = mn;
+      red[2 * w + 1] = mx;
+    }
+    __syncthreads();
+    if (active) {
+      const int wpb = BT / 16, w0 = (t / BT) * wpb;
+      mn = red[2 * w0];
+      mx = red[2 * w0 + 1];
+      for (int k = 1; k < wpb; k++) {
+        mn = fminf(mn, red[2 * (w0 + k)]);
+        mx = fmaxf(mx, red[2 * (w0 + k) + 1]);
+      }
+      const Range r = make_range(mn, mx, L);
+      uint32_t q[32], wd[BITS];
+#pragma unroll
+      for (int k = 0; k < 32; k++) q[k] = quant1(v[k], r, L);
+      pack32<BITS>(q, wd);
+      store_words<BITS>(payload + (size_t)(f * a.tcap + tb) * 16 * BITS + threadIdx.x * 4 * BITS, wd);
+      if (j == 0 && (t % BT) == 0) {
+        float *m = meta + 2 * (f * nblk_f + (tb + t) / BT);
+        m[0] = r.mn;
+        m[1] = r.scale;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ payload,
+                                                  const float *__restrict__ meta,
+                                                  const float *__restrict__ gauges,
+                                                  void *__restrict__ out, QK a) {
+  __shared__ float xs[TILE_T * PITCH];
+  const int64_t f = (int64_t)blockIdx.x / a.chunks;
+  const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
+  const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
+  const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
+  G128Frags fr;
+  if constexpr (G == 128) load_g128<true>(Gf, fr);
+  const int BT = a.block;
+  const int64_t nblk_f = a.tcap / BT;
+  const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
+  for (int64_t tile = chunk * a.tiles_per_chunk;
+       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+    const int64_t tb = a.t0 + tile * TILE_T;
+    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+    float v[32];
+    if (t < nrows) {
+      uint32_t wd[BITS], q[32];
+      load_words<BITS>(payload + (size_t)(f * a.tcap + tb) * 16 * BITS + threadIdx.x * 4 * BITS, wd);
+      unpack32<BITS>(wd, q);
+      const float *m = meta + 2 * (f * nblk_f + (tb + t) / BT);
+      const float mn = m[0], sc = m[1];
+#pragma unroll
+      for (int k = 0; k < 32; k++) v[k] = dequant1(q[k], mn, sc);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 32; k++) v[k] = 0.0f;
+    }
+    write32(xs, t, j, v);
+    __syncthreads();
+    gauge_stage<G, true, false>(xs, nrows, Gf, fr);
+    store_tile<BF16>((uint8_t *)out + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4), nrows, xs);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KIVI-style: keys one range per channel per 32 tokens, values one range per
+// token per 32 channels; the last `residual` rows stay in the storage format.
+// Field payload: codes of rows [0, Tcap - residual), then the tail rows.
+// Metadata: 4 * (Tcap - residual) (mn, scale) pairs per field, keys indexed
+// (row / 32) * 128 + channel, values row * 4 + channel / 32.
+// ---------------------------------------------------------------------------
+
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
+                                                    const float *__restrict__ gauges,
+                                                    uint8_t *__restrict__ payload,
+                                                    float *__restrict__ meta, QK a) {
+  __shared__ float xs[TILE_T * PITCH];
+  __shared__ float pmn[2 * D], pinv[2 * D];
+  __shared__ uint8_t pzero[2 * D];
+  constexpr int L = (1 << BITS) - 1;
+  constexpr size_t ESZ = BF16 ? 2 : 4;
+  const int64_t f = (int64_t)blockIdx.x / a.chunks;
+  const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
+  const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
+  const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
+  G128Frags fr;
+  if constexpr (G == 128) load_g128<false>(Gf, fr);
+  const int64_t Tq = a.tokens - a.residual, Tcq = a.tcap - a.residual;
+  const size_t Pf = (size_t)Tcq * 16 * BITS + (size_t)a.residual * D * ESZ;
+  uint8_t *pf = payload + (size_t)f * Pf;
+  float *mf = meta + 2 * (size_t)f * 4 * Tcq;
+  const bool keys = ((f / ((int64_t)a.batch * a.heads)) % a.kv) == 0;
+  const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
+  for (int64_t tile = chunk * a.tiles_per_chunk;
+       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+    const int64_t tb = a.t0 + tile * TILE_T;
+    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+    load_tile<BF16>((const uint8_t *)kv + (size_t)(f * a.tcap + tb) * D * ESZ, nrows, xs);
+    if (G == 128 && nrows < TILE_T) zero_rows(xs, nrows);
+    __syncthreads();
+    gauge_stage<G, false, BF16>(xs, nrows, Gf, fr);
+    if (keys) {
+      const int gi = threadIdx.x >> 7, c = threadIdx.x & 127;
+      const int r0 = 32 * gi;
+      if (r0 < nrows && tb + r0 < Tq) {
+        float mn = INFINITY, mx = -INFINITY;
+        for (int r = 0; r < 32; r++) {
+          const float x = xs[(r0 + r) * PITCH + c];
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+        }
+        const Range rg = make_range(mn, mx, L);
+        pmn[threadIdx.x] = rg.mn;
+        pinv[threadIdx.x] = rg.inv;
+        pzero[threadIdx.x] = rg.zero;
+        float *m = mf + 2 * (((tb + r0) / 32) * D + c);
+        m[0] = rg.mn;
+        m[1] = rg.scale;
+      }
+      __syncthreads();
+    }
+    if (t < nrows) {
+      const int64_t row = tb + t;
+      float v[32];
+      read32(xs, t, j, v);
+      if (row < Tq) {
+        uint32_t q[32], wd[BITS];
+        if (keys) {
+          const int base = (t >> 5) * D + 32 * j;
+#pragma unroll
+          for (int k = 0; k < 32; k++) {
+            Range rg;
+            rg.mn = pmn[base + k];
+            rg.inv = pinv[base + k];
+            rg.zero = pzero[base + k];
+            q[k] = quant1(v[k], rg, L);
+          }
+        } else {
+          float mn = v[0], mx = v[0];
+#pragma unroll
+          for (int k = 1; k < 32; k++) {
+            mn = fminf(mn, v[k]);
+            mx = fmaxf(mx, v[k]);
+          }
+          const Range rg = make_range(mn, mx, L);
+#pragma unroll
+          for (int k = 0; k < 32; k++) q[k] = quant1(v[k], rg, L);
+          float *m = mf + 2 * (row * 4 + j);
+          m[0] = rg.mn;
+          m[1] = rg.scale;
+        }
+        pack32<BITS>(q, wd);
+        store_words<BITS>(pf + (size_t)row * 16 * BITS + j * 4 * BITS, wd);
+      } else {
+        store32_storage<BF16>(pf + (size_t)Tcq * 16 * BITS + ((size_t)(row - Tq) * D + 32 * j) * ESZ, v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ payload,
+                                                    const float *__restrict__ meta,
+                                                    const float *__restrict__ gauges,
+                                                    void *__restrict__ out, QK a) {
+  __shared__ float xs[TILE_T * PITCH];
+  __shared__ float pmn[2 * D], psc[2 * D];
+  constexpr size_t ESZ = BF16 ? 2 : 4;
+  const int64_t f = (int64_t)blockIdx.x / a.chunks;
+  const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
+  const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
+  const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
+  G128Frags fr;
+  if constexpr (G == 128) load_g128<true>(Gf, fr);
+  const int64_t Tq = a.tokens - a.residual, Tcq = a.tcap - a.residual;
+  const size_t Pf = (size_t)Tcq * 16 * BITS + (size_t)a.residual * D * ESZ;
+  const uint8_t *pf = payload + (size_t)f * Pf;
+  const float *mf = meta + 2 * (size_t)f * 4 * Tcq;
+  const bool keys = ((f / ((int64_t)a.batch * a.heads)) % a.kv) == 0;
+  const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
+  for (int64_t tile = chunk * a.tiles_per_chunk;
+       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+    const int64_t tb = a.t0 + tile * TILE_T;
+    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+    if (keys) {
+      const int gi = threadIdx.x >> 7, c = threadIdx.x & 127;
+      const int r0 = 32 * gi;
+      if (r0 < nrows && tb + r0 < Tq) {
+        const float *m = mf + 2 * (((tb + r0) / 32) * D + c);
+        pmn[threadIdx.x] = m[0];
+        psc[threadIdx.x] = m[1];
+      }
+      __syncthreads();
+    }
+    float v[32];
+    if (t < nrows) {
+      const int64_t row = tb + t;
+      if (row < Tq) {
+        uint32_t wd[BITS], q[32];
+        load_words<BITS>(pf + (size_t)row * 16 * BITS + j * 4 * BITS, wd);
+        unpack32<BITS>(wd, q);
+        if (keys) {
+          const int base = (t >> 5) * D + 32 * j;
+#pragma unroll
+          for (int k = 0; k < 32; k++) v[k] = dequant1(q[k], pmn[base + k], psc[base + k]);
+        } else {
+          const float *m = mf + 2 * (row * 4 + j);
+          const float mn = m[0], sc = m[1];
+#pragma unroll
+          for (int k = 0; k < 32; k++) v[k] = dequant1(q[k], mn, sc);
+        }
+      } else {
+        load32_storage<BF16>(pf + (size_t)Tcq * 16 * BITS + ((size_t)(row - Tq) * D + 32 * j) * ESZ, v);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 32; k++) v[k] = 0.0f;
+    }
+    write32(xs, t, j, v);
+    __syncthreads();
+    gauge_stage<G, true, false>(xs, nrows, Gf, fr);
+    store_tile<BF16>((uint8_t *)out + (size_t)(f * a.tcap + tb) * D * ESZ, nrows, xs);
+    __syncthreads();
+  }
+}
+
+// dense-gauge rows kernel behind cg_gauge_apply(g = 128): same tiles, same
+// fragments, same MFMA sequence as the fused quantizer kernels
+template <bool BF16, bool INV>
+__global__ __launch_bounds__(NT) void k_gauge128_rows(const void *__restrict__ src,
+                                                      const float *__restrict__ gauges,
+                                                      float *__restrict__ out, QK a) {
+  __shared__ float xs[TILE_T * PITCH];
+  const int64_t f = (int64_t)blockIdx.x / a.chunks;
+  const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
+  const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
+  const float *Gf = gauges + gauge_index(f, a.batch, a.heads) * D * 128;
+  G128Frags fr;
+  load_g128<INV>(Gf, fr);
+  for (int64_t tile = chunk * a.tiles_per_chunk;
+       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+    const int64_t tb = a.t0 + tile * TILE_T;
+    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+    load_tile<BF16>((const uint8_t *)src + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4), nrows, xs);
+    if (nrows < TILE_T) zero_rows(xs, nrows);
+    __syncthreads();
+    gauge128_tile<BF16>(xs, fr);
+    store_tile<false>(out + (size_t)(f * a.tcap + tb) * D, nrows, xs);
+    __syncthreads();
+  }
+}
+
+}  // namespace cgq

@@ -1,0 +1,306 @@
+// zfp-style fixed-rate coding of one 4x4 token x channel block, in registers.
+//
+// The Codec-Gauge paper ("Codec-Gauge: Learning Compression-Friendly Gauges
+// for Transformer KV Caches", arXiv HTML, evaluation-protocol paragraph)
+// uses fixed-rate zfp (Lindstrom 2014) on the gauged FP32 field presented as
+// a 2D array with n_x = d_l.  One block is 4 tokens x 4 channels and always
+// occupies exactly 16*R bits:
+//   bit 0            nonzero flag (0: all values are +-0, rest is zero)
+//   bits 1..8        emax + 127, emax = largest frexp exponent, >= -126
+//   bits 9..16R-1    embedded bit-plane code of the 16 transformed integers
+// Steps: block-floating-point integers q = trunc(x * 2^(30-emax)); the
+// 4-point integer lifting transform along channels, then along tokens;
+// total-sequency reordering; negabinary; bit planes 31..0 coded with group
+// tests until the 16R-9 bit budget is spent.
+//
+// GPU formulation (one block per lane, everything in VGPRs):
+//  * the leading all-zero planes cost one 0 bit each, so they are skipped in
+//    one step with a count-leading-zeros of the OR of the 16 words, and the
+//    words are shifted so that the first nonzero plane sits at bit 31;
+//  * all bit planes are produced at once by a 16x16 bit-matrix transpose
+//    applied to both 16-bit halves of the 16 words (4 butterfly stages);
+//  * a plane's verbatim part is one masked shift into the output, and its
+//    group-test/scan part costs one step per coefficient that becomes
+//    significant (each coefficient does so at most once per block);
+//  * the block's bits live in ceil(16R/64) 64-bit accumulators; bits past
+//    16R are dropped, which equals stopping at the budget because the code
+//    of a block is a prefix code emitted strictly left to right.
+// The functions are __host__ __device__ so the same code can be checked on
+// the CPU; they use only portable integer operations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cgz {
+
+constexpr uint32_t kNegaMask = 0xAAAAAAAAu;
+
+// total-sequency order: coefficient (i, j) stored at i + 4j, visited by
+// i + j, then i^2 + j^2, then larger i first
+__host__ __device__ constexpr int seq_index(int k) {
+  constexpr int order[16] = {0, 1, 4, 5, 2, 8, 6, 9, 3, 12, 10, 7, 13, 11, 14, 15};
+  return order[k];
+}
+
+template <int R>
+struct Rate {
+  static constexpr int kBits = 16 * R;
+  static constexpr int kAcc = (kBits + 63) / 64;   // 64-bit accumulators
+};
+
+__host__ __device__ __forceinline__ int32_t shr1(uint32_t s) { return ((int32_t)s) >> 1; }
+
+// forward 4-point lifting transform (integer realization of
+// F = 1/16 [[4,4,4,4],[5,1,-1,-5],[-4,4,4,-4],[-2,6,-6,2]])
+__host__ __device__ __forceinline__ void fwd_xform4(int32_t &a, int32_t &b, int32_t &c,
+                                                    int32_t &d) {
+  a = shr1((uint32_t)a + (uint32_t)d);
+  d = (int32_t)((uint32_t)d - (uint32_t)a);
+  c = shr1((uint32_t)b + (uint32_t)c);
+  b = (int32_t)((uint32_t)b - (uint32_t)c);
+  a = shr1((uint32_t)a + (uint32_t)c);
+  c = (int32_t)((uint32_t)c - (uint32_t)a);
+  d = shr1((uint32_t)d + (uint32_t)b);
+  b = (int32_t)((uint32_t)b - (uint32_t)d);
+  d = (int32_t)((uint32_t)d + (uint32_t)(b >> 1));
+  b = (int32_t)((uint32_t)b - (uint32_t)(d >> 1));
+}
+
+// exact inverse of every lifting step, in reverse order (mod 2^32)
+__host__ __device__ __forceinline__ void inv_xform4(int32_t &a, int32_t &b, int32_t &c,
+                                                    int32_t &d) {
+  b = (int32_t)((uint32_t)b + (uint32_t)(d >> 1));
+  d = (int32_t)((uint32_t)d - (uint32_t)(b >> 1));
+  b = (int32_t)((uint32_t)b + (uint32_t)d);
+  d = (int32_t)(((uint32_t)d << 1) - (uint32_t)b);
+  c = (int32_t)((uint32_t)c + (uint32_t)a);
+  a = (int32_t)(((uint32_t)a << 1) - (uint32_t)c);
+  b = (int32_t)((uint32_t)b + (uint32_t)c);
+  c = (int32_t)(((uint32_t)c << 1) - (uint32_t)b);
+  d = (int32_t)((uint32_t)d + (uint32_t)a);
+  a = (int32_t)(((uint32_t)a << 1) - (uint32_t)d);
+}
+
+// Transpose the two 16x16 bit matrices held in the low and high halves of
+// w[0..15] (row i = word i, column c = bit c of the half).  Afterwards the low
+// half of w[k] is the word whose bit i was bit k of the old w[i], and the high
+// half likewise for bit 16 + k.  The transform is an involution.
+__host__ __device__ __forceinline__ void transpose16x2(uint32_t (&w)[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint32_t t = ((w[i] >> 8) ^ w[i + 8]) & 0x00FF00FFu;
+    w[i + 8] ^= t;
+    w[i] ^= t << 8;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    if (i & 4) continue;
+    uint32_t t = ((w[i] >> 4) ^ w[i + 4]) & 0x0F0F0F0Fu;
+    w[i + 4] ^= t;
+    w[i] ^= t << 4;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    if (i & 2) continue;
+    uint32_t t = ((w[i] >> 2) ^ w[i + 2]) & 0x33333333u;
+    w[i + 2] ^= t;
+    w[i] ^= t << 2;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    uint32_t t = ((w[i] >> 1) ^ w[i + 1]) & 0x55555555u;
+    w[i + 1] ^= t;
+    w[i] ^= t << 1;
+  }
+}
+
+__host__ __device__ __forceinline__ int ctz32(uint32_t x) {  // x != 0
+  return __builtin_ctz(x);
+}
+
+__host__ __device__ __forceinline__ int clz32(uint32_t x) {  // x != 0
+  return __builtin_clz(x);
+}
+
+// Append `len` (<= 32) bits of `code` at bit `pos`; bits at or past 16R are
+// dropped.
+template <int R>
+__host__ __device__ __forceinline__ void put(uint64_t (&acc)[Rate<R>::kAcc], int pos,
+                                             uint32_t code) {
+  constexpr int NA = Rate<R>::kAcc;
+  if (pos >= Rate<R>::kBits) return;
+#pragma unroll
+  for (int a = 0; a < NA; a++) {
+    int sh = pos - 64 * a;
+    if (sh >= 0 && sh < 64)
+      acc[a] |= (uint64_t)code << sh;
+    else if (sh < 0 && sh > -32)
+      acc[a] |= (uint64_t)code >> (-sh);
+  }
+}
+
+// 32 stream bits starting at `pos` (< 16R); bits past 16R read as 0
+template <int R>
+__host__ __device__ __forceinline__ uint32_t window(const uint64_t (&acc)[Rate<R>::kAcc],
+                                                    int pos) {
+  constexpr int NA = Rate<R>::kAcc;
+  if (NA == 1) return (uint32_t)(acc[0] >> pos);
+  uint32_t r = 0;
+#pragma unroll
+  for (int a = 0; a < NA; a++) {
+    int sh = pos - 64 * a;
+    if (sh >= 0 && sh < 64)
+      r |= (uint32_t)(acc[a] >> sh);
+    else if (sh < 0 && sh > -32)
+      r |= (uint32_t)(acc[a] << (-sh));
+  }
+  return r;
+}
+
+// Encode 16 fp32 values v[4j + i] (j = token row, i = channel) at rate R.
+template <int R>
+__host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
+                                                      uint64_t (&acc)[Rate<R>::kAcc]) {
+  constexpr int NA = Rate<R>::kAcc;
+  constexpr int LIMIT = Rate<R>::kBits;
+#pragma unroll
+  for (int a = 0; a < NA; a++) acc[a] = 0;
+
+  // block exponent from the largest magnitude (bit patterns of |x| order like
+  // the values): frexp exponent = biased exponent - 126, clamped at -126
+  uint32_t mx = 0;
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    uint32_t m = __builtin_bit_cast(uint32_t, v[k]) & 0x7FFFFFFFu;
+    mx = m > mx ? m : mx;
+  }
+  if (mx == 0) return;
+  int ebiased = (int)(mx >> 23);
+  int emax = ebiased ? ebiased - 126 : -126;
+
+  int32_t q[16];
+#pragma unroll
+  for (int k = 0; k < 16; k++) q[k] = (int32_t)ldexpf(v[k], 30 - emax);
+#pragma unroll
+  for (int j = 0; j < 4; j++) fwd_xform4(q[4 * j], q[4 * j + 1], q[4 * j + 2], q[4 * j + 3]);
+#pragma unroll
+  for (int i = 0; i < 4; i++) fwd_xform4(q[i], q[4 + i], q[8 + i], q[12 + i]);
+
+  uint32_t u[16];
+  uint32_t any = 0;
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    u[k] = ((uint32_t)q[seq_index(k)] + kNegaMask) ^ kNegaMask;
+    any |= u[k];
+  }
+  acc[0] = 1u | ((uint64_t)(uint32_t)(emax + 127) << 1);
+  if (any == 0) return;
+  const int s = clz32(any);            // planes 31..32-s are all zero
+  int pos = 9 + s;                      // one failed group test per zero plane
+#pragma unroll
+  for (int k = 0; k < 16; k++) u[k] <<= s;
+  transpose16x2(u);                     // u[m]: plane m (low), plane m+16 (high)
+
+  int n = 0;                            // coefficients already significant
+#pragma unroll
+  for (int j = 0; j < 32; j++) {        // plane 31-j of the shifted words
+    if (j > 31 - s || pos >= LIMIT) break;
+    const uint32_t w = j < 16 ? (u[15 - j] >> 16) : (u[31 - j] & 0xFFFFu);
+    // verbatim bits of the significant coefficients
+    put<R>(acc, pos, w & ((1u << n) - 1u));
+    pos += n;
+    if (n < 16) {
+      if ((w >> n) == 0) {
+        pos += 1;                       // failed group test (a 0 bit)
+      } else {
+        int cur = n;
+        for (;;) {
+          const int p = cur + ctz32(w >> cur);   // next one at or after cur
+          if (p >= 15) {                // scan reaches 15: the one is implied
+            put<R>(acc, pos, 1u);       // group test, then 15-cur zeros
+            pos += 16 - cur;
+            cur = 16;
+            break;
+          }
+          const int gap = p - cur;      // group test 1, gap zeros, the 1
+          put<R>(acc, pos, 1u | (1u << (gap + 1)));
+          pos += gap + 2;
+          cur = p + 1;
+          if ((w >> cur) == 0) {        // next group test fails
+            pos += 1;
+            break;
+          }
+          if (pos >= LIMIT) break;
+        }
+        n = cur;
+      }
+    }
+  }
+  if (LIMIT % 64) acc[NA - 1] &= (~0ull) >> (64 - LIMIT % 64);
+}
+
+// Decode one block of 16R bits into 16 fp32 values v[4j + i].
+template <int R>
+__host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate<R>::kAcc],
+                                                      float (&v)[16]) {
+  constexpr int LIMIT = Rate<R>::kBits;
+#pragma unroll
+  for (int k = 0; k < 16; k++) v[k] = 0.0f;
+  if (!(acc[0] & 1u)) return;
+  const int emax = (int)((acc[0] >> 1) & 0xFFu) - 127;
+
+  int pos = 9;
+  uint32_t win = window<R>(acc, pos);
+  const int s = win ? ctz32(win) : 32;  // leading failed group tests
+  if (s >= 32 || pos + s >= LIMIT) return;  // no plane reached: all integers 0
+  pos += s;
+
+  uint32_t w[16];
+#pragma unroll
+  for (int k = 0; k < 16; k++) w[k] = 0;
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < 32; j++) {
+    if (j > 31 - s || pos >= LIMIT) break;
+    uint32_t x = n ? (window<R>(acc, pos) & ((1u << n) - 1u)) : 0u;
+    pos += n;
+    while (n < 16 && pos < LIMIT) {
+      const uint32_t t = window<R>(acc, pos) & 1u;
+      pos += 1;
+      if (!t) break;
+      const int lim0 = 15 - n, room = LIMIT - pos;
+      const int lim = lim0 < room ? lim0 : room;
+      const uint32_t ww = lim > 0 ? window<R>(acc, pos) : 0u;
+      const int z = ww ? ctz32(ww) : 32;
+      int gap;
+      if (z < lim) {
+        gap = z;
+        pos += z + 1;
+      } else {
+        gap = lim;
+        pos += lim;
+      }
+      x |= 1u << (n + gap);
+      n += gap + 1;
+    }
+    if (j < 16)
+      w[15 - j] |= x << 16;
+    else
+      w[31 - j] |= x;
+  }
+  transpose16x2(w);
+
+  int32_t q[16];
+#pragma unroll
+  for (int k = 0; k < 16; k++)
+    q[seq_index(k)] = (int32_t)(((w[k] >> s) ^ kNegaMask) - kNegaMask);
+#pragma unroll
+  for (int i = 0; i < 4; i++) inv_xform4(q[i], q[4 + i], q[8 + i], q[12 + i]);
+#pragma unroll
+  for (int j = 0; j < 4; j++) inv_xform4(q[4 * j], q[4 * j + 1], q[4 * j + 2], q[4 * j + 3]);
+#pragma unroll
+  for (int k = 0; k < 16; k++) v[k] = ldexpf((float)q[k], emax - 30);
+}
+
+}  // namespace cgz

@@ -1,0 +1,150 @@
+// Fused gauge + zfp-style fixed-rate encode, and fused decode + inverse gauge
+// ("Codec-Gauge", arXiv HTML, evaluation-protocol paragraph: the gauged FP32
+// tensor is zfp-encoded at a fixed rate as a 2D field with n_x = d_l, decoded,
+// and the inverse gauge restores the cache before attention).
+//
+// One workgroup (256 threads) owns a tile of 64 tokens x 128 channels of one
+// field: 16 block rows x 32 blocks = 512 blocks, whose 16R-bit codes are one
+// contiguous 1024R-byte span of the stream.
+//   encode: coalesced tile load -> LDS (fp32) -> gauge in place (lane = token,
+//           wave-uniform group, SGPR matrix) -> one block per thread-iteration
+//           (zfp_block.hpp, all in VGPRs) -> codes staged in LDS -> coalesced
+//           16-byte stores of the span.
+//   decode: the mirror image.
+// Stream layout: field f, block (bx, by) (bx = channel block, fastest) sits at
+// bits [((f * Tcap/4 + by) * 32 + bx) * 16R, +16R), stream bit p = bit p%8 of
+// byte p/8 -- the pages' whole-tensor 2D field with the fields in order,
+// since no 4x4 block straddles two fields (Tcap % 4 == 0).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cg_launch.hpp"
+#include "cg_tile.hpp"
+#include "zfp_block.hpp"
+
+namespace cgk {
+
+// write the 16R bits of block b into the LDS stream image (halfword granular)
+template <int R>
+__device__ __forceinline__ void stage_block(uint32_t *os, int b, const uint64_t (&acc)[cgz::Rate<R>::kAcc]) {
+  if constexpr (R % 2 == 0) {
+    uint32_t *d = os + b * (R / 2);
+#pragma unroll
+    for (int h = 0; h < R / 2; h++) d[h] = (uint32_t)(acc[h / 2] >> (32 * (h % 2)));
+  } else {
+    uint16_t *d = (uint16_t *)os + b * R;
+#pragma unroll
+    for (int h = 0; h < R; h++) d[h] = (uint16_t)(acc[h / 4] >> (16 * (h % 4)));
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void unstage_block(const uint32_t *os, int b, uint64_t (&acc)[cgz::Rate<R>::kAcc]) {
+#pragma unroll
+  for (int a = 0; a < cgz::Rate<R>::kAcc; a++) acc[a] = 0;
+  if constexpr (R % 2 == 0) {
+    const uint32_t *s = os + b * (R / 2);
+#pragma unroll
+    for (int h = 0; h < R / 2; h++) acc[h / 2] |= (uint64_t)s[h] << (32 * (h % 2));
+  } else {
+    const uint16_t *s = (const uint16_t *)os + b * R;
+#pragma unroll
+    for (int h = 0; h < R; h++) acc[h / 4] |= (uint64_t)s[h] << (16 * (h % 4));
+  }
+}
+
+template <int R, bool BF16, int G>
+__global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
+                                                   const float *__restrict__ gauges,
+                                                   uint8_t *__restrict__ payload, TileArgs a) {
+  __shared__ float xs[TILE_T * PITCH];
+  __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
+  const int64_t field = (int64_t)blockIdx.x / a.tiles;
+  const int tile = (int)((int64_t)blockIdx.x % a.tiles);
+  const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
+  const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+  const int64_t row0 = field * a.tcap + tb;
+  const size_t esz = BF16 ? 2 : 4;
+  load_tile<BF16>((const uint8_t *)kv + (size_t)row0 * D * esz, nrows, xs);
+  __syncthreads();
+  if constexpr (G != 0) {
+    gauge_tile<G, false>(xs, nrows, gauges + gauge_index(field, a.batch, a.heads) * D * G);
+    __syncthreads();
+  }
+  const int nblk = (nrows / 4) * 32;
+  for (int b = threadIdx.x; b < nblk; b += NT) {
+    const float *src = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float4 t = *(const float4 *)(src + j * PITCH);
+      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    }
+    uint64_t acc[cgz::Rate<R>::kAcc];
+    cgz::encode_block<R>(v, acc);
+    stage_block<R>(os, b, acc);
+  }
+  __syncthreads();
+  uint4 *dst = (uint4 *)(payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R);
+  const int n16 = nblk * 2 * R / 16;
+  for (int i = threadIdx.x; i < n16; i += NT) dst[i] = ((const uint4 *)os)[i];
+}
+
+template <int R, bool BF16, int G>
+__global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ payload,
+                                                   const float *__restrict__ gauges,
+                                                   void *__restrict__ out, TileArgs a) {
+  __shared__ float xs[TILE_T * PITCH];
+  __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
+  const int64_t field = (int64_t)blockIdx.x / a.tiles;
+  const int tile = (int)((int64_t)blockIdx.x % a.tiles);
+  const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
+  const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+  const int64_t row0 = field * a.tcap + tb;
+  const int nblk = (nrows / 4) * 32;
+  const uint4 *src = (const uint4 *)(payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R);
+  const int n16 = nblk * 2 * R / 16;
+  for (int i = threadIdx.x; i < n16; i += NT) ((uint4 *)os)[i] = src[i];
+  __syncthreads();
+  for (int b = threadIdx.x; b < nblk; b += NT) {
+    uint64_t acc[cgz::Rate<R>::kAcc];
+    unstage_block<R>(os, b, acc);
+    float v[16];
+    cgz::decode_block<R>(acc, v);
+    float *dst = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      *(float4 *)(dst + j * PITCH) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+  }
+  __syncthreads();
+  if constexpr (G != 0) {
+    gauge_tile<G, true>(xs, nrows, gauges + gauge_index(field, a.batch, a.heads) * D * G);
+    __syncthreads();
+  }
+  const size_t esz = BF16 ? 2 : 4;
+  store_tile<BF16>((uint8_t *)out + (size_t)row0 * D * esz, nrows, xs);
+}
+
+// all launches of one rate R (encode or decode, storage format, group size)
+template <int R>
+hipError_t zfp_launch_rate(bool encode, bool bf16, int g, const void *src, const float *gauges,
+                           void *dst, const TileArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)a.grid), block(NT);
+#define CG_L(BF, GG)                                                                             \
+  if (bf16 == BF && g == GG) {                                                                   \
+    if (encode)                                                                                  \
+      hipLaunchKernelGGL((k_zfp_encode<R, BF, GG>), grid, block, 0, s, src, gauges,             \
+                         (uint8_t *)dst, a);                                                     \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_zfp_decode<R, BF, GG>), grid, block, 0, s, (const uint8_t *)src,    \
+                         gauges, dst, a);                                                        \
+    return hipGetLastError();                                                                    \
+  }
+  CG_L(true, 0) CG_L(true, 16) CG_L(true, 32) CG_L(false, 0) CG_L(false, 16) CG_L(false, 32)
+#undef CG_L
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cgk

@@ -101,6 +101,7 @@ _slib = None
 def _synth_lib():
     global _slib
     if _slib is None:
+        import torch  # noqa: F401  (bind to torch's HIP runtime, see binding.lib)
         if not os.path.exists(_SYNTH_LIB):
             raise RuntimeError("libcgsynth.so is not built; run __graft_entry__.build()")
         L = ctypes.CDLL(_SYNTH_LIB)

@@ -1,0 +1,216 @@
+/*
+ * codec_gauge.h -- C ABI of libcodecgauge.so, the MI355X (gfx950) Codec-Gauge
+ * KV-cache round trip.
+ *
+ * Method: "Codec-Gauge: Learning Compression-Friendly Gauges for Transformer
+ * KV Caches" (arXiv 2607.20538; HTML page and its Chinese translation).
+ *  - Problem statement (Chinese page): per layer l the cache holds
+ *    K_l, V_l in R^{B x H_l x T x d_l}; for each layer, cache type s in
+ *    {K, V}, head h and channel group r (g channels, R_l = d_l / g groups,
+ *    g = d_l is a full-head gauge) a gauge G_{l,s,h,r} acts on
+ *    X_{l,s}[b,h,t,r] in R^g.  It mixes channels within a group only, never
+ *    tokens, heads or layers.
+ *  - Gauge parameterization (arXiv page): G = exp(A - A^T), orthogonal; the
+ *    gauge is a fixed model-side object, not per-token payload; explicit
+ *    application costs O(N_KV g) multiply-adds and is charged in timing.
+ *  - Evaluation protocol (arXiv page): the cache goes through the gauge, a
+ *    fixed backend (fixed-rate zfp on the FP32-transformed tensor as a 2D
+ *    field n_x = d_l, n_y = numel/d_l; block-uniform ranges per T_b x d_l
+ *    block; KIVI-style per-channel key / per-token value ranges), decode and
+ *    the inverse gauge; actual compressed bytes are recorded (payload plus a
+ *    fixed shape header).
+ *  - Frequency objective (arXiv page): orthonormal 2D DCT of T_b x d_l
+ *    token-channel blocks of X' = G X, spectral-centroid loss L_freq and
+ *    log-amplitude rate proxy L_rate (tau = 0.04), combined with lambda_f,
+ *    lambda_r; the gauge is trained on it with AdamW.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers point to memory the caller allocated on the current HIP
+ *    device (hipMalloc or torch); host pointers are ordinary host memory.
+ *    The library never allocates or frees caller-visible memory and keeps no
+ *    state between calls (except the thread-local error string).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Device work is
+ *    enqueued asynchronously unless stated otherwise.
+ *  - Every argument is validated on the host before anything is enqueued; on
+ *    error nothing is written and a negative CG_E_* code is returned, with a
+ *    message available from cg_last_error().  No C++ exception crosses the
+ *    ABI.
+ *  - KV layout: data[layers][kv][batch][heads][token_capacity][head_dim],
+ *    row-major, rows [0, tokens) valid.  A "field" is one
+ *    (layer, kv, batch, head) slab [token_capacity][head_dim]; fields are
+ *    numbered in that row-major order.
+ *  - Gauge layout: G[layers][kv][heads][head_dim/g][g][g] fp32 row-major,
+ *    shared by every sequence of the batch; x'[r*g+i] = sum_k G[r][i][k]
+ *    x[r*g+k] per token, evaluated (for g <= 32) as an fmaf chain over
+ *    k = 0..g-1 from +0; the inverse applies G^T the same way.
+ *  - Non-finite KV values are not supported (no check is made).
+ */
+#ifndef CODEC_GAUGE_H
+#define CODEC_GAUGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define CG_OK 0
+#define CG_E_INVAL (-1)       /* NULL pointer, bad enum, negative size */
+#define CG_E_SHAPE (-2)       /* sizes not divisible / out of range */
+#define CG_E_UNSUPPORTED (-3) /* valid but not built (dtype/backend/bits/g combination) */
+#define CG_E_SIZE (-4)        /* a caller buffer or workspace is too small */
+#define CG_E_HIP (-5)         /* HIP runtime / launch error (message from HIP) */
+#define CG_E_INTERNAL (-6)
+
+/* storage formats */
+#define CG_DTYPE_F32 0
+#define CG_DTYPE_BF16 1
+
+/* backends */
+#define CG_BACKEND_NONE 0          /* gauge only: payload = gauged fp32 values */
+#define CG_BACKEND_ZFP 1           /* zfp-style fixed rate, 4x4 blocks */
+#define CG_BACKEND_BLOCK_UNIFORM 2 /* one min/max range per block_tokens x head_dim */
+#define CG_BACKEND_KIVI 3          /* keys per-channel, values per-token ranges */
+
+/* size of the fixed per-tensor shape header (one per (layer, kv) tensor) */
+#define CG_HEADER_BYTES 64
+
+typedef struct cg_shape {
+  int32_t layers;         /* L >= 1 */
+  int32_t kv;             /* 1 or 2 (index 0 = K, 1 = V) */
+  int32_t batch;          /* B >= 1 */
+  int32_t heads;          /* KV heads H >= 1 */
+  int64_t tokens;         /* valid rows T, 0 <= T <= token_capacity */
+  int64_t token_capacity; /* allocated rows per field */
+  int32_t head_dim;       /* d_l; this build supports 128 */
+  int32_t dtype;          /* CG_DTYPE_* storage format of the KV tensors */
+} cg_shape;
+
+typedef struct cg_gauge {
+  int32_t group;   /* g: 0 = identity (no arithmetic), else divides head_dim;
+                      built: 16 and 32 for every backend, 128 for
+                      BLOCK_UNIFORM and KIVI (dense full-head gauge) */
+  const float *G;  /* device, fp32 [layers][kv][heads][head_dim/g][g][g];
+                      ignored when group == 0 */
+} cg_gauge;
+
+typedef struct cg_codec {
+  int32_t backend;         /* CG_BACKEND_* */
+  int32_t bits;            /* ZFP: bits per value R in {2,3,4,6,8};
+                              quantizers: code bits in {2,3,4,8} */
+  int32_t block_tokens;    /* BLOCK_UNIFORM: tokens per range block (T_b);
+                              KIVI: group size (tokens per key range, channels
+                              per value range) */
+  int32_t residual_tokens; /* KIVI: trailing tokens kept in the storage
+                              format (after the gauge); else 0 */
+} cg_codec;
+
+typedef struct cg_stats {
+  double L_freq; /* mean over blocks of sum(r E) / sum(E) */
+  double L_rate; /* mean over coefficients of log(1 + |U| / tau) */
+  double L;      /* lambda_f L_freq + lambda_r L_rate */
+  double sum_E;  /* total DCT energy (equals the field energy, Parseval) */
+} cg_stats;
+
+/*
+ * Exact byte counts of an encoded cache (host only, no device work).
+ * Evaluation protocol (arXiv page): reported bytes are the zfp payload plus a
+ * fixed shape header.  Per field of token_capacity rows:
+ *   ZFP            payload token_capacity*d*R/8, no metadata
+ *   BLOCK_UNIFORM  payload token_capacity*d*bits/8, metadata 8 B per block
+ *                  (fp32 min, fp32 step)
+ *   KIVI           payload (token_capacity-residual)*d*bits/8 + residual*d*
+ *                  sizeof(storage), metadata 8 B per group of block_tokens
+ *   NONE           payload token_capacity*d*4 (gauged fp32), no metadata
+ * header = CG_HEADER_BYTES * layers * kv.  Any output pointer may be NULL.
+ */
+int cg_encoded_bytes(const cg_shape *shape, const cg_codec *codec, uint64_t *payload_bytes,
+                     uint64_t *meta_bytes, uint64_t *header_bytes);
+
+/*
+ * Gauge + encode rows [t0, t0+nt) of every field (evaluation protocol: every
+ * new KV token passes through gauge -> backend; rolling compressed history).
+ *   kv       device, storage format, KV layout above (read only)
+ *   payload  device, >= payload_bytes of cg_encoded_bytes; block rows of a
+ *            field sit at fixed offsets, so appends (t0 > 0) only write the
+ *            rows they encode
+ *   meta     device metadata buffer (quantizers), or NULL when meta_cap == 0
+ * ZFP: t0, nt multiples of 4.  BLOCK_UNIFORM: multiples of block_tokens.
+ * KIVI: t0 == 0 and nt == tokens (whole fields).  t0 + nt <= tokens.
+ */
+int cg_encode(const cg_shape *shape, const void *kv, const cg_gauge *gauge,
+              const cg_codec *codec, int64_t t0, int64_t nt, void *payload,
+              uint64_t payload_cap, void *meta, uint64_t meta_cap, void *stream);
+
+/*
+ * Decode + inverse gauge rows [t0, t0+nt) of every field into kv_out
+ * (storage format, KV layout; only those rows are written).  Decoding reads
+ * exactly the bits each block owns, so any payload content decodes without
+ * out-of-bounds access.  Same alignment rules as cg_encode.
+ */
+int cg_decode(const cg_shape *shape, const void *payload, uint64_t payload_cap,
+              const void *meta, uint64_t meta_cap, const cg_gauge *gauge,
+              const cg_codec *codec, int64_t t0, int64_t nt, void *kv_out, void *stream);
+
+/* cg_encode of rows [0, tokens) followed by cg_decode of the same rows. */
+int cg_roundtrip(const cg_shape *shape, const void *kv_in, const cg_gauge *gauge,
+                 const cg_codec *codec, void *payload, uint64_t payload_cap, void *meta,
+                 uint64_t meta_cap, void *kv_out, void *stream);
+
+/*
+ * Gauge-fit statistics (frequency objective, arXiv page) of every field over
+ * rows [0, tokens): X' = G X with G = exp(A - A^T) per group (built here in
+ * fp64 and rounded to fp32), orthonormal 2D DCT-II U of each T_b x head_dim
+ * block, E = U^2, r_uv = sqrt((u/(T_b-1))^2 + (v/(d-1))^2)/sqrt(2),
+ * L_freq = mean over blocks of sum(r E)/sum(E) (0 for an all-zero block),
+ * L_rate = mean over coefficients of log(1 + |U|/tau),
+ * L = lambda_f L_freq + lambda_r L_rate, per field.
+ *   kv         device, storage format, KV layout (tokens % T_b == 0)
+ *   g          16 (built); A_host fp64 [layers][kv][heads][d/g][g][g]
+ *   T_b        16 (built)
+ *   workspace  device scratch of >= cg_stats_workspace_bytes() bytes
+ *   out_host   host cg_stats[n_fields]
+ *   dA_host    host fp64 [n_fields][d/g][g][g] gradient of each field's L
+ *              with respect to its A (through the Frechet derivative of exp),
+ *              or NULL to skip the gradient
+ * Synchronous: returns after the results are in host memory.
+ */
+int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t g, const double *A_host,
+                       int32_t T_b, float tau, float lambda_f, float lambda_r, void *workspace,
+                       size_t ws_bytes, cg_stats *out_host, double *dA_host, void *stream);
+
+/* Device scratch needed by cg_gauge_fit_stats (host only). */
+int cg_stats_workspace_bytes(const cg_shape *shape, int32_t g, int32_t T_b, size_t *bytes);
+
+/*
+ * G = exp(A - A^T) for n matrices of size g x g (gauge parameterization,
+ * arXiv page): host fp64 scaling and squaring with a [13/13] Pade
+ * approximant, rounded to fp32.  A_host fp64 [n][g][g], G_host fp32
+ * [n][g][g] (both host).  Synchronous.
+ */
+int cg_gauge_from_skew(int64_t n, int32_t g, const double *A_host, float *G_host);
+
+/*
+ * Apply the gauge (direction 0: G, 1: G^T) to rows [0, tokens) of every
+ * field with the same device routine the fused kernels use, writing fp32
+ * [fields][token_capacity][head_dim] to `out` (device).  Exported so the
+ * gauge stage can be checked on its own.
+ */
+int cg_gauge_apply(const cg_shape *shape, const void *kv, const cg_gauge *gauge,
+                   int32_t direction, float *out, void *stream);
+
+/* Write the fixed-size shape header of one (layer, kv) tensor into a host
+   buffer of >= CG_HEADER_BYTES bytes. */
+int cg_write_header(const cg_shape *shape, const cg_codec *codec, int32_t layer, int32_t kv,
+                    void *header_host, uint64_t cap);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char *cg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CODEC_GAUGE_H */

@@ -1,0 +1,117 @@
+"""CPU-side contract of libcodecgauge.so: it loads, exports every symbol the
+header declares, validates arguments on the host before any device work,
+counts bytes exactly, and builds gauges with its own fp64 matrix exponential
+(checked against the oracle's).  No device work is started here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from fixed_rate_compression_amd import binding as cg
+from fixed_rate_compression_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "codec_gauge.h")).read()
+    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(cg_\w+)\(", txt, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = cg.lib()
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(cg.EXPORTED)
+
+
+def test_encoded_bytes_exact():
+    # Llama-3-8B-class cache at 3, 4, 6 b/v: payload = rate x values / 8
+    shape = cg.make_shape(32, 2, 1, 8, 32768, 32768, 128, cg.CG_DTYPE_BF16)
+    N = 32 * 2 * 8 * 32768 * 128
+    for R in (2, 3, 4, 6, 8):
+        p, m, h = cg.cg_encoded_bytes(shape, cg.make_codec(cg.CG_BACKEND_ZFP, R))
+        assert p == N * R // 8 and m == 0 and h == 64 * 32 * 2
+        assert abs(8.0 * p / N - R) == 0.0
+
+
+def test_encoded_bytes_quantizers():
+    # block-uniform 3-bit, 64-token blocks: 8 B of metadata per block
+    shape3 = cg.make_shape(32, 2, 1, 8, 131072, 131072, 128, cg.CG_DTYPE_BF16)
+    p, m, _ = cg.cg_encoded_bytes(shape3, cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64))
+    N3 = 512 * 131072 * 128
+    assert p == N3 * 3 // 8 and m == 512 * (131072 // 64) * 8
+    # KIVI 4-bit, group 32, 128-token tail in bf16
+    p, m, _ = cg.cg_encoded_bytes(shape3, cg.make_codec(cg.CG_BACKEND_KIVI, 4, 32, 128))
+    assert p == 512 * ((131072 - 128) * 128 * 4 // 8 + 128 * 128 * 2)
+    assert m == 512 * ((131072 - 128) * 128 // 32) * 8
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(head_dim=64), cg.CG_E_UNSUPPORTED),
+    (dict(kv=3), cg.CG_E_SHAPE),
+    (dict(tokens=10, token_capacity=8), cg.CG_E_SHAPE),
+    (dict(dtype=7), cg.CG_E_INVAL),
+])
+def test_shape_validation(bad, code):
+    args = dict(layers=1, kv=2, batch=1, heads=2, tokens=64, token_capacity=64, head_dim=128,
+                dtype=cg.CG_DTYPE_BF16)
+    args.update(bad)
+    shape = cg.CgShape(**args)
+    with pytest.raises(cg.CodecGaugeError) as e:
+        cg.cg_encoded_bytes(shape, cg.make_codec(cg.CG_BACKEND_ZFP, 4))
+    assert e.value.code == code
+
+
+def test_codec_and_row_validation_before_launch():
+    shape = cg.make_shape(1, 2, 1, 2, 64, 64, 128, cg.CG_DTYPE_BF16)
+    dummy = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    L = cg.lib()
+
+    def enc(codec, t0, nt, gauge=cg.make_gauge(0), cap=1 << 30):
+        return L.cg_encode(ctypes.byref(shape), dummy, ctypes.byref(gauge), ctypes.byref(codec),
+                           t0, nt, dummy, cap, None, 0, None)
+
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 5), 0, 64) == cg.CG_E_UNSUPPORTED
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 2, 60) == cg.CG_E_SHAPE
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 68) == cg.CG_E_SHAPE
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, cap=100) == cg.CG_E_SIZE
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, gauge=cg.make_gauge(12, np.zeros(1, np.float32))) == cg.CG_E_SHAPE
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, gauge=cg.CgGauge(16, None)) == cg.CG_E_INVAL
+    assert enc(cg.make_codec(9, 4), 0, 64) == cg.CG_E_INVAL
+    assert "backend" in cg.cg_last_error()
+    # zero rows is a no-op that launches nothing
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 0) == cg.CG_OK
+
+
+def test_gauge_from_skew_matches_oracle():
+    for g in (2, 16, 32, 128):
+        A = synth.gauge_params(g, 3, g)
+        G = cg.cg_gauge_from_skew(A)
+        ref = oracle.gauge_from_skew(A)
+        assert np.max(np.abs(G.astype(np.float64) - ref)) <= 2.0 ** -24 * 2
+        Gd = G.astype(np.float64)
+        for b in range(3):
+            assert np.max(np.abs(Gd[b].T @ Gd[b] - np.eye(g))) < g * 2.0 ** -23
+
+
+def test_gauge_from_skew_closed_form_g2_large_angle():
+    A = np.array([[[0.0, 3.0], [0.0, 0.0]]])
+    G = cg.cg_gauge_from_skew(A)[0]
+    a = 3.0
+    ref = np.array([[np.cos(a), np.sin(a)], [-np.sin(a), np.cos(a)]])
+    assert np.max(np.abs(G - ref)) < 1e-7
+
+
+def test_header_layout():
+    shape = cg.make_shape(2, 2, 1, 8, 100, 128, 128, cg.CG_DTYPE_BF16)
+    h = cg.cg_write_header(shape, cg.make_codec(cg.CG_BACKEND_ZFP, 4), 1, 0)
+    assert len(h) == 64 and h[:4] == b"CGKV"
+    vals = np.frombuffer(h[4:48], np.int32)
+    assert list(vals) == [1, 1, 4, 0, 0, 1, 1, 0, 1, 8, 128]
+    assert list(np.frombuffer(h[48:64], np.int64)) == [100, 128]

@@ -1,0 +1,238 @@
+"""GPU parity of the fused gauge + block-uniform / KIVI-style quantizers and
+their decoders against the oracle ("Codec-Gauge", arXiv HTML,
+evaluation-protocol paragraph).  Bar: bit-exact codes and metadata; for
+g <= 32 the decoded cache is bit-exact too.  For the dense g = 128 gauge
+(MFMA, accumulation order not reproducible on the CPU) parity is staged: the
+oracle quantizes the library's own gauged field (cg_gauge_apply, the same
+device routine as the fused kernel) and must produce the fused kernel's codes
+exactly; the gauge itself and the decoded cache are checked against fp64
+within a tolerance."""
+import numpy as np
+import pytest
+
+import oracle
+from fixed_rate_compression_amd import binding as cg
+from gpu_util import D, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu, n_fields, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def run(x, G, g, codec, L, KV, B, H, T, bf16):
+    t = torch()
+    shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16 if bf16 else cg.CG_DTYPE_F32)
+    pb, mb, _ = cg.cg_encoded_bytes(shape, codec)
+    pay = empty_u8(pb)
+    meta = t.zeros(mb // 4, dtype=t.float32, device="cuda")
+    xd = to_dev(x)
+    Gd = to_dev(np.ascontiguousarray(G)) if G is not None else None
+    gauge = cg.make_gauge(g, Gd)
+    out = t.zeros_like(xd)
+    cg.cg_encode(shape, xd, gauge, codec, 0, T, pay, meta)
+    cg.cg_decode(shape, pay, meta, gauge, codec, 0, T, out)
+    xg = None
+    if g == 128:
+        xg = t.zeros((n_fields(L, KV, B, H), T, D), dtype=t.float32, device="cuda")
+        cg.cg_gauge_apply(shape, xd, gauge, 0, xg)
+        xg = to_host(xg)
+    t.cuda.synchronize()
+    return to_host(pay), to_host(meta), to_host(out), xg
+
+
+def bits_view(a):
+    return a.view(np.uint16) if a.dtype == np.uint16 else a.view(np.uint32)
+
+
+def rel_err(got, ref):
+    return float(np.max(np.abs(got.astype(np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("Bt", [16, 32, 64])
+@pytest.mark.parametrize("g", [0, 16, 32])
+def test_block_uniform_bit_exact(bits, Bt, g):
+    L, KV, B, H, T = 1, 2, 1, 2, 64 * 3 + 16 * (1 if Bt == 16 else 0)
+    T -= T % Bt
+    x = kv_cpu(20 + bits, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    G = gauges_for(30 + g, L, KV, H, g)
+    codec = cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, bits, Bt)
+    pay, meta, out, _ = run(x, G, g, codec, L, KV, B, H, T, True)
+    per, nb = T * D * bits // 8, T // Bt
+    meta = meta.reshape(-1, nb, 2)
+    for f in range(n_fields(L, KV, B, H)):
+        Gf = gauge_of_field(G, f, KV, B, H)
+        xg = oracle.gauge_forward(oracle.to_f32(x[f]), Gf, g)
+        p_ref, m_ref = oracle.bu_encode_field(xg, Bt, bits)
+        assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f
+        assert np.array_equal(meta[f].view(np.uint32), m_ref.view(np.uint32)), f
+        y = oracle.gauge_inverse(oracle.bu_decode_field(p_ref, m_ref, T, D, Bt, bits), Gf, g)
+        assert np.array_equal(out[f], oracle.f32_to_bf16(y)), f
+
+
+def test_block_uniform_small_config_fp32_g16():
+    # 1 layer x K/V x 2 heads x 4096 tokens, fp32, g = 16, 4-bit, 32-token blocks
+    L, KV, B, H, T, bits, Bt = 1, 2, 1, 2, 4096, 4, 32
+    x = kv_cpu(1, L, KV, B, H, T, T, 0.9, 2, bf16=False)
+    G = gauges_for(101, L, KV, H, 16)
+    codec = cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, bits, Bt)
+    pay, meta, out, _ = run(x, G, 16, codec, L, KV, B, H, T, False)
+    per, nb = T * D * bits // 8, T // Bt
+    meta = meta.reshape(-1, nb, 2)
+    for f in range(4):
+        Gf = gauge_of_field(G, f, KV, B, H)
+        xg = oracle.gauge_forward(x[f], Gf, 16)
+        p_ref, m_ref = oracle.bu_encode_field(xg, Bt, bits)
+        assert np.array_equal(pay[f * per:(f + 1) * per], p_ref)
+        assert np.array_equal(meta[f].view(np.uint32), m_ref.view(np.uint32))
+        y = oracle.gauge_inverse(oracle.bu_decode_field(p_ref, m_ref, T, D, Bt, bits), Gf, 16)
+        assert np.array_equal(out[f].view(np.uint32), y.view(np.uint32))
+
+
+def kivi_split(pay, meta, f, T, res, bits, esz):
+    Tq = T - res
+    per = Tq * D * bits // 8 + res * D * esz
+    pf = pay[f * per:(f + 1) * per]
+    mf = meta.reshape(-1, 4 * Tq, 2)[f]
+    return pf[:Tq * D * bits // 8], pf[Tq * D * bits // 8:], mf
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("g", [0, 16, 32])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_kivi_bit_exact(bits, g, bf16):
+    L, KV, B, H, T, res = 1, 2, 2, 1, 352, 128    # 224 quantized rows (7 groups), 3.5 tiles
+    x = kv_cpu(40 + bits, L, KV, B, H, T, T, 0.95, 4, bf16=bf16)
+    G = gauges_for(50 + g, L, KV, H, g)
+    codec = cg.make_codec(cg.CG_BACKEND_KIVI, bits, 32, res)
+    pay, meta, out, _ = run(x, G, g, codec, L, KV, B, H, T, bf16)
+    esz = 2 if bf16 else 4
+    for f in range(n_fields(L, KV, B, H)):
+        kind = (f // (B * H)) % KV
+        Gf = gauge_of_field(G, f, KV, B, H)
+        xg = oracle.gauge_forward(oracle.to_f32(x[f]), Gf, g)
+        p_ref, m_ref, tail = oracle.kivi_encode_field(xg, kind, 32, bits, res)
+        pq, pt, mf = kivi_split(pay, meta, f, T, res, bits, esz)
+        assert np.array_equal(pq, p_ref), f
+        assert np.array_equal(mf.view(np.uint32), m_ref.view(np.uint32)), f
+        tail_st = oracle.from_f32(tail, x.dtype)
+        assert np.array_equal(pt, tail_st.view(np.uint8).reshape(-1)), f
+        yq = oracle.kivi_decode_field(p_ref, m_ref, oracle.to_f32(tail_st), T, D, kind, 32, bits, res)
+        y = oracle.from_f32(oracle.gauge_inverse(yq, Gf, g), x.dtype)
+        assert np.array_equal(bits_view(out[f]), bits_view(y)), f
+
+
+def test_kivi_all_tail_and_constant_groups():
+    L, KV, B, H, T = 1, 2, 1, 1, 128
+    x = kv_cpu(3, L, KV, B, H, T, T, 0.9, 2, bf16=True)
+    codec = cg.make_codec(cg.CG_BACKEND_KIVI, 4, 32, 128)
+    pay, meta, out, _ = run(x, None, 0, codec, L, KV, B, H, T, True)
+    assert np.array_equal(out, x)                     # everything is tail: exact
+    x2 = kv_cpu(4, L, KV, B, H, 160, 160, 0.9, 2, bf16=True)
+    x2[:, :32, :] = x2[:, :1, :]                      # constant key columns over a group
+    x2[:, 40, :] = x2[:, 40, :1]                      # a constant value row
+    codec = cg.make_codec(cg.CG_BACKEND_KIVI, 2, 32, 128)
+    pay, meta, out, _ = run(x2, None, 0, codec, L, KV, B, H, 160, True)
+    for f in range(2):
+        p_ref, m_ref, tail = oracle.kivi_encode_field(oracle.to_f32(x2[f]), f, 32, 2, 128)
+        pq, pt, mf = kivi_split(pay, meta, f, 160, 128, 2, 2)
+        assert np.array_equal(pq, p_ref) and np.array_equal(mf.view(np.uint32), m_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("backend,bits,blk,res", [
+    (cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64, 0),
+    (cg.CG_BACKEND_KIVI, 2, 32, 128),
+    (cg.CG_BACKEND_KIVI, 4, 32, 128),
+])
+def test_dense_gauge_staged(backend, bits, blk, res):
+    L, KV, B, H, T = 1, 2, 1, 2, 1152 + 64 * 3    # more than one 16-tile chunk, ragged chunk
+    x = kv_cpu(60 + bits, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    G = gauges_for(70, L, KV, H, 128)
+    codec = cg.make_codec(backend, bits, blk, res)
+    pay, meta, out, xg = run(x, G, 128, codec, L, KV, B, H, T, True)
+    worst_g, worst_o = 0.0, 0.0
+    for f in range(n_fields(L, KV, B, H)):
+        Gf = gauge_of_field(G, f, KV, B, H).astype(np.float64)
+        ref_g = oracle.gauge_forward_f64(oracle.to_f32(x[f]), Gf, 128)
+        worst_g = max(worst_g, rel_err(xg[f], ref_g))
+        if backend == cg.CG_BACKEND_BLOCK_UNIFORM:
+            p_ref, m_ref = oracle.bu_encode_field(xg[f], blk, bits)
+            per = T * D * bits // 8
+            assert np.array_equal(pay[f * per:(f + 1) * per], p_ref)
+            assert np.array_equal(meta.reshape(-1, T // blk, 2)[f].view(np.uint32), m_ref.view(np.uint32))
+            deq = oracle.bu_decode_field(p_ref, m_ref, T, D, blk, bits)
+        else:
+            kind = (f // (B * H)) % KV
+            p_ref, m_ref, tail = oracle.kivi_encode_field(xg[f], kind, 32, bits, res)
+            pq, pt, mf = kivi_split(pay, meta, f, T, res, bits, 2)
+            assert np.array_equal(pq, p_ref)
+            assert np.array_equal(mf.view(np.uint32), m_ref.view(np.uint32))
+            tail_st = oracle.f32_to_bf16(tail)
+            assert np.array_equal(pt, tail_st.view(np.uint8).reshape(-1))
+            deq = oracle.kivi_decode_field(p_ref, m_ref, oracle.to_f32(tail_st), T, D, kind, 32, bits, res)
+        ref_o = oracle.gauge_inverse_f64(deq, Gf, 128)
+        worst_o = max(worst_o, rel_err(oracle.to_f32(out[f]), ref_o))
+    print(f"dense gauge max rel err {worst_g:.3e}; decoded (bf16) max rel err {worst_o:.3e}")
+    assert worst_g <= 1e-4       # bf16 I/O bar is 1e-2; measured ~1e-5
+    assert worst_o <= 1e-2
+
+
+def test_dense_gauge_apply_fp32_and_inverse():
+    t = torch()
+    L, KV, B, H, T = 1, 1, 1, 2, 200
+    x = kv_cpu(80, L, KV, B, H, T, T, 0.95, 4, bf16=False)
+    G = gauges_for(81, L, KV, H, 128)
+    shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_F32)
+    Gd = to_dev(np.ascontiguousarray(G))
+    gauge = cg.make_gauge(128, Gd)
+    xd = to_dev(x)
+    y = t.zeros_like(xd)
+    z = t.zeros_like(xd)
+    cg.cg_gauge_apply(shape, xd, gauge, 0, y)
+    cg.cg_gauge_apply(shape, y, gauge, 1, z)
+    t.cuda.synchronize()
+    yh, zh = to_host(y), to_host(z)
+    for f in range(2):
+        Gf = gauge_of_field(G, f, KV, B, H).astype(np.float64)
+        ref = oracle.gauge_forward_f64(x[f], Gf, 128)
+        e1 = rel_err(yh[f], ref)
+        e2 = rel_err(zh[f], x[f].astype(np.float64))
+        print(f"fp32 dense gauge rel err {e1:.3e}, round trip {e2:.3e}")
+        assert e1 <= 3e-5 and e2 <= 6e-5
+
+
+def test_full_head_config_sampled_fields():
+    """Full-head gauge workload: 32 layers x K/V x 8 KV heads x 131072 tokens,
+    bf16, dense 128 x 128 gauges; KIVI-style 4-bit (group 32, 128-token tail).
+    Sampled fields of layers 0 and 31 are checked staged (bit-exact codes and
+    metadata on the library's gauged field)."""
+    t = torch()
+    L, KV, B, H, T, res, bits = 32, 2, 1, 8, 131072, 128, 4
+    x = kv_gpu(3, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    G = gauges_for(103, L, KV, H, 128)
+    shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16)
+    codec = cg.make_codec(cg.CG_BACKEND_KIVI, bits, 32, res)
+    pb, mb, _ = cg.cg_encoded_bytes(shape, codec)
+    pay = empty_u8(pb)
+    meta = t.zeros(mb // 4, dtype=t.float32, device="cuda")
+    gauge = cg.make_gauge(128, to_dev(np.ascontiguousarray(G)))
+    cg.cg_encode(shape, x, gauge, codec, 0, T, pay, meta)
+    t.cuda.synchronize()
+    Tq = T - res
+    per = Tq * D * bits // 8 + res * D * 2
+    sub = cg.make_shape(1, 1, 1, 1, T, T, D, cg.CG_DTYPE_BF16)
+    for (l, s, h) in [(0, 0, 0), (0, 1, 7), (31, 0, 3), (31, 1, 5)]:
+        f = (l * KV + s) * H + h
+        xg = t.zeros((1, T, D), dtype=t.float32, device="cuda")
+        cg.cg_gauge_apply(sub, x[f:f + 1].contiguous(), cg.make_gauge(128, gauge._keep[l, s, h].contiguous()), 0, xg)
+        t.cuda.synchronize()
+        xg = to_host(xg)[0]
+        p_ref, m_ref, tail = oracle.kivi_encode_field(xg, s, 32, bits, res)
+        pf = to_host(pay[f * per:(f + 1) * per])
+        assert np.array_equal(pf[:Tq * D * bits // 8], p_ref), (l, s, h)
+        mf = to_host(meta[f * 8 * Tq:(f + 1) * 8 * Tq]).reshape(-1, 2)
+        assert np.array_equal(mf.view(np.uint32), m_ref.view(np.uint32)), (l, s, h)
+        assert np.array_equal(pf[Tq * D * bits // 8:], oracle.f32_to_bf16(tail).view(np.uint8).reshape(-1))
