@@ -10,8 +10,9 @@ concave log-amplitude proxy with tau = 0.04; the objective combines them with
 lambda_f = 1.0 and lambda_r = 0.02 (gauge-training paragraph).  The
 equations themselves are missing from the page; the readings used (DCT-II,
 r_uv = sqrt((u/(T_b-1))^2 + (v/(d-1))^2)/sqrt(2), per-block centroid
-averaged over blocks, rate = mean log(1 + |U|/tau), L = lambda_f L_freq +
-lambda_r L_rate) are listed in the design doc.
+averaged over blocks, rate = mean log(1 + U^2/tau^2) -- smooth in U and
+concave in the energy E = U^2, as the page's energy-preservation argument
+needs -- and L = lambda_f L_freq + lambda_r L_rate) are listed in the design doc.
 
 Everything is fp64 and written as the plain definition: U = C_Tb X'_blk C_d^T
 with explicit DCT matrices, plain sums, and the gradient by the chain rule
@@ -60,7 +61,8 @@ def dct_stats_field(x: np.ndarray, A: np.ndarray | None, g: int, Tb: int = 16,
     gauge exp(A_r - A_r^T) per group (A [d/g, g, g], fp64).  g = 0 means the
     identity gauge.  An explicit G [d/g, g, g] may be given instead of A (then
     no dA is returned).  Returns a dict with per-field L_freq, L_rate, L,
-    sum_E, the per-block centroids, and (grad=True) dG and dA."""
+    sum_E, the per-block centroids, the coefficients U [blocks, Tb, d], and
+    (grad=True) dG and dA."""
     x = np.asarray(x, dtype=np.float64)
     T, d = x.shape
     assert T % Tb == 0
@@ -83,16 +85,16 @@ def dct_stats_field(x: np.ndarray, A: np.ndarray | None, g: int, Tb: int = 16,
     Lb = np.where(SE > 0, SRE / np.where(SE > 0, SE, 1.0), 0.0)
     Nc = U.size
     L_freq = Lb.mean()
-    L_rate = np.log1p(np.abs(U) / tau).sum() / Nc
+    L_rate = np.log1p(U * U / (tau * tau)).sum() / Nc
     out = {"L_freq": float(L_freq), "L_rate": float(L_rate),
            "L": float(lambda_f * L_freq + lambda_r * L_rate),
-           "sum_E": float(SE.sum()), "L_block": Lb}
+           "sum_E": float(SE.sum()), "L_block": Lb, "U": U}
     if not grad:
         return out
     safe = np.where(SE > 0, SE, 1.0)[:, None, None]
     dU = (lambda_f / nb) * np.where(SE[:, None, None] > 0,
                                     2.0 * U * (r[None] - Lb[:, None, None]) / safe, 0.0)
-    dU = dU + (lambda_r / Nc) * np.sign(U) / (tau + np.abs(U))
+    dU = dU + (lambda_r / Nc) * 2.0 * U / (tau * tau + U * U)
     dXp = (Ct.T[None] @ dU @ Cd[None]).reshape(T, d)
     if g == 0:
         out["dG"] = None

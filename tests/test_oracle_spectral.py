@@ -63,12 +63,11 @@ def test_zero_field():
 
 
 def test_rate_proxy_closed_form():
-    # one DC-only block with U00 = c: L_rate = log(1 + |c|/tau) / (16*128)
+    # one DC-only block with U00 = c: L_rate = log(1 + c^2/tau^2) / (16*128)
     c, tau = 3.0, 0.04
     blk = np.full((16, 128), c / np.sqrt(16 * 128))
     st = oracle.dct_stats_field(blk, None, 0, grad=False, tau=tau)
-    # (the other coefficients are DCT round-off, ~1e-17 each)
-    assert abs(st["L_rate"] - np.log1p(c / tau) / (16 * 128)) < 1e-11 * st["L_rate"]
+    assert abs(st["L_rate"] - np.log1p(c * c / (tau * tau)) / (16 * 128)) < 1e-11 * st["L_rate"]
 
 
 def test_centroid_range_and_gauge_energy_invariance():
@@ -114,3 +113,4 @@ def test_gradient_wrt_gauge_finite_differences():
         fd = (oracle.dct_stats_field(x, None, g, Tb=Tb, grad=False, G=Gp)["L"] -
               oracle.dct_stats_field(x, None, g, Tb=Tb, grad=False, G=Gm)["L"]) / (2 * h)
         assert abs(st["dG"][idx] - fd) <= 1e-6 * max(1e-3, abs(fd))
+
