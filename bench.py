@@ -122,12 +122,178 @@ def cpu_baseline(s, n_fields=32):
                        f"inverse round trip, {wall:.2f} s wall on {threads} threads")
 
 
+# ---------------------------------------------------------------------------
+# the other workloads (one JSON line each with --workload all)
+# ---------------------------------------------------------------------------
+
+def _gen(F, T, Tcap, rho, seed, outliers, bf16, scale_fields=None, windows=1):
+    import torch
+
+    from fixed_rate_compression_amd import synth
+    D = 128
+    x = torch.zeros((F * windows, Tcap // windows, D), dtype=torch.bfloat16 if bf16 else torch.float32,
+                    device="cuda")
+    sc = synth.channel_scales_many(seed, range(F), D, outliers)
+    if windows > 1:
+        sc = np.repeat(sc, windows, axis=0)
+    synth.generate_gpu(x, T // windows, rho, seed, np.arange(F * windows), sc)
+    return x.view(F, Tcap, D)
+
+
+def _gauge(L, KV, H, g, seed):
+    import torch
+
+    from fixed_rate_compression_amd import binding as cg
+    from fixed_rate_compression_amd import synth
+    if g == 0:
+        return None, None
+    A = synth.gauge_params(seed, L * KV * H * (128 // g), g)
+    return torch.from_numpy(cg.cg_gauge_from_skew(A)).cuda(), A
+
+
+def _time(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e-3
+
+
+def _codec_line(name, shape, x, G, g, codec, steps, warmup, esz, desc):
+    import torch
+
+    from fixed_rate_compression_amd import binding as cg
+    pb, mb, hb = cg.cg_encoded_bytes(shape, codec)
+    pay = torch.empty(max(pb, 1), dtype=torch.uint8, device="cuda")
+    meta = torch.empty(max(mb // 4, 1), dtype=torch.float32, device="cuda") if mb else None
+    out = torch.empty_like(x)
+    gauge = cg.make_gauge(g, G)
+    T = shape.tokens
+    enc = lambda: cg.cg_encode(shape, x, gauge, codec, 0, T, pay, meta)
+    dec = lambda: cg.cg_decode(shape, pay, meta, gauge, codec, 0, T, out)
+    enc()
+    te = _time(enc, steps, warmup)
+    td = _time(dec, steps, warmup)
+    N = x.numel()
+    alg = N * esz + pb + mb
+    del pay, meta, out
+    torch.cuda.empty_cache()
+    return {"workload": name, "desc": desc, "values": N, "bits_per_value": round(8.0 * (pb + mb + hb) / N, 6),
+            "encode_ms": round(te * 1e3, 4), "decode_ms": round(td * 1e3, 4),
+            "encode_kv_GBs": round(N * esz / te / 1e9, 2), "decode_kv_GBs": round(N * esz / td / 1e9, 2),
+            "encode_hbm_frac": round(alg / te / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_hbm_frac": round(alg / td / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def workload_lines(steps, warmup):
+    import torch
+
+    from fixed_rate_compression_amd import binding as cg
+    from fixed_rate_compression_amd.rolling import RollingHistory
+    lines = []
+    # small cache, fp32: zfp-4 and block-uniform 4-bit (32-token blocks), g = 16
+    L, KV, B, H, T = 1, 2, 1, 2, 4096
+    x = _gen(L * KV * B * H, T, T, 0.9, 1, 2, False)
+    G, _ = _gauge(L, KV, H, 16, 101)
+    sh = cg.make_shape(L, KV, B, H, T, T, 128, cg.CG_DTYPE_F32)
+    for codec, nm in ((cg.make_codec(cg.CG_BACKEND_ZFP, 4), "zfp4"),
+                      (cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, 4, 32), "bu4")):
+        lines.append(_codec_line(f"small_fp32_{nm}", sh, x, G, 16, codec, steps, warmup, 4,
+                                 "1 layer x K/V x 2 heads x 4096 tokens fp32, g=16 (cache-resident)"))
+    del x
+    # Llama-3-8B-class cache at 3 and 6 b/v (4 b/v is the headline line)
+    L, KV, B, H, T = 32, 2, 1, 8, 32768
+    x = _gen(L * KV * B * H, T, T, 0.95, 2, 4, True)
+    G, _ = _gauge(L, KV, H, 16, 102)
+    sh = cg.make_shape(L, KV, B, H, T, T, 128, cg.CG_DTYPE_BF16)
+    for R in (3, 6):
+        lines.append(_codec_line(f"llama8b_zfp{R}", sh, x, G, 16, cg.make_codec(cg.CG_BACKEND_ZFP, R),
+                                 steps, warmup, 2, "32 layers x K/V x 8 heads x 32768 tokens bf16, g=16"))
+    del x
+    torch.cuda.empty_cache()
+    # full-head gauge (g = 128, MFMA): KIVI-2/4 (group 32, 128-token tail), block-uniform 3-bit
+    L, KV, B, H, T = 32, 2, 1, 8, 131072
+    x = _gen(L * KV * B * H, T, T, 0.95, 3, 4, True)
+    G, _ = _gauge(L, KV, H, 128, 103)
+    sh = cg.make_shape(L, KV, B, H, T, T, 128, cg.CG_DTYPE_BF16)
+    for codec, nm in ((cg.make_codec(cg.CG_BACKEND_KIVI, 2, 32, 128), "kivi2"),
+                      (cg.make_codec(cg.CG_BACKEND_KIVI, 4, 32, 128), "kivi4"),
+                      (cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64), "bu3")):
+        lines.append(_codec_line(f"fullhead_{nm}", sh, x, G, 128, codec, max(3, steps // 4), 1, 2,
+                                 "32 layers x K/V x 8 heads x 131072 tokens bf16, dense g=128"))
+    del x
+    torch.cuda.empty_cache()
+    # rolling history: 64 seq x 28 layers x 4 heads, 8192 -> 8192 + n tokens, g = 32, 4 b/v
+    L, KV, B, H, T0, nsteps = 28, 2, 64, 4, 8192, 64
+    cap = T0 + 256
+    raw = _gen(L * KV * B * H, T0 + nsteps, cap, 0.95, 4, 4, True)
+    G, _ = _gauge(L, KV, H, 32, 104)
+    rh = RollingHistory(L, KV, B, H, cap, cg.make_gauge(32, G), 4)
+    rh.prefill(raw, T0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(nsteps):
+        rh.append(raw[:, T0 + k])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / nsteps
+    Nmean = L * KV * B * H * 128 * (T0 + nsteps / 2)
+    lines.append({"workload": "rolling_g32_zfp4", "desc": "64 seq x 28 layers x 4 heads, history 8192+, "
+                  f"{nsteps} appends (encode each completed 4-token block, decode whole history)",
+                  "ms_per_step": round(ms, 4), "history_values_mean": int(Nmean),
+                  "decode_kv_GBs": round(Nmean * 2 / (ms * 1e-3) / 1e9, 2),
+                  "decode_hbm_frac": round(Nmean * 2.5 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    del raw, rh
+    torch.cuda.empty_cache()
+    # 27B-class cache (zfp-3, g = 16) + gauge-fit statistics over 64 x 4096-token windows
+    L, KV, B, H, T = 46, 2, 1, 16, 65536
+    F = L * KV * B * H
+    x = _gen(F, T, T, 0.95, 5, 4, True)
+    G, A = _gauge(L, KV, H, 16, 105)
+    sh = cg.make_shape(L, KV, B, H, T, T, 128, cg.CG_DTYPE_BF16)
+    lines.append(_codec_line("27b_zfp3", sh, x, G, 16, cg.make_codec(cg.CG_BACKEND_ZFP, 3), steps, warmup, 2,
+                             "46 layers x K/V x 16 heads x 65536 tokens bf16, g=16"))
+    del x
+    torch.cuda.empty_cache()
+    W, Tw = 64, 4096
+    xw = _gen(F, W * Tw, W * Tw, 0.95, 205, 4, True, windows=W)
+    shw = cg.make_shape(L, KV, B, H, W * Tw, W * Tw, 128, cg.CG_DTYPE_BF16)
+    ws = torch.empty(cg.cg_stats_workspace_bytes(shw, 16, 16), dtype=torch.uint8, device="cuda")
+    for _ in range(1):
+        cg.cg_gauge_fit_stats(shw, xw, 16, A, 16, 0.04, 1.0, 0.02, ws, grad=True)
+    t0 = time.perf_counter()
+    st, dA = cg.cg_gauge_fit_stats(shw, xw, 16, A, 16, 0.04, 1.0, 0.02, ws, grad=True)
+    wall = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    cg.cg_gauge_fit_stats(shw, xw, 16, A, 16, 0.04, 1.0, 0.02, ws, grad=False)
+    wall_nograd = time.perf_counter() - t1
+    N = xw.numel()
+    lines.append({"workload": "27b_stats_windows", "desc": "1472 heads x 64 windows x 4096 tokens bf16, "
+                  "g=16, T_b=16, tau=0.04; statistics + dL/dA (synchronous, includes host Frechet)",
+                  "values": N, "wall_s_with_grad": round(wall, 4), "wall_s_stats_only": round(wall_nograd, 4),
+                  "kv_GBs_with_grad": round(N * 2 / wall / 1e9, 2),
+                  "kv_GBs_stats_only": round(N * 2 / wall_nograd / 1e9, 2),
+                  "mean_L_freq": float(np.mean(st["L_freq"])), "mean_L": float(np.mean(st["L"]))})
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "all"],
+                    help="all: also print one JSON line per other workload after the main line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain device copy of the KV tensor (counter calibration)")
     args = ap.parse_args()
@@ -189,6 +355,11 @@ def main():
         log("cpu baseline: oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(s)
     print(json.dumps(res), flush=True)
+    if args.workload == "all":
+        del s
+        torch.cuda.empty_cache()
+        for line in workload_lines(max(3, args.steps // 2), 1):
+            print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -86,33 +86,25 @@ __host__ __device__ __forceinline__ void inv_xform4(int32_t &a, int32_t &b, int3
 // w[0..15] (row i = word i, column c = bit c of the half).  Afterwards the low
 // half of w[k] is the word whose bit i was bit k of the old w[i], and the high
 // half likewise for bit 16 + k.  The transform is an involution.
+__host__ __device__ __forceinline__ void swap_stage(uint32_t &a, uint32_t &b, int s, uint32_t m) {
+  // exchange the columns selected by (m << s) of row a with the columns m of row b
+  const uint32_t na = (a & ~(m << s)) | ((b << s) & (m << s));
+  const uint32_t nb = (b & ~m) | ((a >> s) & m);
+  a = na;
+  b = nb;
+}
+
 __host__ __device__ __forceinline__ void transpose16x2(uint32_t (&w)[16]) {
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    uint32_t t = ((w[i] >> 8) ^ w[i + 8]) & 0x00FF00FFu;
-    w[i + 8] ^= t;
-    w[i] ^= t << 8;
-  }
+  for (int i = 0; i < 8; i++) swap_stage(w[i], w[i + 8], 8, 0x00FF00FFu);
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    if (i & 4) continue;
-    uint32_t t = ((w[i] >> 4) ^ w[i + 4]) & 0x0F0F0F0Fu;
-    w[i + 4] ^= t;
-    w[i] ^= t << 4;
-  }
+  for (int i = 0; i < 16; i++)
+    if (!(i & 4)) swap_stage(w[i], w[i + 4], 4, 0x0F0F0F0Fu);
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    if (i & 2) continue;
-    uint32_t t = ((w[i] >> 2) ^ w[i + 2]) & 0x33333333u;
-    w[i + 2] ^= t;
-    w[i] ^= t << 2;
-  }
+  for (int i = 0; i < 16; i++)
+    if (!(i & 2)) swap_stage(w[i], w[i + 2], 2, 0x33333333u);
 #pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    uint32_t t = ((w[i] >> 1) ^ w[i + 1]) & 0x55555555u;
-    w[i + 1] ^= t;
-    w[i] ^= t << 1;
-  }
+  for (int i = 0; i < 16; i += 2) swap_stage(w[i], w[i + 1], 1, 0x55555555u);
 }
 
 __host__ __device__ __forceinline__ int ctz32(uint32_t x) {  // x != 0
@@ -140,6 +132,37 @@ __host__ __device__ __forceinline__ void put(uint64_t (&acc)[Rate<R>::kAcc], int
   }
 }
 
+// OR a 64-bit code into the block's bits at `pos` (bits at or past 16R are
+// dropped by the final mask).
+template <int R>
+__host__ __device__ __forceinline__ void put64(uint64_t (&acc)[Rate<R>::kAcc], int pos,
+                                               uint64_t code) {
+  constexpr int NA = Rate<R>::kAcc;
+#pragma unroll
+  for (int a = 0; a < NA; a++) {
+    const int sh = pos - 64 * a;
+    if (sh >= 0 && sh < 64)
+      acc[a] |= code << sh;
+    else if (sh < 0 && sh > -64)
+      acc[a] |= code >> (-sh);
+  }
+}
+
+// 8-bit expansion table entry: every 1 followed by an inserted 1, LSB first
+__host__ __device__ constexpr uint16_t dbl8_entry(uint32_t s) {
+  uint32_t out = 0;
+  int p = 0;
+  for (int i = 0; i < 8; i++) {
+    if ((s >> i) & 1u) {
+      out |= 3u << p;
+      p += 2;
+    } else {
+      p += 1;
+    }
+  }
+  return (uint16_t)out;
+}
+
 // 32 stream bits starting at `pos` (< 16R); bits past 16R read as 0
 template <int R>
 __host__ __device__ __forceinline__ uint32_t window(const uint64_t (&acc)[Rate<R>::kAcc],
@@ -161,7 +184,8 @@ __host__ __device__ __forceinline__ uint32_t window(const uint64_t (&acc)[Rate<R
 // Encode 16 fp32 values v[4j + i] (j = token row, i = channel) at rate R.
 template <int R>
 __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
-                                                      uint64_t (&acc)[Rate<R>::kAcc]) {
+                                                      uint64_t (&acc)[Rate<R>::kAcc],
+                                                      const uint16_t *__restrict__ dbl) {
   constexpr int NA = Rate<R>::kAcc;
   constexpr int LIMIT = Rate<R>::kBits;
 #pragma unroll
@@ -169,12 +193,10 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
 
   // block exponent from the largest magnitude (bit patterns of |x| order like
   // the values): frexp exponent = biased exponent - 126, clamped at -126
-  uint32_t mx = 0;
+  float fm = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 16; k++) {
-    uint32_t m = __builtin_bit_cast(uint32_t, v[k]) & 0x7FFFFFFFu;
-    mx = m > mx ? m : mx;
-  }
+  for (int k = 0; k < 16; k++) fm = fmaxf(fm, fabsf(v[k]));
+  const uint32_t mx = __builtin_bit_cast(uint32_t, fm);
   if (mx == 0) return;
   int ebiased = (int)(mx >> 23);
   int emax = ebiased ? ebiased - 126 : -126;
@@ -202,39 +224,37 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
   for (int k = 0; k < 16; k++) u[k] <<= s;
   transpose16x2(u);                     // u[m]: plane m (low), plane m+16 (high)
 
+  // Planes from the top, one fixed-cost step each.  For plane word w with n
+  // coefficients already significant the code is: the n verbatim bits, then
+  // (if n < 16) either a failed group test (0) or a 1 followed by the bits
+  // w[n..min(hb,14)] with every 1 among them followed by one more bit -- 1 if
+  // another one follows in the plane, 0 after the last one (hb = highest set
+  // bit; a one at position 15 is implied and not sent).  The "1 after every
+  // 1" expansion comes from the 256-entry table `dbl`.
   int n = 0;                            // coefficients already significant
 #pragma unroll
   for (int j = 0; j < 32; j++) {        // plane 31-j of the shifted words
-    if (j > 31 - s || pos >= LIMIT) break;
-    const uint32_t w = j < 16 ? (u[15 - j] >> 16) : (u[31 - j] & 0xFFFFu);
-    // verbatim bits of the significant coefficients
-    put<R>(acc, pos, w & ((1u << n) - 1u));
-    pos += n;
-    if (n < 16) {
-      if ((w >> n) == 0) {
-        pos += 1;                       // failed group test (a 0 bit)
-      } else {
-        int cur = n;
-        for (;;) {
-          const int p = cur + ctz32(w >> cur);   // next one at or after cur
-          if (p >= 15) {                // scan reaches 15: the one is implied
-            put<R>(acc, pos, 1u);       // group test, then 15-cur zeros
-            pos += 16 - cur;
-            cur = 16;
-            break;
-          }
-          const int gap = p - cur;      // group test 1, gap zeros, the 1
-          put<R>(acc, pos, 1u | (1u << (gap + 1)));
-          pos += gap + 2;
-          cur = p + 1;
-          if ((w >> cur) == 0) {        // next group test fails
-            pos += 1;
-            break;
-          }
-          if (pos >= LIMIT) break;
-        }
-        n = cur;
+    if (pos < LIMIT) {                  // (no early exit: keeps the loop unrollable)
+      const uint32_t w = j < 16 ? (u[15 - j] >> 16) : (u[31 - j] & 0xFFFFu);
+      const uint32_t rest = w >> n;
+      const int hb = 31 - clz32(w | 1u);
+      const int e14 = hb < 14 ? hb : 14;
+      const int L = e14 - n + 1;          // scanned positions n..e14 (when rest != 0)
+      const uint32_t S = L > 0 ? (rest & ((1u << L) - 1u)) : 0u;
+      const uint32_t lo = S & 0xFFu, hi = S >> 8;
+      const int pclo = __builtin_popcount(lo), pc = pclo + __builtin_popcount(hi);
+      const uint32_t D = (uint32_t)dbl[lo] | ((uint32_t)dbl[hi] << (8 + pclo));
+      uint32_t code = 1u | (D << 1);
+      if (hb <= 14) code &= ~(1u << (L + pc));
+      int len = 1 + L + pc;
+      if (rest == 0) {
+        code = 0u;
+        len = n < 16 ? 1 : 0;
       }
+      const uint64_t full = (uint64_t)(w & ((1u << n) - 1u)) | ((uint64_t)code << n);
+      put64<R>(acc, pos, full);
+      pos += n + len;
+      n = rest ? hb + 1 : n;
     }
   }
   if (LIMIT % 64) acc[NA - 1] &= (~0ull) >> (64 - LIMIT % 64);
@@ -262,7 +282,7 @@ __host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate
   int n = 0;
 #pragma unroll
   for (int j = 0; j < 32; j++) {
-    if (j > 31 - s || pos >= LIMIT) break;
+    if (j > 31 - s || pos >= LIMIT) continue;  // (no early exit: keeps the loop unrollable)
     uint32_t x = n ? (window<R>(acc, pos) & ((1u << n) - 1u)) : 0u;
     pos += n;
     while (n < 16 && pos < LIMIT) {

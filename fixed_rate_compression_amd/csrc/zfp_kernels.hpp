@@ -61,12 +61,14 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
                                                    uint8_t *__restrict__ payload, TileArgs a) {
   __shared__ float xs[TILE_T * PITCH];
   __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
+  __shared__ uint16_t dbl[256];
   const int64_t field = (int64_t)blockIdx.x / a.tiles;
   const int tile = (int)((int64_t)blockIdx.x % a.tiles);
   const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
   const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
   const int64_t row0 = field * a.tcap + tb;
   const size_t esz = BF16 ? 2 : 4;
+  dbl[threadIdx.x] = cgz::dbl8_entry(threadIdx.x);
   load_tile<BF16>((const uint8_t *)kv + (size_t)row0 * D * esz, nrows, xs);
   __syncthreads();
   if constexpr (G != 0) {
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
       v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
     }
     uint64_t acc[cgz::Rate<R>::kAcc];
-    cgz::encode_block<R>(v, acc);
+    cgz::encode_block<R>(v, acc, dbl);
     stage_block<R>(os, b, acc);
   }
   __syncthreads();

@@ -21,8 +21,8 @@
  *    fixed shape header).
  *  - Frequency objective (arXiv page): orthonormal 2D DCT of T_b x d_l
  *    token-channel blocks of X' = G X, spectral-centroid loss L_freq and
- *    log-amplitude rate proxy L_rate (tau = 0.04), combined with lambda_f,
- *    lambda_r; the gauge is trained on it with AdamW.
+ *    smooth log-amplitude rate proxy L_rate (tau = 0.04), combined with
+ *    lambda_f, lambda_r; the gauge is trained on it with AdamW.
  *
  * Conventions for every entry point:
  *  - Device pointers point to memory the caller allocated on the current HIP
@@ -109,7 +109,7 @@ typedef struct cg_codec {
 
 typedef struct cg_stats {
   double L_freq; /* mean over blocks of sum(r E) / sum(E) */
-  double L_rate; /* mean over coefficients of log(1 + |U| / tau) */
+  double L_rate; /* mean over coefficients of log(1 + U^2 / tau^2) */
   double L;      /* lambda_f L_freq + lambda_r L_rate */
   double sum_E;  /* total DCT energy (equals the field energy, Parseval) */
 } cg_stats;
@@ -165,7 +165,8 @@ int cg_roundtrip(const cg_shape *shape, const void *kv_in, const cg_gauge *gauge
  * fp64 and rounded to fp32), orthonormal 2D DCT-II U of each T_b x head_dim
  * block, E = U^2, r_uv = sqrt((u/(T_b-1))^2 + (v/(d-1))^2)/sqrt(2),
  * L_freq = mean over blocks of sum(r E)/sum(E) (0 for an all-zero block),
- * L_rate = mean over coefficients of log(1 + |U|/tau),
+ * L_rate = mean over coefficients of log(1 + U^2/tau^2) (smooth in U,
+ * concave in the energy U^2),
  * L = lambda_f L_freq + lambda_r L_rate, per field.
  *   kv         device, storage format, KV layout (tokens % T_b == 0)
  *   g          16 (built); A_host fp64 [layers][kv][heads][d/g][g][g]
