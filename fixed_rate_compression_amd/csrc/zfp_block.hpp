@@ -282,27 +282,23 @@ __host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate
   int n = 0;
 #pragma unroll
   for (int j = 0; j < 32; j++) {
-    if (j > 31 - s || pos >= LIMIT) continue;  // (no early exit: keeps the loop unrollable)
-    uint32_t x = n ? (window<R>(acc, pos) & ((1u << n) - 1u)) : 0u;
-    pos += n;
-    while (n < 16 && pos < LIMIT) {
-      const uint32_t t = window<R>(acc, pos) & 1u;
-      pos += 1;
-      if (!t) break;
-      const int lim0 = 15 - n, room = LIMIT - pos;
-      const int lim = lim0 < room ? lim0 : room;
-      const uint32_t ww = lim > 0 ? window<R>(acc, pos) : 0u;
-      const int z = ww ? ctz32(ww) : 32;
-      int gap;
-      if (z < lim) {
-        gap = z;
-        pos += z + 1;
-      } else {
-        gap = lim;
-        pos += lim;
+    uint32_t x = 0u;                    // plane word 31-j of the shifted words
+    if (j <= 31 - s && pos < LIMIT) {   // (no early exit: keeps the loop unrollable)
+      x = window<R>(acc, pos) & ((1u << n) - 1u);   // verbatim bits (n <= 16)
+      pos += n;
+      // group tests, each positive one followed by a unary scan
+      while (n < 16 && pos < LIMIT) {
+        const uint32_t win = window<R>(acc, pos);
+        pos += 1;
+        if (!(win & 1u)) break;         // failed group test: plane done
+        const int room = LIMIT - pos, lim0 = 15 - n;
+        const uint32_t lim = (uint32_t)(lim0 < room ? lim0 : room);
+        const uint32_t z = (win >> 1) ? (uint32_t)ctz32(win >> 1) : 32u;
+        const uint32_t gap = z < lim ? z : lim;
+        pos += (int)gap + (z < lim ? 1 : 0);
+        x |= 1u << (n + (int)gap);      // also when the budget ends inside the scan
+        n += (int)gap + 1;
       }
-      x |= 1u << (n + gap);
-      n += gap + 1;
     }
     if (j < 16)
       w[15 - j] |= x << 16;
