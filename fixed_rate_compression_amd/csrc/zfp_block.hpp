@@ -260,6 +260,60 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
   if (LIMIT % 64) acc[NA - 1] &= (~0ull) >> (64 - LIMIT % 64);
 }
 
+// Group-test/scan part of one bit plane, read bit-parallel.  On entry `pos`
+// is at the plane's first group test and `n` (< 16) coefficients are
+// significant.  The code there is a run of pairs "1 0^gap 1" (a positive
+// group test, zeros scanned over, the newly significant coefficient's 1) and
+// ends with a 0 (failed test), or with the budget, or with the implicit 1 of
+// coefficient 15 (a scan reaching index 15 reads no bit).  With P the
+// inclusive prefix parity of the window, a 1 at odd parity is a test, a 1 at
+// even parity ends a scan and a 0 at even parity is the failed test; the k-th
+// scan-ending 1 (k from 0) at window bit t is coefficient n + t - (k + 1).
+// Returns the new coefficients' bits relative to n; advances pos and n.
+template <int R>
+__host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Rate<R>::kAcc],
+                                                        int &pos, int &n) {
+  constexpr int LIMIT = Rate<R>::kBits;
+  const uint32_t W = window<R>(acc, pos);
+  uint32_t P = W;
+  P ^= P << 1;
+  P ^= P << 2;
+  P ^= P << 4;
+  P ^= P << 8;
+  P ^= P << 16;
+  const uint32_t tests = W & P;
+  const uint32_t fails = ~(W | P);
+  const uint32_t ef = fails ? (uint32_t)ctz32(fails) : 32u;  // first failed test
+  const uint32_t room = (uint32_t)(LIMIT - pos);              // >= 1
+  const uint32_t m = 15u - (uint32_t)n;                       // index of coefficient 15
+  // a plane's group part never spans more than 2m+1 bits
+  uint32_t E = ef < room ? ef : room;
+  E = E < 2u * m + 2u ? E : 2u * m + 2u;                      // <= 32
+  const uint32_t below = E >= 32u ? ~0u : (1u << E) - 1u;
+  uint32_t term = W & ~P & below;
+  uint32_t y = 0u, bias = 1u;
+  while (term) {                        // one step per newly significant coefficient
+    const uint32_t low = term & (0u - term);
+    y |= low >> bias;
+    term ^= low;
+    bias += 1u;
+  }
+  const uint32_t cnt = E - (uint32_t)__builtin_popcount(tests & below);  // bits scanned before E
+  uint32_t used;
+  if (cnt > m) {                        // the scan reaches coefficient 15: implicit 1
+    y = (y & ((1u << m) - 1u)) | (1u << m);
+    used = m + (uint32_t)__builtin_popcount(y);
+  } else if (ef < room) {               // failed group test at ef
+    used = ef + 1u;
+  } else {                              // budget ends at room (<= ef <= 32)
+    if ((P >> (room - 1u)) & 1u) y |= 1u << cnt;   // inside a scan: set the scanned index
+    used = room;
+  }
+  pos += (int)used;
+  n += y ? 32 - clz32(y) : 0;           // every index up to the last new one is now verbatim
+  return y;
+}
+
 // Decode one block of 16R bits into 16 fp32 values v[4j + i].
 template <int R>
 __host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate<R>::kAcc],
@@ -286,19 +340,8 @@ __host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate
     if (j <= 31 - s && pos < LIMIT) {   // (no early exit: keeps the loop unrollable)
       x = window<R>(acc, pos) & ((1u << n) - 1u);   // verbatim bits (n <= 16)
       pos += n;
-      // group tests, each positive one followed by a unary scan
-      while (n < 16 && pos < LIMIT) {
-        const uint32_t win = window<R>(acc, pos);
-        pos += 1;
-        if (!(win & 1u)) break;         // failed group test: plane done
-        const int room = LIMIT - pos, lim0 = 15 - n;
-        const uint32_t lim = (uint32_t)(lim0 < room ? lim0 : room);
-        const uint32_t z = (win >> 1) ? (uint32_t)ctz32(win >> 1) : 32u;
-        const uint32_t gap = z < lim ? z : lim;
-        pos += (int)gap + (z < lim ? 1 : 0);
-        x |= 1u << (n + (int)gap);      // also when the budget ends inside the scan
-        n += (int)gap + 1;
-      }
+      const int n0 = n;
+      if (n < 16 && pos < LIMIT) x |= group_part<R>(acc, pos, n) << n0;
     }
     if (j < 16)
       w[15 - j] |= x << 16;
