@@ -35,8 +35,15 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two values -> packed bf16 pair (lo in bits 0..15) with the gfx950 pair
+// conversion (v_cvt_pk_bf16_f32).  For every non-NaN fp32 input it returns
+// exactly bf16_rne (checked exhaustively over all 2^32 bit patterns on an
+// MI355X), one instruction per pair instead of five.
+typedef __bf16 cg_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float cg_f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  const cg_f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, cg_bf16x2_t));
 }
 
 // rows [0, nrows) of a [rows][128] storage-format array -> LDS fp32 tile
