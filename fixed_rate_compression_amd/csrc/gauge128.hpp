@@ -77,11 +77,84 @@ __device__ __forceinline__ void load_g128(const float *__restrict__ Gf, G128Frag
   }
 }
 
-// In-place X <- X G^T (forward fragments) or X G (inverse fragments) on the
-// 64-row LDS tile.  EXACT: every tile value is a bf16 number (X_lo = 0).
-// Contains two workgroup barriers.
+// The tile as MFMA A operands: bf16 "hi" and "lo" parts of its 64 x 128
+// values in LDS, row pitch HP bf16 (272 B = 17 x 16 B, so the 16 lanes of a
+// fragment read, 16 B each from 16 rows, hit 64 distinct banks).  Every tile
+// value is split exactly once, by the thread that produced it; the waves then
+// read their fragments with plain 16-B loads.  The fp32 result tile (pitch
+// PITCH floats) overlays the same LDS after all waves have read the operands.
+constexpr int HP = 136;
+constexpr int SPLIT_BYTES = 2 * TILE_T * HP * 2;                 // hi + lo tiles
+constexpr int TILE_BYTES = TILE_T * PITCH * 4;                   // fp32 tile
+constexpr int LDS_TILE_BYTES = SPLIT_BYTES > TILE_BYTES ? SPLIT_BYTES : TILE_BYTES;
+
+// two values -> packed bf16 hi parts and packed bf16 remainders (each part
+// round-to-nearest-even, as split_bf16)
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
+
+// One tile of a storage-format [rows][128] array held in registers between
+// its global load and its LDS store, so that a workgroup can fetch tile i+1
+// while the matrix cores work on tile i.  Thread i holds the 16-B pieces
+// i, i + NT, ... (coalesced); rows past nrows read as zero.
+template <bool BF16>
+struct TileFetch {
+  static constexpr int N = BF16 ? 4 : 8;   // 16-B pieces per thread
+  uint4 r[N];
+
+  __device__ __forceinline__ void fetch(const void *__restrict__ src, int nrows) {
+    const uint4 *s = (const uint4 *)src;
+#pragma unroll
+    for (int k = 0; k < N; k++) {
+      const int i = threadIdx.x + NT * k;
+      const int row = BF16 ? (i >> 4) : (i >> 5);
+      r[k] = row < nrows ? s[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  // -> split tiles (bf16 inputs are their own hi part; lo is not used)
+  __device__ __forceinline__ void put(uint16_t *sh, uint16_t *sl) const {
+#pragma unroll
+    for (int k = 0; k < N; k++) {
+      const int i = threadIdx.x + NT * k;
+      if (BF16) {
+        *(uint4 *)(sh + (i >> 4) * HP + 8 * (i & 15)) = r[k];
+      } else {
+        uint2 h, l;
+        split_pair(__uint_as_float(r[k].x), __uint_as_float(r[k].y), h.x, l.x);
+        split_pair(__uint_as_float(r[k].z), __uint_as_float(r[k].w), h.y, l.y);
+        *(uint2 *)(sh + (i >> 5) * HP + 4 * (i & 31)) = h;
+        *(uint2 *)(sl + (i >> 5) * HP + 4 * (i & 31)) = l;
+      }
+    }
+  }
+};
+
+// the 32 values of row t, channels 32 j .. 32 j + 31 -> split tiles
+__device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j, const float (&v)[32]) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint4 h, l;
+    split_pair(v[8 * q], v[8 * q + 1], h.x, l.x);
+    split_pair(v[8 * q + 2], v[8 * q + 3], h.y, l.y);
+    split_pair(v[8 * q + 4], v[8 * q + 5], h.z, l.z);
+    split_pair(v[8 * q + 6], v[8 * q + 7], h.w, l.w);
+    *(uint4 *)(sh + t * HP + 32 * j + 8 * q) = h;
+    *(uint4 *)(sl + t * HP + 32 * j + 8 * q) = l;
+  }
+}
+
+// X G^T (forward fragments) or X G (inverse fragments) of the split tile into
+// the fp32 tile xs, which may overlay sh/sl.  EXACT: every tile value is a
+// bf16 number (no lo part: two passes instead of three).  Each accumulator
+// takes its products in the order ks = 0..3, and within a ks hi*G_hi,
+// hi*G_lo, lo*G_hi, so results depend on the tile only.  Contains two
+// workgroup barriers; the caller has synchronized after writing sh/sl.
 template <bool EXACT>
-__device__ __forceinline__ void gauge128_tile(float *xs, const G128Frags &f) {
+__device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t *sl, float *xs,
+                                              const G128Frags &f) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   f32x4_t acc[4][2];
@@ -89,36 +162,24 @@ __device__ __forceinline__ void gauge128_tile(float *xs, const G128Frags &f) {
   for (int mt = 0; mt < 4; mt++) {
     acc[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int off = (16 * mt + (lane & 15)) * HP + 8 * (lane >> 4);
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-      const float *src = xs + (16 * mt + (lane & 15)) * PITCH + 32 * ks + 8 * (lane >> 4);
-      const float4 v0 = *(const float4 *)src, v1 = *(const float4 *)(src + 4);
-      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      uint32_t h[8], l[8];
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        if (EXACT) {
-          h[e] = __float_as_uint(v[e]) >> 16;
-          l[e] = 0;
-        } else {
-          split_bf16(v[e], h[e], l[e]);
-        }
-      }
-      const bf16x8_t ah = pack8(h);
+      const bf16x8_t ah = *(const bf16x8_t *)(sh + off + 32 * ks);
 #pragma unroll
       for (int ntl = 0; ntl < 2; ntl++) {
         acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
         acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, f.lo[ntl][ks], acc[mt][ntl], 0, 0, 0);
       }
       if (!EXACT) {
-        const bf16x8_t al = pack8(l);
+        const bf16x8_t al = *(const bf16x8_t *)(sl + off + 32 * ks);
 #pragma unroll
         for (int ntl = 0; ntl < 2; ntl++)
           acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
       }
     }
   }
-  __syncthreads();  // every wave has read the whole tile
+  __syncthreads();  // every wave has read its operands: xs may overwrite them
 #pragma unroll
   for (int mt = 0; mt < 4; mt++)
 #pragma unroll

@@ -40,6 +40,11 @@ struct QK {
   int32_t residual;         // KIVI: tail rows kept in the storage format
 };
 
+// valid rows of tile `tile` of the call's row range
+__device__ __forceinline__ int tile_rows(const QK &a, int64_t tile) {
+  return (int)min((int64_t)TILE_T, a.nt - tile * TILE_T);
+}
+
 struct Range {
   float mn, scale, inv;
   bool zero;
@@ -154,20 +159,60 @@ __device__ __forceinline__ void write32(float *xs, int t, int j, const float (&v
   for (int k = 0; k < 32; k += 4) *(float4 *)(d + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
 }
 
-__device__ __forceinline__ void zero_rows(float *xs, int from) {
-  for (int i = threadIdx.x; i < (TILE_T - from) * 32; i += NT)
-    *(float4 *)(xs + (from + (i >> 5)) * PITCH + (i & 31) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-}
+// Forward-gauged tiles of one workgroup's chunk.  next() loads the tile at
+// token tb (rows [0, nrows)) and applies the forward gauge; the fp32 result is
+// in the tile view of `lds` (PITCH floats per row; rows past nrows are zero
+// for the dense gauge).  With the dense gauge the global loads of the
+// following tile (prefetch()) are in flight during the matrix work.
+template <int G, bool BF16>
+struct GaugedTiles {
+  TileFetch<BF16> pre;
 
-// gauge stage of a tile; DIR false = forward, true = inverse; EXACT: values
-// are bf16 numbers (dense gauge takes two passes instead of three)
-template <int G, bool INV, bool EXACT>
-__device__ __forceinline__ void gauge_stage(float *xs, int nrows, const float *Gf, const G128Frags &fr) {
-  if constexpr (G == 16 || G == 32) {
-    gauge_tile<G, INV>(xs, nrows, Gf);
+  __device__ __forceinline__ void prefetch(const void *__restrict__ src, int nrows) {
+    if constexpr (G == 128) pre.fetch(src, nrows);
+  }
+
+  // next_src/next_rows: the tile after this one (next_rows = 0: none)
+  __device__ __forceinline__ void next(const void *__restrict__ src, int nrows,
+                                       const void *__restrict__ next_src, int next_rows,
+                                       unsigned char *lds, const float *Gf, const G128Frags &fr) {
+    float *xs = (float *)lds;
+    if constexpr (G == 128) {
+      uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
+      pre.put(sh, sl);
+      __syncthreads();
+      if (next_rows > 0) pre.fetch(next_src, next_rows);
+      gauge128_tile<BF16>(sh, sl, xs, fr);
+    } else {
+      load_tile<BF16>(src, nrows, xs);
+      __syncthreads();
+      if constexpr (G == 16 || G == 32) {
+        gauge_tile<G, false>(xs, nrows, Gf);
+        __syncthreads();
+      }
+    }
+  }
+};
+
+// Every thread hands over its 32 decoded values (row t, channels 32 j ..);
+// apply the inverse gauge to the whole tile, result in the tile view of lds.
+template <int G>
+__device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, int j,
+                                                    const float (&v)[32], int nrows,
+                                                    const float *Gf, const G128Frags &fr) {
+  float *xs = (float *)lds;
+  if constexpr (G == 128) {
+    uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
+    split32(sh, sl, t, j, v);
     __syncthreads();
-  } else if constexpr (G == 128) {
-    gauge128_tile<EXACT>(xs, fr);
+    gauge128_tile<false>(sh, sl, xs, fr);
+  } else {
+    write32(xs, t, j, v);
+    __syncthreads();
+    if constexpr (G == 16 || G == 32) {
+      gauge_tile<G, true>(xs, nrows, Gf);
+      __syncthreads();
+    }
   }
 }
 
@@ -218,7 +263,8 @@ __global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
                                                   const float *__restrict__ gauges,
                                                   uint8_t *__restrict__ payload,
                                                   float *__restrict__ meta, QK a) {
-  __shared__ float xs[TILE_T * PITCH];
+  __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  float *xs = (float *)lds;
   __shared__ float red[8];
   constexpr int L = (1 << BITS) - 1;
   const int64_t f = (int64_t)blockIdx.x / a.chunks;
@@ -230,14 +276,17 @@ __global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
   const int BT = a.block;
   const int64_t nblk_f = a.tcap / BT;
   const int t = threadIdx.x >> 2, j = threadIdx.x & 3, w = threadIdx.x >> 6;
-  for (int64_t tile = chunk * a.tiles_per_chunk;
-       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+  constexpr size_t ESZ = BF16 ? 2 : 4;
+  const uint8_t *src_f = (const uint8_t *)kv + (size_t)f * a.tcap * D * ESZ;
+  const int64_t tile0 = chunk * a.tiles_per_chunk;
+  const int64_t tend = min(ntiles, (chunk + 1) * a.tiles_per_chunk);
+  GaugedTiles<G, BF16> tiles;
+  if (tile0 < tend) tiles.prefetch(src_f + (size_t)(a.t0 + tile0 * TILE_T) * D * ESZ, tile_rows(a, tile0));
+  for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
-    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
-    load_tile<BF16>((const uint8_t *)kv + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4), nrows, xs);
-    if (G == 128 && nrows < TILE_T) zero_rows(xs, nrows);
-    __syncthreads();
-    gauge_stage<G, false, BF16>(xs, nrows, Gf, fr);
+    const int nrows = tile_rows(a, tile);
+    tiles.next(src_f + (size_t)tb * D * ESZ, nrows, src_f + (size_t)(tb + TILE_T) * D * ESZ,
+               tile + 1 < tend ? tile_rows(a, tile + 1) : 0, lds, Gf, fr);
     const bool active = t < nrows;
     float v[32];
     float mn = INFINITY, mx = -INFINITY;
@@ -285,7 +334,8 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
                                                   const float *__restrict__ meta,
                                                   const float *__restrict__ gauges,
                                                   void *__restrict__ out, QK a) {
-  __shared__ float xs[TILE_T * PITCH];
+  __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  float *xs = (float *)lds;
   const int64_t f = (int64_t)blockIdx.x / a.chunks;
   const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
@@ -312,9 +362,7 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
 #pragma unroll
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
-    write32(xs, t, j, v);
-    __syncthreads();
-    gauge_stage<G, true, false>(xs, nrows, Gf, fr);
+    inverse_gauged_tile<G>(lds, t, j, v, nrows, Gf, fr);
     store_tile<BF16>((uint8_t *)out + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4), nrows, xs);
     __syncthreads();
   }
@@ -333,7 +381,8 @@ __global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
                                                     const float *__restrict__ gauges,
                                                     uint8_t *__restrict__ payload,
                                                     float *__restrict__ meta, QK a) {
-  __shared__ float xs[TILE_T * PITCH];
+  __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  float *xs = (float *)lds;
   __shared__ float pmn[2 * D], pinv[2 * D];
   __shared__ uint8_t pzero[2 * D];
   constexpr int L = (1 << BITS) - 1;
@@ -350,14 +399,16 @@ __global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
   float *mf = meta + 2 * (size_t)f * 4 * Tcq;
   const bool keys = ((f / ((int64_t)a.batch * a.heads)) % a.kv) == 0;
   const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
-  for (int64_t tile = chunk * a.tiles_per_chunk;
-       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+  const uint8_t *src_f = (const uint8_t *)kv + (size_t)f * a.tcap * D * ESZ;
+  const int64_t tile0 = chunk * a.tiles_per_chunk;
+  const int64_t tend = min(ntiles, (chunk + 1) * a.tiles_per_chunk);
+  GaugedTiles<G, BF16> tiles;
+  if (tile0 < tend) tiles.prefetch(src_f + (size_t)(a.t0 + tile0 * TILE_T) * D * ESZ, tile_rows(a, tile0));
+  for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
-    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
-    load_tile<BF16>((const uint8_t *)kv + (size_t)(f * a.tcap + tb) * D * ESZ, nrows, xs);
-    if (G == 128 && nrows < TILE_T) zero_rows(xs, nrows);
-    __syncthreads();
-    gauge_stage<G, false, BF16>(xs, nrows, Gf, fr);
+    const int nrows = tile_rows(a, tile);
+    tiles.next(src_f + (size_t)tb * D * ESZ, nrows, src_f + (size_t)(tb + TILE_T) * D * ESZ,
+               tile + 1 < tend ? tile_rows(a, tile + 1) : 0, lds, Gf, fr);
     if (keys) {
       const int gi = threadIdx.x >> 7, c = threadIdx.x & 127;
       const int r0 = 32 * gi;
@@ -423,7 +474,8 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
                                                     const float *__restrict__ meta,
                                                     const float *__restrict__ gauges,
                                                     void *__restrict__ out, QK a) {
-  __shared__ float xs[TILE_T * PITCH];
+  __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  float *xs = (float *)lds;
   __shared__ float pmn[2 * D], psc[2 * D];
   constexpr size_t ESZ = BF16 ? 2 : 4;
   const int64_t f = (int64_t)blockIdx.x / a.chunks;
@@ -476,9 +528,7 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
 #pragma unroll
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
-    write32(xs, t, j, v);
-    __syncthreads();
-    gauge_stage<G, true, false>(xs, nrows, Gf, fr);
+    inverse_gauged_tile<G>(lds, t, j, v, nrows, Gf, fr);
     store_tile<BF16>((uint8_t *)out + (size_t)(f * a.tcap + tb) * D * ESZ, nrows, xs);
     __syncthreads();
   }
@@ -490,21 +540,28 @@ template <bool BF16, bool INV>
 __global__ __launch_bounds__(NT) void k_gauge128_rows(const void *__restrict__ src,
                                                       const float *__restrict__ gauges,
                                                       float *__restrict__ out, QK a) {
-  __shared__ float xs[TILE_T * PITCH];
+  __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  float *xs = (float *)lds;
+  uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
+  constexpr size_t ESZ = BF16 ? 2 : 4;
   const int64_t f = (int64_t)blockIdx.x / a.chunks;
   const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = gauges + gauge_index(f, a.batch, a.heads) * D * 128;
   G128Frags fr;
   load_g128<INV>(Gf, fr);
-  for (int64_t tile = chunk * a.tiles_per_chunk;
-       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+  const uint8_t *src_f = (const uint8_t *)src + (size_t)f * a.tcap * D * ESZ;
+  const int64_t tile0 = chunk * a.tiles_per_chunk;
+  const int64_t tend = min(ntiles, (chunk + 1) * a.tiles_per_chunk);
+  TileFetch<BF16> pre;
+  if (tile0 < tend) pre.fetch(src_f + (size_t)(a.t0 + tile0 * TILE_T) * D * ESZ, tile_rows(a, tile0));
+  for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
-    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
-    load_tile<BF16>((const uint8_t *)src + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4), nrows, xs);
-    if (nrows < TILE_T) zero_rows(xs, nrows);
+    const int nrows = tile_rows(a, tile);
+    pre.put(sh, sl);
     __syncthreads();
-    gauge128_tile<BF16>(xs, fr);
+    if (tile + 1 < tend) pre.fetch(src_f + (size_t)(tb + TILE_T) * D * ESZ, tile_rows(a, tile + 1));
+    gauge128_tile<BF16>(sh, sl, xs, fr);
     store_tile<false>(out + (size_t)(f * a.tcap + tb) * D, nrows, xs);
     __syncthreads();
   }
