@@ -345,23 +345,35 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
   const int BT = a.block;
   const int64_t nblk_f = a.tcap / BT;
   const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
-  for (int64_t tile = chunk * a.tiles_per_chunk;
-       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+  const int64_t tile0 = chunk * a.tiles_per_chunk;
+  const int64_t tend = min(ntiles, (chunk + 1) * a.tiles_per_chunk);
+  // this thread's codes and range of a tile, loaded one tile ahead
+  uint32_t wd[BITS];
+  float mn = 0.0f, sc = 0.0f;
+  auto fetch = [&](int64_t tile) {
     const int64_t tb = a.t0 + tile * TILE_T;
-    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+    if (t < tile_rows(a, tile)) {
+      load_words<BITS>(payload + (size_t)(f * a.tcap + tb) * 16 * BITS + threadIdx.x * 4 * BITS, wd);
+      const float *m = meta + 2 * (f * nblk_f + (tb + t) / BT);
+      mn = m[0];
+      sc = m[1];
+    }
+  };
+  if (tile0 < tend) fetch(tile0);
+  for (int64_t tile = tile0; tile < tend; tile++) {
+    const int64_t tb = a.t0 + tile * TILE_T;
+    const int nrows = tile_rows(a, tile);
     float v[32];
     if (t < nrows) {
-      uint32_t wd[BITS], q[32];
-      load_words<BITS>(payload + (size_t)(f * a.tcap + tb) * 16 * BITS + threadIdx.x * 4 * BITS, wd);
+      uint32_t q[32];
       unpack32<BITS>(wd, q);
-      const float *m = meta + 2 * (f * nblk_f + (tb + t) / BT);
-      const float mn = m[0], sc = m[1];
 #pragma unroll
       for (int k = 0; k < 32; k++) v[k] = dequant1(q[k], mn, sc);
     } else {
 #pragma unroll
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
+    if (tile + 1 < tend) fetch(tile + 1);
     inverse_gauged_tile<G>(lds, t, j, v, nrows, Gf, fr);
     store_tile<BF16>((uint8_t *)out + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4), nrows, xs);
     __syncthreads();
@@ -490,17 +502,39 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
   const float *mf = meta + 2 * (size_t)f * 4 * Tcq;
   const bool keys = ((f / ((int64_t)a.batch * a.heads)) % a.kv) == 0;
   const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
-  for (int64_t tile = chunk * a.tiles_per_chunk;
-       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
+  const int gi = threadIdx.x >> 7, c = threadIdx.x & 127, r0 = 32 * gi;
+  const int64_t tile0 = chunk * a.tiles_per_chunk;
+  const int64_t tend = min(ntiles, (chunk + 1) * a.tiles_per_chunk);
+  // this thread's codes, its row's value range and (keys) one column range of
+  // a tile, loaded one tile ahead; tail rows are read when they are used
+  uint32_t wd[BITS];
+  float mn = 0.0f, sc = 0.0f, kmn = 0.0f, ksc = 0.0f;
+  auto fetch = [&](int64_t tile) {
     const int64_t tb = a.t0 + tile * TILE_T;
-    const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
+    const int nrows = tile_rows(a, tile);
+    if (keys && r0 < nrows && tb + r0 < Tq) {
+      const float *m = mf + 2 * (((tb + r0) / 32) * D + c);
+      kmn = m[0];
+      ksc = m[1];
+    }
+    const int64_t row = tb + t;
+    if (t < nrows && row < Tq) {
+      load_words<BITS>(pf + (size_t)row * 16 * BITS + j * 4 * BITS, wd);
+      if (!keys) {
+        const float *m = mf + 2 * (row * 4 + j);
+        mn = m[0];
+        sc = m[1];
+      }
+    }
+  };
+  if (tile0 < tend) fetch(tile0);
+  for (int64_t tile = tile0; tile < tend; tile++) {
+    const int64_t tb = a.t0 + tile * TILE_T;
+    const int nrows = tile_rows(a, tile);
     if (keys) {
-      const int gi = threadIdx.x >> 7, c = threadIdx.x & 127;
-      const int r0 = 32 * gi;
       if (r0 < nrows && tb + r0 < Tq) {
-        const float *m = mf + 2 * (((tb + r0) / 32) * D + c);
-        pmn[threadIdx.x] = m[0];
-        psc[threadIdx.x] = m[1];
+        pmn[threadIdx.x] = kmn;
+        psc[threadIdx.x] = ksc;
       }
       __syncthreads();
     }
@@ -508,16 +542,13 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
     if (t < nrows) {
       const int64_t row = tb + t;
       if (row < Tq) {
-        uint32_t wd[BITS], q[32];
-        load_words<BITS>(pf + (size_t)row * 16 * BITS + j * 4 * BITS, wd);
+        uint32_t q[32];
         unpack32<BITS>(wd, q);
         if (keys) {
           const int base = (t >> 5) * D + 32 * j;
 #pragma unroll
           for (int k = 0; k < 32; k++) v[k] = dequant1(q[k], pmn[base + k], psc[base + k]);
         } else {
-          const float *m = mf + 2 * (row * 4 + j);
-          const float mn = m[0], sc = m[1];
 #pragma unroll
           for (int k = 0; k < 32; k++) v[k] = dequant1(q[k], mn, sc);
         }
@@ -528,6 +559,7 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
 #pragma unroll
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
+    if (tile + 1 < tend) fetch(tile + 1);
     inverse_gauged_tile<G>(lds, t, j, v, nrows, Gf, fr);
     store_tile<BF16>((uint8_t *)out + (size_t)(f * a.tcap + tb) * D * ESZ, nrows, xs);
     __syncthreads();
