@@ -138,8 +138,10 @@ template <int R>
 __host__ __device__ __forceinline__ void put64(uint64_t (&acc)[Rate<R>::kAcc], int pos,
                                                uint64_t code) {
   constexpr int NA = Rate<R>::kAcc;
+  // pos is in [0, 16R): the first word never needs a right shift
+  if (pos < 64) acc[0] |= code << pos;
 #pragma unroll
-  for (int a = 0; a < NA; a++) {
+  for (int a = 1; a < NA; a++) {
     const int sh = pos - 64 * a;
     if (sh >= 0 && sh < 64)
       acc[a] |= code << sh;
