@@ -83,14 +83,14 @@ __device__ __forceinline__ void store_tile(void *__restrict__ dst, int nrows, co
 }
 
 // Gauge (INV = false: y = G x) or inverse gauge (INV = true: y = G^T x) of
-// every token row of the tile, in place, for group size G in {16, 32}.
+// every token row of the tile, in place, for group size G in {8, 16, 32}.
 // Each output is an fmaf chain over the group's inputs in index order from
 // +0.  A wave owns whole groups (the group index is wave-uniform), so the
 // g x g matrix is read through the scalar cache and every FMA takes its
 // matrix operand from an SGPR; lane = token row.
 template <int G, bool INV>
 __device__ __forceinline__ void gauge_tile(float *xs, int nrows, const float *__restrict__ Gf) {
-  static_assert(G == 16 || G == 32, "VALU gauge handles g = 16 and 32");
+  static_assert(G == 8 || G == 16 || G == 32, "VALU gauge handles g = 8, 16 and 32");
   constexpr int NG = D / G;      // groups per head
   constexpr int GPW = NG / 4;    // groups per wave
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

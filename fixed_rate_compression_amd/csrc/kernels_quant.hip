@@ -17,7 +17,7 @@ bool bu_block_built(int bt) { return bt == 16 || bt == 32 || bt == 64; }
 static hipError_t launch(bool encode, bool bf16, int g, const void *src, const float *gauges,
                          void *dst, const void *meta_in, float *meta_out, const QuantArgs &q,
                          hipStream_t s) {
-  if (g != 0 && g != 16 && g != 32 && g != 128) return hipErrorInvalidValue;
+  if (g != 0 && g != 8 && g != 16 && g != 32 && g != 128) return hipErrorInvalidValue;
   switch (q.bits) {
     case 2: return quant_launch_bits<2>(encode, bf16, g, q.backend, src, gauges, dst, meta_in, meta_out, q, s);
     case 3: return quant_launch_bits<3>(encode, bf16, g, q.backend, src, gauges, dst, meta_in, meta_out, q, s);

@@ -66,7 +66,9 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
   __shared__ float cm[D * D];                // C128[v][c] at v*128 + ((c + rot(v)) & 127)
   float *xs = buf, *xr = buf + TILE_T * PITCH;
   __shared__ double red[4][3];
-  constexpr int NGT = G == 32 ? 16 : (G == 16 ? 8 : 0);  // 16x16 Gamma tiles per field
+  // 16x16 Gamma tiles per field; g = 8 groups are the 8x8 diagonal blocks of
+  // the g = 16 tiles
+  constexpr int NGT = G == 32 ? 16 : (G == 16 || G == 8 ? 8 : 0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, lg = lane >> 4, lm = lane & 15;
   const int64_t f = (int64_t)blockIdx.x / a.chunks;
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
       }
       // Gamma_r[i][k] += sum_t dX'[t][gi] x[t][gk] over this block's 16 rows
       const float *Xr = xr + 16 * wave * PITCH;
-      if constexpr (G == 16) {
+      if constexpr (G == 8 || G == 16) {
 #pragma unroll
         for (int r = 0; r < 8; r++)
 #pragma unroll
@@ -278,11 +280,12 @@ hipError_t stats_launch(bool bf16, int g, const void *kv, const float *gauges, c
   if (bf16 == BF && g == GG)                                                                  \
     hipLaunchKernelGGL((k_dct_stats<BF, GG>), grid, block, 0, s, kv, gauges, C128, C16, rtab, \
                        part, gpart, a);
-  CG_S(true, 0) CG_S(true, 16) CG_S(true, 32) CG_S(false, 0) CG_S(false, 16) CG_S(false, 32)
+  CG_S(true, 0) CG_S(true, 8) CG_S(true, 16) CG_S(true, 32)
+  CG_S(false, 0) CG_S(false, 8) CG_S(false, 16) CG_S(false, 32)
 #undef CG_S
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int ng = g == 32 ? 16 * 256 : (g == 16 ? 8 * 256 : 0);
+  const int ng = g == 32 ? 16 * 256 : (g == 16 || g == 8 ? 8 * 256 : 0);
   hipLaunchKernelGGL(k_stats_reduce, dim3((unsigned)fields), block, 0, s, part, gpart, out,
                      a.chunks, ng, a.grad && g != 0);
   return hipGetLastError();

@@ -26,7 +26,7 @@ bool zfp_rate_built(int R) {
 
 static hipError_t zfp_launch(int R, bool encode, bool bf16, int g, const void *src,
                              const float *gauges, void *dst, const TileArgs &a, hipStream_t s) {
-  if (g != 0 && g != 16 && g != 32) return hipErrorInvalidValue;
+  if (g != 0 && g != 8 && g != 16 && g != 32) return hipErrorInvalidValue;
   switch (R) {
 #define CASE(r) case r: return zfp_launch_rate<r>(encode, bf16, g, src, gauges, dst, a, s);
     CG_ZFP_RATES(CASE)
@@ -73,6 +73,9 @@ static hipError_t gauge_rows_g(int g, const void *src, const float *gauges, void
   switch (g) {
     case 0:
       hipLaunchKernelGGL((k_gauge_rows<SB, DB, 0, INV>), grid, block, 0, s, src, gauges, dst, a);
+      return hipGetLastError();
+    case 8:
+      hipLaunchKernelGGL((k_gauge_rows<SB, DB, 8, INV>), grid, block, 0, s, src, gauges, dst, a);
       return hipGetLastError();
     case 16:
       hipLaunchKernelGGL((k_gauge_rows<SB, DB, 16, INV>), grid, block, 0, s, src, gauges, dst, a);

@@ -186,7 +186,7 @@ struct GaugedTiles {
     } else {
       load_tile<BF16>(src, nrows, xs);
       __syncthreads();
-      if constexpr (G == 16 || G == 32) {
+      if constexpr (G != 0) {
         gauge_tile<G, false>(xs, nrows, Gf);
         __syncthreads();
       }
@@ -209,7 +209,7 @@ __device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, i
   } else {
     write32(xs, t, j, v);
     __syncthreads();
-    if constexpr (G == 16 || G == 32) {
+    if constexpr (G != 0) {
       gauge_tile<G, true>(xs, nrows, Gf);
       __syncthreads();
     }

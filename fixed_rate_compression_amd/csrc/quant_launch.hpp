@@ -49,8 +49,8 @@ hipError_t quant_launch_bits(bool encode, bool bf16, int g, int backend, const v
                          (const float *)meta_in, gauges, dst, a);                                    \
     return hipGetLastError();                                                                        \
   }
-  CG_Q(true, 0) CG_Q(true, 16) CG_Q(true, 32) CG_Q(true, 128)
-  CG_Q(false, 0) CG_Q(false, 16) CG_Q(false, 32) CG_Q(false, 128)
+  CG_Q(true, 0) CG_Q(true, 8) CG_Q(true, 16) CG_Q(true, 32) CG_Q(true, 128)
+  CG_Q(false, 0) CG_Q(false, 8) CG_Q(false, 16) CG_Q(false, 32) CG_Q(false, 128)
 #undef CG_Q
   return hipErrorInvalidValue;
 }

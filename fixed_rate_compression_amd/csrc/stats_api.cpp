@@ -45,7 +45,7 @@ Layout layout(const cg_shape *s, int g) {
   const int64_t ntiles = (s->tokens + kTileT - 1) / kTileT;
   L.chunks = (ntiles + kTilesPerChunk - 1) / kTilesPerChunk;
   if (L.chunks < 1) L.chunks = 1;
-  L.ng = g == 32 ? 16 * 256 : (g == 16 ? 8 * 256 : 0);
+  L.ng = g == 32 ? 16 * 256 : (g == 16 || g == 8 ? 8 * 256 : 0);
   size_t off = 0;
   L.G = off;     off += align256((size_t)(g ? ngauge * kD * g : 1) * 4);
   L.C128 = off;  off += align256((size_t)kD * kD * 4);
@@ -67,7 +67,8 @@ int validate(const cg_shape *s, int g, int T_b) {
   if (s->tokens < 0 || s->tokens > s->token_capacity) return fail(CG_E_SHAPE, "bad token counts");
   if (T_b != 16) return fail(CG_E_UNSUPPORTED, "T_b must be 16");
   if (s->tokens % T_b) return fail(CG_E_SHAPE, "tokens must be a multiple of T_b");
-  if (g != 0 && g != 16 && g != 32) return fail(CG_E_UNSUPPORTED, "gauge group must be 0, 16 or 32");
+  if (g != 0 && g != 8 && g != 16 && g != 32)
+    return fail(CG_E_UNSUPPORTED, "gauge group must be 0, 8, 16 or 32");
   return CG_OK;
 }
 
@@ -198,11 +199,13 @@ extern "C" int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t
         const double *A = A_host + ((size_t)gidx * R + q) * gg;
         for (int i = 0; i < g; i++)
           for (int j = 0; j < g; j++) St[i * g + j] = A[j * g + i] - A[i * g + j];  // S^T
-        // Gamma tiles: g = 16 -> tile q holds [16][16]; g = 32 -> tiles 4q + 2a + b
+        // Gamma tiles: g = 16 -> tile q holds [16][16]; g = 32 -> tiles 4q + 2a + b;
+        // g = 8 -> diagonal block q % 2 of tile q / 2
         for (int i = 0; i < g; i++)
           for (int j = 0; j < g; j++) {
             double v;
             if (g == 16) v = r[q * 256 + i * 16 + j];
+            else if (g == 8) v = r[(q / 2) * 256 + (8 * (q % 2) + i) * 16 + 8 * (q % 2) + j];
             else v = r[(q * 4 + (i / 16) * 2 + (j / 16)) * 256 + (i % 16) * 16 + (j % 16)];
             Gam[i * g + j] = v;
           }

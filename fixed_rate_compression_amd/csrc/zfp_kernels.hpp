@@ -144,7 +144,8 @@ hipError_t zfp_launch_rate(bool encode, bool bf16, int g, const void *src, const
                          gauges, dst, a);                                                        \
     return hipGetLastError();                                                                    \
   }
-  CG_L(true, 0) CG_L(true, 16) CG_L(true, 32) CG_L(false, 0) CG_L(false, 16) CG_L(false, 32)
+  CG_L(true, 0) CG_L(true, 8) CG_L(true, 16) CG_L(true, 32)
+  CG_L(false, 0) CG_L(false, 8) CG_L(false, 16) CG_L(false, 32)
 #undef CG_L
   return hipErrorInvalidValue;
 }

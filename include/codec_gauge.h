@@ -90,7 +90,7 @@ typedef struct cg_shape {
 
 typedef struct cg_gauge {
   int32_t group;   /* g: 0 = identity (no arithmetic), else divides head_dim;
-                      built: 16 and 32 for every backend, 128 for
+                      built: 8, 16 and 32 for every backend, 128 for
                       BLOCK_UNIFORM and KIVI (dense full-head gauge) */
   const float *G;  /* device, fp32 [layers][kv][heads][head_dim/g][g][g];
                       ignored when group == 0 */
@@ -169,7 +169,8 @@ int cg_roundtrip(const cg_shape *shape, const void *kv_in, const cg_gauge *gauge
  * concave in the energy U^2),
  * L = lambda_f L_freq + lambda_r L_rate, per field.
  *   kv         device, storage format, KV layout (tokens % T_b == 0)
- *   g          16 (built); A_host fp64 [layers][kv][heads][d/g][g][g]
+ *   g          0 (identity), 8, 16 or 32 (built); A_host fp64
+ *              [layers][kv][heads][d/g][g][g] (ignored when g == 0)
  *   T_b        16 (built)
  *   workspace  device scratch of >= cg_stats_workspace_bytes() bytes
  *   out_host   host cg_stats[n_fields]

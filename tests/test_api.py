@@ -83,6 +83,11 @@ def test_codec_and_row_validation_before_launch():
     assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, cap=100) == cg.CG_E_SIZE
     assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, gauge=cg.make_gauge(12, np.zeros(1, np.float32))) == cg.CG_E_SHAPE
     assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, gauge=cg.CgGauge(16, None)) == cg.CG_E_INVAL
+    # groups that divide head_dim but are not built are refused before any launch
+    Gz = np.zeros(1, np.float32)
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, gauge=cg.make_gauge(4, Gz)) == cg.CG_E_UNSUPPORTED
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, gauge=cg.make_gauge(128, Gz)) == cg.CG_E_UNSUPPORTED
+    assert "not built" in cg.cg_last_error()
     assert enc(cg.make_codec(9, 4), 0, 64) == cg.CG_E_INVAL
     assert "backend" in cg.cg_last_error()
     # zero rows is a no-op that launches nothing

@@ -53,7 +53,7 @@ def rel_err(got, ref):
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("Bt", [16, 32, 64])
-@pytest.mark.parametrize("g", [0, 16, 32])
+@pytest.mark.parametrize("g", [0, 8, 16, 32])
 def test_block_uniform_bit_exact(bits, Bt, g):
     L, KV, B, H, T = 1, 2, 1, 2, 64 * 3 + 16 * (1 if Bt == 16 else 0)
     T -= T % Bt
@@ -101,7 +101,7 @@ def kivi_split(pay, meta, f, T, res, bits, esz):
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("g", [0, 16, 32])
+@pytest.mark.parametrize("g", [0, 8, 16, 32])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_kivi_bit_exact(bits, g, bf16):
     L, KV, B, H, T, res = 1, 2, 2, 1, 352, 128    # 224 quantized rows (7 groups), 3.5 tiles

@@ -38,7 +38,7 @@ def compare(stats, dA, x_host_field, A_field, g, f, tol=1e-5):
     return d
 
 
-@pytest.mark.parametrize("g", [16, 32, 0])
+@pytest.mark.parametrize("g", [8, 16, 32, 0])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_stats_small(g, bf16):
     L, KV, B, H, T = 1, 2, 1, 2, 64 * 3 + 16

@@ -61,7 +61,7 @@ def test_small_config_fp32_g16_rate4():
 
 
 @pytest.mark.parametrize("R", [2, 3, 4, 6, 8])
-@pytest.mark.parametrize("g", [0, 16, 32])
+@pytest.mark.parametrize("g", [0, 8, 16, 32])
 def test_bf16_rates_groups_ragged(R, g):
     # T = 200: three full 64-token tiles and a ragged 8-token tile; capacity 256
     L, KV, B, H, T, Tcap = 2, 2, 1, 2, 200, 256
@@ -71,7 +71,7 @@ def test_bf16_rates_groups_ragged(R, g):
     check_against_oracle(x, G, g, R, L, KV, B, H, T, Tcap, pay, out)
 
 
-@pytest.mark.parametrize("g", [0, 32])
+@pytest.mark.parametrize("g", [0, 8, 32])
 def test_fp32_other_groups_batch(g):
     L, KV, B, H, T = 1, 2, 3, 1, 132
     x = kv_cpu(5, L, KV, B, H, T, T, 0.9, 2, bf16=False)
