@@ -240,6 +240,11 @@ def workload_lines(steps, warmup):
     for R in (3, 6):
         lines.append(_codec_line(f"llama8b_zfp{R}", sh, x, G, 16, cg.make_codec(cg.CG_BACKEND_ZFP, R),
                                  steps, warmup, 2, "32 layers x K/V x 8 heads x 32768 tokens bf16, g=16"))
+    for g in (8, 32, 128):
+        Gg, _ = _gauge(L, KV, H, g, 102 + g)
+        lines.append(_codec_line(f"llama8b_zfp4_g{g}", sh, x, Gg, g, cg.make_codec(cg.CG_BACKEND_ZFP, 4),
+                                 steps, warmup, 2, f"32 layers x K/V x 8 heads x 32768 tokens bf16, g={g}"
+                                 + (" (dense, matrix cores)" if g == 128 else "")))
     del x
     torch.cuda.empty_cache()
     # full-head gauge (g = 128, MFMA): KIVI-2/4 (group 32, 128-token tail), block-uniform 3-bit

@@ -8,6 +8,7 @@
 namespace cgk {
 
 constexpr int TILE_T = 64;  // tokens per workgroup tile of the rows kernels
+constexpr int ZFP128_CHUNK = 16;  // tiles per workgroup with the dense (g = 128) gauge
 
 // geometry of a rows launch over every field: one workgroup per
 // (field, 64-token tile) of rows [t0, t0 + nt)
@@ -19,7 +20,7 @@ struct TileArgs {
   int32_t tiles;  // tiles per field = ceil(nt / 64)
   int32_t batch;  // B (gauges are shared across the batch)
   int32_t heads;  // H
-  int32_t pad;
+  int32_t chunks; // dense gauge: workgroups per field = ceil(tiles / ZFP128_CHUNK)
 };
 
 bool zfp_rate_built(int R);

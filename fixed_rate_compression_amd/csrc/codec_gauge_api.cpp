@@ -58,9 +58,10 @@ int check_gauge(const cg_gauge *g, const cg_shape *s, const cg_codec *c) {
   if (g->group < 0 || s->head_dim % g->group)
     return fail(CG_E_SHAPE, "gauge group %d must divide head_dim %d", g->group, s->head_dim);
   if (!g->G) return fail(CG_E_INVAL, "gauge matrices are NULL");
-  const bool quant = c && (c->backend == CG_BACKEND_BLOCK_UNIFORM || c->backend == CG_BACKEND_KIVI);
+  const bool dense_ok = !c || c->backend == CG_BACKEND_ZFP || c->backend == CG_BACKEND_BLOCK_UNIFORM ||
+                        c->backend == CG_BACKEND_KIVI;
   if (g->group == 8 || g->group == 16 || g->group == 32) return CG_OK;
-  if (g->group == 128 && (quant || !c)) return CG_OK;
+  if (g->group == 128 && dense_ok) return CG_OK;
   return fail(CG_E_UNSUPPORTED, "gauge group %d is not built for this backend", g->group);
 }
 

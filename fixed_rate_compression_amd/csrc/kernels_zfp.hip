@@ -26,7 +26,7 @@ bool zfp_rate_built(int R) {
 
 static hipError_t zfp_launch(int R, bool encode, bool bf16, int g, const void *src,
                              const float *gauges, void *dst, const TileArgs &a, hipStream_t s) {
-  if (g != 0 && g != 8 && g != 16 && g != 32) return hipErrorInvalidValue;
+  if (g != 0 && g != 8 && g != 16 && g != 32 && g != 128) return hipErrorInvalidValue;
   switch (R) {
 #define CASE(r) case r: return zfp_launch_rate<r>(encode, bf16, g, src, gauges, dst, a, s);
     CG_ZFP_RATES(CASE)

@@ -22,6 +22,7 @@
 
 #include "cg_launch.hpp"
 #include "cg_tile.hpp"
+#include "gauge128.hpp"
 #include "zfp_block.hpp"
 
 namespace cgk {
@@ -129,6 +130,124 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
   store_tile<BF16>((uint8_t *)out + (size_t)row0 * D * esz, nrows, xs);
 }
 
+// Dense (g = 128) gauge on the matrix cores (gauge128.hpp): a workgroup walks
+// ZFP128_CHUNK consecutive tiles of one field so the 64 KB gauge is turned
+// into VGPR fragments once, and loads tile i+1 (KV rows, or code words) while
+// it works on tile i.
+template <int R, bool BF16>
+__global__ __launch_bounds__(NT) void k_zfp_encode128(const void *__restrict__ kv,
+                                                      const float *__restrict__ gauges,
+                                                      uint8_t *__restrict__ payload, TileArgs a) {
+  __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
+  __shared__ uint16_t dbl[256];
+  float *xs = (float *)lds;
+  uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
+  const int64_t field = (int64_t)blockIdx.x / a.chunks;
+  const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * ZFP128_CHUNK;
+  const int tend = min(a.tiles, tile0 + ZFP128_CHUNK);
+  const size_t esz = BF16 ? 2 : 4;
+  dbl[threadIdx.x] = cgz::dbl8_entry(threadIdx.x);
+  G128Frags fr;
+  load_g128<false>(gauges + gauge_index(field, a.batch, a.heads) * D * 128, fr);
+  const uint8_t *src_f = (const uint8_t *)kv + (size_t)field * a.tcap * D * esz;
+  auto rows = [&](int tile) { return (int)min((int64_t)TILE_T, a.nt - (int64_t)tile * TILE_T); };
+  TileFetch<BF16> pre;
+  if (tile0 < tend) pre.fetch(src_f + (size_t)(a.t0 + (int64_t)tile0 * TILE_T) * D * esz, rows(tile0));
+  for (int tile = tile0; tile < tend; tile++) {
+    const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
+    const int nrows = rows(tile);
+    pre.put(sh, sl);
+    __syncthreads();
+    if (tile + 1 < tend) pre.fetch(src_f + (size_t)(tb + TILE_T) * D * esz, rows(tile + 1));
+    gauge128_tile<BF16>(sh, sl, xs, fr);
+    const int nblk = (nrows / 4) * 32;
+    for (int b = threadIdx.x; b < nblk; b += NT) {
+      const float *src = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float4 t = *(const float4 *)(src + j * PITCH);
+        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+      }
+      uint64_t acc[cgz::Rate<R>::kAcc];
+      cgz::encode_block<R>(v, acc, dbl);
+      stage_block<R>(os, b, acc);
+    }
+    __syncthreads();  // codes staged; every thread is done with xs
+    uint4 *dst = (uint4 *)(payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R);
+    const int n16 = nblk * 2 * R / 16;
+    for (int i = threadIdx.x; i < n16; i += NT) dst[i] = ((const uint4 *)os)[i];
+  }
+}
+
+template <int R, bool BF16>
+__global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict__ payload,
+                                                      const float *__restrict__ gauges,
+                                                      void *__restrict__ out, TileArgs a) {
+  __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
+  constexpr int NC = (TILE_T / 4 * 32 * 2 * R / 16 + NT - 1) / NT;  // 16-B code pieces per thread
+  float *xs = (float *)lds;
+  uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
+  const int64_t field = (int64_t)blockIdx.x / a.chunks;
+  const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * ZFP128_CHUNK;
+  const int tend = min(a.tiles, tile0 + ZFP128_CHUNK);
+  const size_t esz = BF16 ? 2 : 4;
+  G128Frags fr;
+  load_g128<true>(gauges + gauge_index(field, a.batch, a.heads) * D * 128, fr);
+  auto rows = [&](int tile) { return (int)min((int64_t)TILE_T, a.nt - (int64_t)tile * TILE_T); };
+  auto codes = [&](int tile) {
+    return (const uint4 *)(payload + (size_t)(field * (a.tcap / 4) + (a.t0 + (int64_t)tile * TILE_T) / 4) * 32 * 2 * R);
+  };
+  uint4 pre[NC];
+  auto fetch = [&](int tile) {
+    const uint4 *src = codes(tile);
+    const int n16 = (rows(tile) / 4) * 32 * 2 * R / 16;
+#pragma unroll
+    for (int k = 0; k < NC; k++) {
+      const int i = threadIdx.x + NT * k;
+      if (i < n16) pre[k] = src[i];
+    }
+  };
+  if (tile0 < tend) fetch(tile0);
+  for (int tile = tile0; tile < tend; tile++) {
+    const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
+    const int nrows = rows(tile);
+    const int nblk = (nrows / 4) * 32;
+    const int n16 = nblk * 2 * R / 16;
+#pragma unroll
+    for (int k = 0; k < NC; k++) {
+      const int i = threadIdx.x + NT * k;
+      if (i < n16) ((uint4 *)os)[i] = pre[k];
+    }
+    __syncthreads();
+    if (tile + 1 < tend) fetch(tile + 1);
+    // decoded blocks go straight into the split operand tiles (rows past
+    // nrows keep stale values: output rows depend on their own row only and
+    // are not stored)
+    for (int b = threadIdx.x; b < nblk; b += NT) {
+      uint64_t acc[cgz::Rate<R>::kAcc];
+      unstage_block<R>(os, b, acc);
+      float v[16];
+      cgz::decode_block<R>(acc, v);
+      const int off = (b >> 5) * 4 * HP + (b & 31) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        uint2 h, l;
+        split_pair(v[4 * j], v[4 * j + 1], h.x, l.x);
+        split_pair(v[4 * j + 2], v[4 * j + 3], h.y, l.y);
+        *(uint2 *)(sh + off + j * HP) = h;
+        *(uint2 *)(sl + off + j * HP) = l;
+      }
+    }
+    __syncthreads();
+    gauge128_tile<false>(sh, sl, xs, fr);
+    store_tile<BF16>((uint8_t *)out + (size_t)(field * a.tcap + tb) * D * esz, nrows, xs);
+    __syncthreads();
+  }
+}
+
 // all launches of one rate R (encode or decode, storage format, group size)
 template <int R>
 hipError_t zfp_launch_rate(bool encode, bool bf16, int g, const void *src, const float *gauges,
@@ -147,6 +266,24 @@ hipError_t zfp_launch_rate(bool encode, bool bf16, int g, const void *src, const
   CG_L(true, 0) CG_L(true, 8) CG_L(true, 16) CG_L(true, 32)
   CG_L(false, 0) CG_L(false, 8) CG_L(false, 16) CG_L(false, 32)
 #undef CG_L
+  if (g == 128) {
+    TileArgs c = a;
+    const int64_t fields = a.grid / a.tiles;
+    c.chunks = (a.tiles + ZFP128_CHUNK - 1) / ZFP128_CHUNK;
+    const dim3 grid128((unsigned)(fields * c.chunks));
+#define CG_L128(BF)                                                                              \
+  if (bf16 == BF) {                                                                              \
+    if (encode)                                                                                  \
+      hipLaunchKernelGGL((k_zfp_encode128<R, BF>), grid128, block, 0, s, src, gauges,           \
+                         (uint8_t *)dst, c);                                                     \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_zfp_decode128<R, BF>), grid128, block, 0, s, (const uint8_t *)src,  \
+                         gauges, dst, c);                                                        \
+    return hipGetLastError();                                                                    \
+  }
+    CG_L128(true) CG_L128(false)
+#undef CG_L128
+  }
   return hipErrorInvalidValue;
 }
 

@@ -90,8 +90,9 @@ typedef struct cg_shape {
 
 typedef struct cg_gauge {
   int32_t group;   /* g: 0 = identity (no arithmetic), else divides head_dim;
-                      built: 8, 16 and 32 for every backend, 128 for
-                      BLOCK_UNIFORM and KIVI (dense full-head gauge) */
+                      built: 8, 16 and 32 for every backend, 128 (dense
+                      full-head gauge, matrix cores) for ZFP,
+                      BLOCK_UNIFORM and KIVI */
   const float *G;  /* device, fp32 [layers][kv][heads][head_dim/g][g][g];
                       ignored when group == 0 */
 } cg_gauge;

@@ -86,7 +86,8 @@ def test_codec_and_row_validation_before_launch():
     # groups that divide head_dim but are not built are refused before any launch
     Gz = np.zeros(1, np.float32)
     assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, gauge=cg.make_gauge(4, Gz)) == cg.CG_E_UNSUPPORTED
-    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, gauge=cg.make_gauge(128, Gz)) == cg.CG_E_UNSUPPORTED
+    assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 64, gauge=cg.make_gauge(64, Gz)) == cg.CG_E_UNSUPPORTED
+    assert enc(cg.make_codec(cg.CG_BACKEND_NONE, 4), 0, 64, gauge=cg.make_gauge(128, Gz)) == cg.CG_E_UNSUPPORTED
     assert "not built" in cg.cg_last_error()
     assert enc(cg.make_codec(9, 4), 0, 64) == cg.CG_E_INVAL
     assert "backend" in cg.cg_last_error()

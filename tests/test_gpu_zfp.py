@@ -200,3 +200,47 @@ def test_llama8b_class_full_size_sampled_fields():
         p_ref, y_ref = zfp_oracle_field(xf, gauge_of_field(G, f, KV, B, H), g, R, T, T)
         assert np.array_equal(to_host(pay[f * per:(f + 1) * per]), p_ref), f
         assert np.array_equal(to_host(out[f]), y_ref), f
+
+
+@pytest.mark.parametrize("R", [3, 4, 8])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_dense_gauge_zfp_staged(R, bf16):
+    """Full-head gauge (g = 128, matrix cores) with the zfp-style coder.  The
+    dense gauge is not an fmaf chain, so parity is staged: (1) the gauge,
+    through cg_gauge_apply (the routine the fused kernels run), against the
+    fp64 oracle; (2) the codes bit-exact against the oracle's coder applied to
+    those gauged values; (3) the decoded cache bit-exact against the oracle's
+    decode of the same codes taken through the same inverse routine."""
+    t = __import__("torch")
+    # 22 tiles: one full 16-tile workgroup chunk, a ragged chunk, an 8-row last tile
+    L, KV, B, H, T = 1, 2, 1, 2, 64 * 21 + 8
+    x = kv_cpu(400 + R, L, KV, B, H, T, T, 0.95, 4, bf16=bf16)
+    G = gauges_for(410, L, KV, H, 128)
+    pay, out = run_zfp(x, G, 128, R, L, KV, B, H, T, T, bf16)
+    F = n_fields(L, KV, B, H)
+    shape_in = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16 if bf16 else cg.CG_DTYPE_F32)
+    shape32 = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_F32)
+    gauge = cg.make_gauge(128, to_dev(np.ascontiguousarray(G)))
+    xg_d = t.zeros((F, T, D), dtype=t.float32, device="cuda")
+    cg.cg_gauge_apply(shape_in, to_dev(x), gauge, 0, xg_d)
+    t.cuda.synchronize()
+    xg = to_host(xg_d)
+    per = T * D * R // 8
+    dec = np.zeros((F, T, D), np.float32)
+    worst = 0.0
+    for f in range(F):
+        Gf = gauge_of_field(G, f, KV, B, H).astype(np.float64)
+        ref = oracle.gauge_forward_f64(oracle.to_f32(x[f]), Gf, 128)
+        worst = max(worst, float(np.max(np.abs(xg[f] - ref)) / np.max(np.abs(ref))))
+        p_ref = oracle.zfp_encode_field(xg[f], R)
+        assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f"payload mismatch in field {f}"
+        dec[f] = oracle.zfp_decode_field(p_ref, T, D, R)
+    assert worst <= 1e-4, worst
+    y_d = t.zeros((F, T, D), dtype=t.float32, device="cuda")
+    cg.cg_gauge_apply(shape32, to_dev(dec), gauge, 1, y_d)
+    t.cuda.synchronize()
+    y = to_host(y_d)
+    if bf16:
+        assert np.array_equal(out, oracle.f32_to_bf16(y))
+    else:
+        assert np.array_equal(out.view(np.uint32), y.view(np.uint32))
