@@ -23,6 +23,7 @@ CG_HEADER_BYTES = 64
 
 EXPORTED = ["cg_encoded_bytes", "cg_encode", "cg_decode", "cg_roundtrip", "cg_gauge_fit_stats",
             "cg_stats_workspace_bytes", "cg_gauge_from_skew", "cg_gauge_apply", "cg_write_header",
+            "cg_decode_error_workspace_bytes", "cg_decode_error", "cg_cache_error_summary",
             "cg_last_error"]
 
 
@@ -40,6 +41,17 @@ class CgGauge(ctypes.Structure):
 class CgCodec(ctypes.Structure):
     _fields_ = [("backend", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("block_tokens", ctypes.c_int32), ("residual_tokens", ctypes.c_int32)]
+
+
+class CgFieldError(ctypes.Structure):
+    _fields_ = [("sse", ctypes.c_double), ("ref_ss", ctypes.c_double), ("max_abs", ctypes.c_double),
+                ("values", ctypes.c_double)]
+
+
+class CgCacheError(ctypes.Structure):
+    _fields_ = [("mse", ctypes.c_double), ("nrmse", ctypes.c_double), ("key_nrmse", ctypes.c_double),
+                ("value_nrmse", ctypes.c_double), ("max_abs", ctypes.c_double),
+                ("values", ctypes.c_double)]
 
 
 class CgStats(ctypes.Structure):
@@ -82,6 +94,9 @@ def lib():
             "cg_gauge_from_skew": [I64, I32, P, P],
             "cg_gauge_apply": [SP, P, GP, I32, P, P],
             "cg_write_header": [SP, CP, I32, I32, P, U64],
+            "cg_decode_error_workspace_bytes": [SP, GP, CP, I64, I64, ctypes.POINTER(ctypes.c_size_t)],
+            "cg_decode_error": [SP, P, U64, P, U64, GP, CP, I64, I64, P, P, P, ctypes.c_size_t, P, P],
+            "cg_cache_error_summary": [SP, P, ctypes.POINTER(CgCacheError)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -159,6 +174,31 @@ def cg_decode(shape, payload, meta, gauge, codec, t0, nt, kv_out, stream=None):
                                         _ptr(meta), _nbytes(meta), ctypes.byref(gauge),
                                         ctypes.byref(codec), t0, nt, _ptr(kv_out),
                                         _stream(stream)))
+
+
+def cg_decode_error_workspace_bytes(shape, gauge, codec, t0, nt):
+    b = ctypes.c_size_t()
+    _check("cg_decode_error_workspace_bytes", lib().cg_decode_error_workspace_bytes(
+        ctypes.byref(shape), ctypes.byref(gauge), ctypes.byref(codec), t0, nt, ctypes.byref(b)))
+    return b.value
+
+
+def cg_decode_error(shape, payload, meta, gauge, codec, t0, nt, kv_out, kv_ref, workspace, err,
+                    stream=None):
+    """err: device float64 tensor [n_fields, 4] (sse, ref_ss, max_abs, values)."""
+    _check("cg_decode_error", lib().cg_decode_error(
+        ctypes.byref(shape), _ptr(payload), _nbytes(payload), _ptr(meta), _nbytes(meta),
+        ctypes.byref(gauge), ctypes.byref(codec), t0, nt, _ptr(kv_out), _ptr(kv_ref),
+        _ptr(workspace), _nbytes(workspace), _ptr(err), _stream(stream)))
+
+
+def cg_cache_error_summary(shape, err_host: np.ndarray) -> dict:
+    """err_host float64 [n_fields, 4] -> dict of the whole-cache figures."""
+    e = np.ascontiguousarray(err_host, np.float64)
+    out = CgCacheError()
+    _check("cg_cache_error_summary", lib().cg_cache_error_summary(ctypes.byref(shape), e.ctypes.data,
+                                                                  ctypes.byref(out)))
+    return {k: getattr(out, k) for k, _ in CgCacheError._fields_}
 
 
 def cg_roundtrip(shape, kv_in, gauge, codec, payload, meta, kv_out, stream=None):

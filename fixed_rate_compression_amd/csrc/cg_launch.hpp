@@ -21,6 +21,10 @@ struct TileArgs {
   int32_t batch;  // B (gauges are shared across the batch)
   int32_t heads;  // H
   int32_t chunks; // dense gauge: workgroups per field = ceil(tiles / ZFP128_CHUNK)
+  // decode only: reference rows in the output layout (or null) and the
+  // per-workgroup error partials [grid][3] they produce
+  const void *ref;
+  double *epart;
 };
 
 bool zfp_rate_built(int R);
@@ -30,5 +34,9 @@ hipError_t zfp_decode_launch(int R, bool bf16, int g, const uint8_t *payload, co
                              void *out, const TileArgs &a, hipStream_t s);
 hipError_t gauge_rows_launch(bool src_bf16, bool dst_bf16, bool inverse, int g, const void *src,
                              const float *gauges, void *dst, const TileArgs &a, hipStream_t s);
+// per field: sum its `per_field` consecutive error partials in order ->
+// out[field][4] = {sum e^2, sum x^2, max |e|, values}
+hipError_t error_reduce_launch(const double *epart, int64_t fields, int64_t per_field,
+                               double values_per_field, double *out, hipStream_t s);
 
 }  // namespace cgk

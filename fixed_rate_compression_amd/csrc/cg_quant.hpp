@@ -17,6 +17,8 @@ struct QuantArgs {
   int32_t bits;
   int32_t block;     // BU: tokens per block; KIVI: group (32)
   int32_t residual;  // KIVI tail rows
+  const void *ref;   // decode: reference rows for the error sums (or null)
+  double *epart;     // decode: per-workgroup error partials [grid][3]
 };
 
 bool bits_built(int bits);

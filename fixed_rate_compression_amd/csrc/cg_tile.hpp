@@ -82,6 +82,82 @@ __device__ __forceinline__ void store_tile(void *__restrict__ dst, int nrows, co
   }
 }
 
+// Cache-side error of decoded values against the reference, on the values as
+// stored (after rounding to the storage format): sum of squared errors and of
+// squared reference values, and the largest absolute error, all in fp64 (the
+// difference of two storage values is exact in fp64).
+struct ErrAcc {
+  double sse = 0.0, ssr = 0.0, mx = 0.0;
+  __device__ __forceinline__ void add(float xhat, float x) {
+    const double e = (double)xhat - (double)x;
+    sse += e * e;
+    ssr += (double)x * (double)x;
+    mx = fmax(mx, fabs(e));
+  }
+};
+
+// store_tile that also accumulates the error against `ref` (same layout as dst)
+template <bool BF16>
+__device__ __forceinline__ void store_tile_err(void *__restrict__ dst, int nrows, const float *xs,
+                                               const void *__restrict__ ref, ErrAcc &e) {
+  if (BF16) {
+    uint4 *d = (uint4 *)dst;
+    const uint4 *r = (const uint4 *)ref;
+    for (int i = threadIdx.x; i < nrows * 16; i += NT) {
+      const float *s = xs + (i >> 4) * PITCH + (i & 15) * 8;
+      const float4 a = *(const float4 *)s, b = *(const float4 *)(s + 4);
+      const uint4 w = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                                 pack_bf16x2(b.z, b.w));
+      d[i] = w;
+      const uint4 q = r[i];
+      e.add(bf16lo(w.x), bf16lo(q.x)); e.add(bf16hi(w.x), bf16hi(q.x));
+      e.add(bf16lo(w.y), bf16lo(q.y)); e.add(bf16hi(w.y), bf16hi(q.y));
+      e.add(bf16lo(w.z), bf16lo(q.z)); e.add(bf16hi(w.z), bf16hi(q.z));
+      e.add(bf16lo(w.w), bf16lo(q.w)); e.add(bf16hi(w.w), bf16hi(q.w));
+    }
+  } else {
+    float4 *d = (float4 *)dst;
+    const float4 *r = (const float4 *)ref;
+    for (int i = threadIdx.x; i < nrows * 32; i += NT) {
+      const float4 v = *(const float4 *)(xs + (i >> 5) * PITCH + (i & 31) * 4);
+      d[i] = v;
+      const float4 q = r[i];
+      e.add(v.x, q.x); e.add(v.y, q.y); e.add(v.z, q.z); e.add(v.w, q.w);
+    }
+  }
+}
+
+// workgroup total of the error sums in a fixed order -> epart[blockIdx.x][3]
+// (contains a workgroup barrier)
+__device__ __forceinline__ void write_err(ErrAcc e, double *__restrict__ epart) {
+  __shared__ double red[NT / 64][3];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    e.sse += __shfl_xor(e.sse, m);
+    e.ssr += __shfl_xor(e.ssr, m);
+    e.mx = fmax(e.mx, __shfl_xor(e.mx, m));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[w][0] = e.sse;
+    red[w][1] = e.ssr;
+    red[w][2] = e.mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double a = red[0][0], b = red[0][1], c = red[0][2];
+    for (int k = 1; k < NT / 64; k++) {
+      a += red[k][0];
+      b += red[k][1];
+      c = fmax(c, red[k][2]);
+    }
+    double *o = epart + (size_t)blockIdx.x * 3;
+    o[0] = a;
+    o[1] = b;
+    o[2] = c;
+  }
+}
+
 // Gauge (INV = false: y = G x) or inverse gauge (INV = true: y = G^T x) of
 // every token row of the tile, in place, for group size G in {8, 16, 32}.
 // Each output is an fmaf chain over the group's inputs in index order from

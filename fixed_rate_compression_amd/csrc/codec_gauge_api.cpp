@@ -344,10 +344,19 @@ int cg_encode(const cg_shape *shape, const void *kv, const cg_gauge *gauge, cons
   return CG_OK;
 }
 
-int cg_decode(const cg_shape *shape, const void *payload, uint64_t payload_cap, const void *meta,
-              uint64_t meta_cap, const cg_gauge *gauge, const cg_codec *codec, int64_t t0,
-              int64_t nt, void *kv_out, void *stream) {
-  g_err.clear();
+namespace {
+
+// error partials per field of a decode launch (one per workgroup)
+int64_t err_per_field(const cg_codec *c, int g, int64_t nt) {
+  const int64_t tiles = (nt + cgk::TILE_T - 1) / cgk::TILE_T;
+  if (g == 128) return (tiles + cgk::ZFP128_CHUNK - 1) / cgk::ZFP128_CHUNK;
+  (void)c;
+  return tiles;
+}
+
+int decode_impl(const cg_shape *shape, const void *payload, uint64_t payload_cap, const void *meta,
+                uint64_t meta_cap, const cg_gauge *gauge, const cg_codec *codec, int64_t t0,
+                int64_t nt, void *kv_out, const void *ref, double *epart, void *stream) {
   int rc;
   if ((rc = check_shape(shape))) return rc;
   if ((rc = check_codec(codec, shape))) return rc;
@@ -365,24 +374,103 @@ int cg_decode(const cg_shape *shape, const void *payload, uint64_t payload_cap, 
   const bool bf16 = shape->dtype == CG_DTYPE_BF16;
   const int g = gauge->group;
   hipError_t e = hipSuccess;
+  cgk::TileArgs ta = tile_args(shape, t0, nt);
+  ta.ref = ref;
+  ta.epart = epart;
   switch (codec->backend) {
     case CG_BACKEND_NONE:
-      e = cgk::gauge_rows_launch(false, bf16, true, g, payload, gauge->G, kv_out, tile_args(shape, t0, nt), s);
+      e = cgk::gauge_rows_launch(false, bf16, true, g, payload, gauge->G, kv_out, ta, s);
       break;
     case CG_BACKEND_ZFP:
-      e = cgk::zfp_decode_launch(codec->bits, bf16, g, (const uint8_t *)payload, gauge->G, kv_out,
-                                 tile_args(shape, t0, nt), s);
+      e = cgk::zfp_decode_launch(codec->bits, bf16, g, (const uint8_t *)payload, gauge->G, kv_out, ta, s);
       break;
     case CG_BACKEND_BLOCK_UNIFORM:
     case CG_BACKEND_KIVI: {
       cgq::QuantArgs q = cgq::make_args(shape->token_capacity, shape->tokens, t0, nt, n_fields(shape),
                                         shape->batch, shape->heads, codec->backend, codec->bits,
                                         codec->block_tokens, codec->residual_tokens, shape->kv);
+      q.ref = ref;
+      q.epart = epart;
       e = cgq::decode_launch(q, bf16, g, (const uint8_t *)payload, (const float *)meta, gauge->G, kv_out, s);
       break;
     }
   }
   if (e != hipSuccess) return hip_fail(e, "cg_decode launch");
+  return CG_OK;
+}
+
+}  // namespace
+
+int cg_decode(const cg_shape *shape, const void *payload, uint64_t payload_cap, const void *meta,
+              uint64_t meta_cap, const cg_gauge *gauge, const cg_codec *codec, int64_t t0,
+              int64_t nt, void *kv_out, void *stream) {
+  g_err.clear();
+  return decode_impl(shape, payload, payload_cap, meta, meta_cap, gauge, codec, t0, nt, kv_out,
+                     nullptr, nullptr, stream);
+}
+
+int cg_decode_error_workspace_bytes(const cg_shape *shape, const cg_gauge *gauge,
+                                    const cg_codec *codec, int64_t t0, int64_t nt, size_t *bytes) {
+  g_err.clear();
+  int rc;
+  if (!bytes) return fail(CG_E_INVAL, "bytes is NULL");
+  if ((rc = check_shape(shape))) return rc;
+  if ((rc = check_codec(codec, shape))) return rc;
+  if ((rc = check_gauge(gauge, shape, codec))) return rc;
+  if ((rc = check_rows(shape, codec, t0, nt))) return rc;
+  *bytes = (size_t)n_fields(shape) * (size_t)err_per_field(codec, gauge->group, nt) * 3 * sizeof(double);
+  return CG_OK;
+}
+
+int cg_decode_error(const cg_shape *shape, const void *payload, uint64_t payload_cap,
+                    const void *meta, uint64_t meta_cap, const cg_gauge *gauge,
+                    const cg_codec *codec, int64_t t0, int64_t nt, void *kv_out,
+                    const void *kv_ref, void *workspace, size_t ws_bytes, cg_field_error *err,
+                    void *stream) {
+  g_err.clear();
+  size_t need = 0;
+  int rc = cg_decode_error_workspace_bytes(shape, gauge, codec, t0, nt, &need);
+  if (rc) return rc;
+  if (!kv_ref || !err) return fail(CG_E_INVAL, "kv_ref or err is NULL");
+  if (need && (!workspace || ws_bytes < need))
+    return fail(CG_E_SIZE, "workspace missing or smaller than %zu bytes", need);
+  if (nt == 0) {  // no rows: every field's sums are zero (written by the reduce kernel)
+    hipError_t e = cgk::error_reduce_launch(nullptr, n_fields(shape), 0, 0.0, (double *)err,
+                                            (hipStream_t)stream);
+    return e == hipSuccess ? CG_OK : hip_fail(e, "cg_decode_error reduce");
+  }
+  double *epart = (double *)workspace;
+  rc = decode_impl(shape, payload, payload_cap, meta, meta_cap, gauge, codec, t0, nt, kv_out, kv_ref,
+                   epart, stream);
+  if (rc) return rc;
+  hipError_t e = cgk::error_reduce_launch(epart, n_fields(shape), err_per_field(codec, gauge->group, nt),
+                                          (double)nt * shape->head_dim, (double *)err, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cg_decode_error reduce");
+  return CG_OK;
+}
+
+int cg_cache_error_summary(const cg_shape *shape, const cg_field_error *err, cg_cache_error *out) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if (!err || !out) return fail(CG_E_INVAL, "err or out is NULL");
+  double sse[2] = {0.0, 0.0}, ssr[2] = {0.0, 0.0}, n[2] = {0.0, 0.0}, mx = 0.0;
+  const int64_t F = n_fields(shape);
+  for (int64_t f = 0; f < F; f++) {
+    const int kind = (int)((f / ((int64_t)shape->batch * shape->heads)) % shape->kv);
+    sse[kind] += err[f].sse;
+    ssr[kind] += err[f].ref_ss;
+    n[kind] += err[f].values;
+    mx = fmax(mx, err[f].max_abs);
+  }
+  auto nrmse = [](double e, double r) { return r > 0.0 ? sqrt(e / r) : (e > 0.0 ? INFINITY : 0.0); };
+  const double E = sse[0] + sse[1], Rr = ssr[0] + ssr[1], N = n[0] + n[1];
+  out->values = N;
+  out->mse = N > 0.0 ? E / N : 0.0;
+  out->nrmse = nrmse(E, Rr);
+  out->key_nrmse = nrmse(sse[0], ssr[0]);
+  out->value_nrmse = shape->kv == 2 ? nrmse(sse[1], ssr[1]) : 0.0;
+  out->max_abs = mx;
   return CG_OK;
 }
 

@@ -63,7 +63,14 @@ __global__ __launch_bounds__(NT) void k_gauge_rows(const void *__restrict__ src,
     gauge_tile<G, INV>(xs, nrows, gauges + gauge_index(field, a.batch, a.heads) * D * G);
     __syncthreads();
   }
-  store_tile<DST_BF16>((uint8_t *)dst + (size_t)row0 * D * (DST_BF16 ? 2 : 4), nrows, xs);
+  const size_t off = (size_t)row0 * D * (DST_BF16 ? 2 : 4);
+  if (a.ref) {
+    ErrAcc e;
+    store_tile_err<DST_BF16>((uint8_t *)dst + off, nrows, xs, (const uint8_t *)a.ref + off, e);
+    write_err(e, a.epart);
+  } else {
+    store_tile<DST_BF16>((uint8_t *)dst + off, nrows, xs);
+  }
 }
 
 template <bool SB, bool DB, bool INV>
@@ -99,6 +106,32 @@ hipError_t gauge_rows_launch(bool src_bf16, bool dst_bf16, bool inverse, int g, 
                                 : gauge_rows_g<true, false, false>(g, src, gauges, dst, a, s);
   return dst_bf16 ? gauge_rows_g<false, true, false>(g, src, gauges, dst, a, s)
                   : gauge_rows_g<false, false, false>(g, src, gauges, dst, a, s);
+}
+
+__global__ __launch_bounds__(64) void k_error_reduce(const double *__restrict__ epart,
+                                                      int64_t per_field, double values,
+                                                      double *__restrict__ out) {
+  if (threadIdx.x != 0) return;
+  const int64_t f = blockIdx.x;
+  const double *p = epart + (size_t)f * per_field * 3;
+  double a = 0.0, b = 0.0, c = 0.0;
+  for (int64_t j = 0; j < per_field; j++) {
+    a += p[3 * j];
+    b += p[3 * j + 1];
+    c = fmax(c, p[3 * j + 2]);
+  }
+  double *o = out + (size_t)f * 4;
+  o[0] = a;
+  o[1] = b;
+  o[2] = c;
+  o[3] = values;
+}
+
+hipError_t error_reduce_launch(const double *epart, int64_t fields, int64_t per_field,
+                               double values_per_field, double *out, hipStream_t s) {
+  hipLaunchKernelGGL(k_error_reduce, dim3((unsigned)fields), dim3(64), 0, s, epart, per_field,
+                     values_per_field, out);
+  return hipGetLastError();
 }
 
 }  // namespace cgk

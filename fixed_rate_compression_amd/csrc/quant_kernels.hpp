@@ -38,6 +38,8 @@ struct QK {
   int32_t batch, heads, kv;
   int32_t block;            // block-uniform: tokens per range block
   int32_t residual;         // KIVI: tail rows kept in the storage format
+  const void *ref;          // decode: reference rows for the error sums (or null)
+  double *epart;            // decode: per-workgroup error partials [grid][3]
 };
 
 // valid rows of tile `tile` of the call's row range
@@ -360,6 +362,7 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
     }
   };
   if (tile0 < tend) fetch(tile0);
+  ErrAcc err;
   for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
     const int nrows = tile_rows(a, tile);
@@ -375,9 +378,14 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
     }
     if (tile + 1 < tend) fetch(tile + 1);
     inverse_gauged_tile<G>(lds, t, j, v, nrows, Gf, fr);
-    store_tile<BF16>((uint8_t *)out + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4), nrows, xs);
+    const size_t off = (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
+    if (a.ref)
+      store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
+    else
+      store_tile<BF16>((uint8_t *)out + off, nrows, xs);
     __syncthreads();
   }
+  if (a.ref) write_err(err, a.epart);
 }
 
 // ---------------------------------------------------------------------------
@@ -528,6 +536,7 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
     }
   };
   if (tile0 < tend) fetch(tile0);
+  ErrAcc err;
   for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
     const int nrows = tile_rows(a, tile);
@@ -561,9 +570,14 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
     }
     if (tile + 1 < tend) fetch(tile + 1);
     inverse_gauged_tile<G>(lds, t, j, v, nrows, Gf, fr);
-    store_tile<BF16>((uint8_t *)out + (size_t)(f * a.tcap + tb) * D * ESZ, nrows, xs);
+    const size_t off = (size_t)(f * a.tcap + tb) * D * ESZ;
+    if (a.ref)
+      store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
+    else
+      store_tile<BF16>((uint8_t *)out + off, nrows, xs);
     __syncthreads();
   }
+  if (a.ref) write_err(err, a.epart);
 }
 
 // dense-gauge rows kernel behind cg_gauge_apply(g = 128): same tiles, same

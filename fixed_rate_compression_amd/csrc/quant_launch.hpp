@@ -19,6 +19,8 @@ inline QK make_qk(const QuantArgs &q, int tiles_per_chunk) {
   a.kv = q.kv;
   a.block = q.block;
   a.residual = q.residual;
+  a.ref = q.ref;
+  a.epart = q.epart;
   return a;
 }
 

@@ -127,7 +127,14 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
     __syncthreads();
   }
   const size_t esz = BF16 ? 2 : 4;
-  store_tile<BF16>((uint8_t *)out + (size_t)row0 * D * esz, nrows, xs);
+  if (a.ref) {
+    ErrAcc e;
+    store_tile_err<BF16>((uint8_t *)out + (size_t)row0 * D * esz, nrows, xs,
+                         (const uint8_t *)a.ref + (size_t)row0 * D * esz, e);
+    write_err(e, a.epart);
+  } else {
+    store_tile<BF16>((uint8_t *)out + (size_t)row0 * D * esz, nrows, xs);
+  }
 }
 
 // Dense (g = 128) gauge on the matrix cores (gauge128.hpp): a workgroup walks
@@ -211,6 +218,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
     }
   };
   if (tile0 < tend) fetch(tile0);
+  ErrAcc err;
   for (int tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
     const int nrows = rows(tile);
@@ -243,9 +251,14 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
     }
     __syncthreads();
     gauge128_tile<false>(sh, sl, xs, fr);
-    store_tile<BF16>((uint8_t *)out + (size_t)(field * a.tcap + tb) * D * esz, nrows, xs);
+    const size_t off = (size_t)(field * a.tcap + tb) * D * esz;
+    if (a.ref)
+      store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
+    else
+      store_tile<BF16>((uint8_t *)out + off, nrows, xs);
     __syncthreads();
   }
+  if (a.ref) write_err(err, a.epart);
 }
 
 // all launches of one rate R (encode or decode, storage format, group size)

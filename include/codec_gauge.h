@@ -155,6 +155,54 @@ int cg_decode(const cg_shape *shape, const void *payload, uint64_t payload_cap,
               const void *meta, uint64_t meta_cap, const cg_gauge *gauge,
               const cg_codec *codec, int64_t t0, int64_t nt, void *kv_out, void *stream);
 
+/*
+ * Cache-side error (evaluation protocol, arXiv page: compressed bytes, actual
+ * bits/value, KV MSE, KV NRMSE, key/value NRMSE and maximum absolute error;
+ * the evaluator keeps raw sums and counts).  Per field, over the decoded rows
+ * as stored (after rounding to the storage format), against a reference in
+ * the same layout:
+ *   sse     = sum (x_hat - x)^2      ref_ss = sum x^2
+ *   max_abs = max |x_hat - x|        values = rows * head_dim
+ * Sums are fp64, reduced in a fixed order (deterministic).
+ */
+typedef struct cg_field_error {
+  double sse;
+  double ref_ss;
+  double max_abs;
+  double values;
+} cg_field_error;
+
+/* Whole-cache figures from the per-field sums: mse = sse / values,
+   nrmse = sqrt(sse / ref_ss) (over all, key and value fields), max_abs. */
+typedef struct cg_cache_error {
+  double mse;
+  double nrmse;
+  double key_nrmse;
+  double value_nrmse; /* 0 when kv == 1 */
+  double max_abs;
+  double values;
+} cg_cache_error;
+
+/* Device scratch needed by cg_decode_error for these rows (host only). */
+int cg_decode_error_workspace_bytes(const cg_shape *shape, const cg_gauge *gauge,
+                                    const cg_codec *codec, int64_t t0, int64_t nt, size_t *bytes);
+
+/*
+ * cg_decode that also accumulates the error of every decoded value against
+ * kv_ref (device, storage format, KV layout; rows [t0, t0+nt) are read) in the
+ * kernels that store it.  err: device cg_field_error[n_fields], overwritten
+ * (values = nt * head_dim).  Same validation and errors as cg_decode, plus
+ * CG_E_SIZE for a missing or small workspace.
+ */
+int cg_decode_error(const cg_shape *shape, const void *payload, uint64_t payload_cap,
+                    const void *meta, uint64_t meta_cap, const cg_gauge *gauge,
+                    const cg_codec *codec, int64_t t0, int64_t nt, void *kv_out,
+                    const void *kv_ref, void *workspace, size_t ws_bytes, cg_field_error *err,
+                    void *stream);
+
+/* Host: per-field sums (host array of n_fields) -> whole-cache figures. */
+int cg_cache_error_summary(const cg_shape *shape, const cg_field_error *err, cg_cache_error *out);
+
 /* cg_encode of rows [0, tokens) followed by cg_decode of the same rows. */
 int cg_roundtrip(const cg_shape *shape, const void *kv_in, const cg_gauge *gauge,
                  const cg_codec *codec, void *payload, uint64_t payload_cap, void *meta,

@@ -1,0 +1,106 @@
+"""GPU parity of the cache-side error sums fused into decode
+(cg_decode_error) against the oracle's plain fp64 sums over the same decoded
+values ("Codec-Gauge", arXiv HTML, evaluation protocol: KV MSE, NRMSE,
+key/value NRMSE, maximum absolute error from raw sums and counts).  The
+decoded cache itself must equal cg_decode's output bit for bit."""
+import numpy as np
+import pytest
+
+from fixed_rate_compression_amd import binding as cg
+from gpu_util import D, gauges_for, kv_cpu, n_fields, to_dev, to_host
+from oracle import metrics
+
+pytestmark = pytest.mark.gpu
+
+
+def as_f64(a):
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if a.dtype == np.uint16 \
+        else a.astype(np.float64)
+
+
+def run(x, G, g, codec, L, KV, B, H, T, bf16, t0=0, nt=None):
+    import torch
+    nt = T if nt is None else nt
+    shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16 if bf16 else cg.CG_DTYPE_F32)
+    gauge = cg.make_gauge(g, to_dev(np.ascontiguousarray(G)) if G is not None else None)
+    xd = to_dev(x)
+    pb, mb, _ = cg.cg_encoded_bytes(shape, codec)
+    pay = torch.zeros(max(pb, 1), dtype=torch.uint8, device="cuda")
+    meta = torch.zeros(max(mb // 4, 1), dtype=torch.float32, device="cuda") if mb else None
+    cg.cg_encode(shape, xd, gauge, codec, 0, T, pay, meta)
+    out1 = torch.zeros_like(xd)
+    out2 = torch.zeros_like(xd)
+    cg.cg_decode(shape, pay, meta, gauge, codec, t0, nt, out1)
+    ws = torch.zeros(max(cg.cg_decode_error_workspace_bytes(shape, gauge, codec, t0, nt), 8),
+                     dtype=torch.uint8, device="cuda")
+    err = torch.full((n_fields(L, KV, B, H), 4), -1.0, dtype=torch.float64, device="cuda")
+    cg.cg_decode_error(shape, pay, meta, gauge, codec, t0, nt, out2, xd, ws, err)
+    torch.cuda.synchronize()
+    return shape, to_host(out1), to_host(out2), err.cpu().numpy()
+
+
+def check(x, out1, out2, err, L, KV, B, H, t0, nt, exact_zero=False):
+    assert np.array_equal(out1, out2)
+    F = n_fields(L, KV, B, H)
+    for f in range(F):
+        ref = metrics.field_error(as_f64(out2[f, t0:t0 + nt]), as_f64(x[f, t0:t0 + nt]))
+        assert err[f, 3] == ref[3]
+        assert err[f, 2] == ref[2]
+        assert err[f, 0] == pytest.approx(ref[0], rel=1e-12, abs=1e-300)
+        assert err[f, 1] == pytest.approx(ref[1], rel=1e-12)
+        if exact_zero:
+            assert err[f, 0] == 0.0 and err[f, 2] == 0.0
+
+
+@pytest.mark.parametrize("g,R", [(16, 4), (8, 3), (128, 4), (0, 6)])
+def test_zfp_error_sums(g, R):
+    L, KV, B, H, T = 1, 2, 1, 2, 64 * 17 + 12     # ragged tile; two chunks for g = 128
+    x = kv_cpu(500 + g, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    G = gauges_for(510 + g, L, KV, H, g)
+    shape, o1, o2, err = run(x, G, g, cg.make_codec(cg.CG_BACKEND_ZFP, R), L, KV, B, H, T, True)
+    check(x, o1, o2, err, L, KV, B, H, 0, T)
+    s = cg.cg_cache_error_summary(shape, err)
+    assert 0.0 < s["nrmse"] < 0.5 and s["values"] == n_fields(L, KV, B, H) * T * D
+
+
+def test_zfp_error_sums_fp32_partial_rows():
+    L, KV, B, H, T = 1, 2, 2, 1, 256
+    x = kv_cpu(520, L, KV, B, H, T, T, 0.9, 2, bf16=False)
+    G = gauges_for(521, L, KV, H, 32)
+    _, o1, o2, err = run(x, G, 32, cg.make_codec(cg.CG_BACKEND_ZFP, 4), L, KV, B, H, T, False,
+                         t0=64, nt=132)
+    check(x, o1, o2, err, L, KV, B, H, 64, 132)
+
+
+@pytest.mark.parametrize("backend,bits,blk,res,g", [
+    (cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64, 0, 8),
+    (cg.CG_BACKEND_BLOCK_UNIFORM, 4, 32, 0, 128),
+    (cg.CG_BACKEND_KIVI, 2, 32, 128, 16),
+    (cg.CG_BACKEND_KIVI, 4, 32, 128, 128),
+])
+def test_quantizer_error_sums(backend, bits, blk, res, g):
+    L, KV, B, H, T = 1, 2, 1, 2, 64 * 18
+    x = kv_cpu(530 + bits, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    G = gauges_for(531 + g, L, KV, H, g)
+    _, o1, o2, err = run(x, G, g, cg.make_codec(backend, bits, blk, res), L, KV, B, H, T, True)
+    check(x, o1, o2, err, L, KV, B, H, 0, T)
+
+
+def test_sanity_rows_identity_clone_and_gauge_round_trip():
+    # identity clone: zero error; gauge round trip without compression: tiny
+    L, KV, B, H, T = 1, 2, 1, 2, 320
+    x = kv_cpu(540, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    none = cg.make_codec(cg.CG_BACKEND_NONE, 0)
+    shape, o1, o2, err = run(x, None, 0, none, L, KV, B, H, T, True)
+    check(x, o1, o2, err, L, KV, B, H, 0, T, exact_zero=True)
+    G = gauges_for(541, L, KV, H, 16)
+    shape, o1, o2, err = run(x, G, 16, none, L, KV, B, H, T, True)
+    check(x, o1, o2, err, L, KV, B, H, 0, T)
+    assert cg.cg_cache_error_summary(shape, err)["nrmse"] < 1e-3
+
+
+def test_no_rows_gives_zero_sums():
+    L, KV, B, H, T = 1, 1, 1, 1, 64
+    x = kv_cpu(550, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    _, _, _, err = run(x, None, 0, cg.make_codec(cg.CG_BACKEND_ZFP, 4), L, KV, B, H, T, True, t0=0, nt=0)
+    assert np.all(err == 0.0)
