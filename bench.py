@@ -205,11 +205,21 @@ def _codec_line(name, shape, x, G, g, codec, steps, warmup, esz, desc):
     enc()
     te = _time(enc, steps, warmup)
     td = _time(dec, steps, warmup)
+    # decode with the cache-side error sums against the input (fused in the decode kernels)
+    ws = torch.empty(max(cg.cg_decode_error_workspace_bytes(shape, gauge, codec, 0, T), 8),
+                     dtype=torch.uint8, device="cuda")
+    err = torch.empty((x.shape[0], 4), dtype=torch.float64, device="cuda")
+    dece = lambda: cg.cg_decode_error(shape, pay, meta, gauge, codec, 0, T, out, x, ws, err)
+    tde = _time(dece, steps, warmup)
+    summ = cg.cg_cache_error_summary(shape, err.cpu().numpy())
     N = x.numel()
     alg = N * esz + pb + mb
-    del pay, meta, out
+    del pay, meta, out, ws
     torch.cuda.empty_cache()
     return {"workload": name, "desc": desc, "values": N, "bits_per_value": round(8.0 * (pb + mb + hb) / N, 6),
+            "kv_nrmse": round(summ["nrmse"], 6), "key_nrmse": round(summ["key_nrmse"], 6),
+            "value_nrmse": round(summ["value_nrmse"], 6), "kv_mse": summ["mse"],
+            "max_abs_err": summ["max_abs"], "decode_with_error_ms": round(tde * 1e3, 4),
             "encode_ms": round(te * 1e3, 4), "decode_ms": round(td * 1e3, 4),
             "encode_kv_GBs": round(N * esz / te / 1e9, 2), "decode_kv_GBs": round(N * esz / td / 1e9, 2),
             "encode_hbm_frac": round(alg / te / 1e9 / HBM_PEAK_GBS, 4),
