@@ -24,7 +24,10 @@ CG_HEADER_BYTES = 64
 EXPORTED = ["cg_encoded_bytes", "cg_encode", "cg_decode", "cg_roundtrip", "cg_gauge_fit_stats",
             "cg_stats_workspace_bytes", "cg_gauge_from_skew", "cg_gauge_apply", "cg_write_header",
             "cg_decode_error_workspace_bytes", "cg_decode_error", "cg_cache_error_summary",
-            "cg_last_error"]
+            "cg_adamw_update", "cg_gauge_control", "cg_second_moment_workspace_bytes",
+            "cg_second_moment", "cg_last_error"]
+
+CG_CONTROL_IDENTITY, CG_CONTROL_HADAMARD, CG_CONTROL_DCT, CG_CONTROL_ORTHONORMALIZE, CG_CONTROL_KLT = range(5)
 
 
 class CgShape(ctypes.Structure):
@@ -97,6 +100,11 @@ def lib():
             "cg_decode_error_workspace_bytes": [SP, GP, CP, I64, I64, ctypes.POINTER(ctypes.c_size_t)],
             "cg_decode_error": [SP, P, U64, P, U64, GP, CP, I64, I64, P, P, P, ctypes.c_size_t, P, P],
             "cg_cache_error_summary": [SP, P, ctypes.POINTER(CgCacheError)],
+            "cg_adamw_update": [I64, P, P, P, P, I64, ctypes.c_double, ctypes.c_double,
+                                ctypes.c_double, ctypes.c_double, ctypes.c_double],
+            "cg_gauge_control": [I32, I64, I32, P, P],
+            "cg_second_moment_workspace_bytes": [SP, I32, ctypes.POINTER(ctypes.c_size_t)],
+            "cg_second_moment": [SP, P, I32, P, ctypes.c_size_t, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -116,6 +124,8 @@ def _check(fn, rc):
 def _ptr(t):
     if t is None:
         return None
+    if isinstance(t, int):          # a raw device address (e.g. a window inside a tensor)
+        return t
     if isinstance(t, np.ndarray):
         assert t.flags["C_CONTIGUOUS"]
         return t.ctypes.data
@@ -201,6 +211,43 @@ def cg_cache_error_summary(shape, err_host: np.ndarray) -> dict:
     return {k: getattr(out, k) for k, _ in CgCacheError._fields_}
 
 
+def cg_adamw_update(param, grad, m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                    weight_decay=1e-2):
+    """In place on host fp64 arrays of equal size."""
+    arrs = [param, grad, m, v]
+    for a in arrs:
+        assert isinstance(a, np.ndarray) and a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+        assert a.size == param.size
+    _check("cg_adamw_update", lib().cg_adamw_update(param.size, *[a.ctypes.data for a in arrs], step,
+                                                    lr, beta1, beta2, eps, weight_decay))
+
+
+def cg_gauge_control(kind, n, g, M=None) -> np.ndarray:
+    """-> fp32 [n, g, g] control gauges (M fp64 [n, g, g] for ORTHONORMALIZE / KLT)."""
+    G = np.empty((n, g, g), np.float32)
+    Mc = np.ascontiguousarray(M, np.float64) if M is not None else None
+    if Mc is not None:
+        assert Mc.shape == (n, g, g)
+    _check("cg_gauge_control", lib().cg_gauge_control(kind, n, g, Mc.ctypes.data if Mc is not None else None,
+                                                      G.ctypes.data))
+    return G
+
+
+def cg_second_moment_workspace_bytes(shape, g):
+    b = ctypes.c_size_t()
+    _check("cg_second_moment_workspace_bytes",
+           lib().cg_second_moment_workspace_bytes(ctypes.byref(shape), g, ctypes.byref(b)))
+    return b.value
+
+
+def cg_second_moment(shape, kv, g, workspace, stream=None) -> np.ndarray:
+    """-> fp64 [layers, kv, heads, d/g, g, g] second moments (synchronous)."""
+    M = np.empty((shape.layers, shape.kv, shape.heads, shape.head_dim // g, g, g), np.float64)
+    _check("cg_second_moment", lib().cg_second_moment(ctypes.byref(shape), _ptr(kv), g, _ptr(workspace),
+                                                      _nbytes(workspace), M.ctypes.data, _stream(stream)))
+    return M
+
+
 def cg_roundtrip(shape, kv_in, gauge, codec, payload, meta, kv_out, stream=None):
     _check("cg_roundtrip", lib().cg_roundtrip(ctypes.byref(shape), _ptr(kv_in),
                                               ctypes.byref(gauge), ctypes.byref(codec),
@@ -235,10 +282,12 @@ def cg_gauge_fit_stats(shape, kv, g, A_host: np.ndarray, T_b, tau, lambda_f, lam
     """Returns (stats structured array [n_fields], dA fp64 or None)."""
     nf = shape.layers * shape.kv * shape.batch * shape.heads
     out = (CgStats * nf)()
-    A = np.ascontiguousarray(A_host, np.float64)
+    A = np.ascontiguousarray(A_host, np.float64) if A_host is not None else None
+    grad = grad and g != 0
     dA = np.zeros((nf, shape.head_dim // g, g, g), np.float64) if grad else None
     _check("cg_gauge_fit_stats", lib().cg_gauge_fit_stats(
-        ctypes.byref(shape), _ptr(kv), g, A.ctypes.data, T_b, tau, lambda_f, lambda_r,
+        ctypes.byref(shape), _ptr(kv), g, A.ctypes.data if A is not None else None, T_b, tau,
+        lambda_f, lambda_r,
         _ptr(workspace), _nbytes(workspace), ctypes.cast(out, ctypes.c_void_p),
         dA.ctypes.data if grad else None, _stream(stream)))
     stats = np.array([(o.L_freq, o.L_rate, o.L, o.sum_E) for o in out],

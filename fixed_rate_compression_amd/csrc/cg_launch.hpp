@@ -34,6 +34,10 @@ hipError_t zfp_decode_launch(int R, bool bf16, int g, const uint8_t *payload, co
                              void *out, const TileArgs &a, hipStream_t s);
 hipError_t gauge_rows_launch(bool src_bf16, bool dst_bf16, bool inverse, int g, const void *src,
                              const float *gauges, void *dst, const TileArgs &a, hipStream_t s);
+// per-group second moments: part[field][moment_chunks(tokens)][D * g] (fp64)
+int64_t moment_chunks(int64_t tokens);
+hipError_t second_moment_launch(bool bf16, int g, const void *kv, int64_t tcap, int64_t tokens,
+                                int64_t fields, double *part, hipStream_t s);
 // per field: sum its `per_field` consecutive error partials in order ->
 // out[field][4] = {sum e^2, sum x^2, max |e|, values}
 hipError_t error_reduce_launch(const double *epart, int64_t fields, int64_t per_field,

@@ -252,6 +252,48 @@ int cg_gauge_from_skew(int64_t n, int32_t g, const double *A_host, float *G_host
 int cg_gauge_apply(const cg_shape *shape, const void *kv, const cg_gauge *gauge,
                    int32_t direction, float *out, void *stream);
 
+/*
+ * Gauge training and coordinate controls.
+ *
+ * One AdamW step (gauge-training paragraph, arXiv page: the gauge parameters
+ * are optimized with AdamW; decoupled weight decay, Loshchilov and Hutter):
+ *   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) grad;  v <- b2 v + (1 - b2) grad^2
+ *   p <- p - lr (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps)
+ * param, grad, m, v: host fp64 arrays of n values (m, v start at 0); step >= 1.
+ */
+int cg_adamw_update(int64_t n, double *param, const double *grad, double *m, double *v,
+                    int64_t step, double lr, double beta1, double beta2, double eps,
+                    double weight_decay);
+
+/* control gauges (main-grid and coordinate-control paragraphs, arXiv page) */
+#define CG_CONTROL_IDENTITY 0
+#define CG_CONTROL_HADAMARD 1       /* Sylvester order, scaled 1/sqrt(g); g a power of two */
+#define CG_CONTROL_DCT 2            /* orthonormal DCT-II, rows = frequencies */
+#define CG_CONTROL_ORTHONORMALIZE 3 /* Q of M = Q R with diag(R) > 0 (Haar for Gaussian M) */
+#define CG_CONTROL_KLT 4            /* rows = eigenvectors of the symmetric M, decreasing
+                                       eigenvalue, largest-magnitude component positive */
+
+/*
+ * n control gauges of size g x g, computed in fp64 and rounded to fp32:
+ * G_host fp32 [n][g][g]; M_host fp64 [n][g][g] for ORTHONORMALIZE and KLT
+ * (a random matrix drawn by the caller; a second moment from
+ * cg_second_moment), else ignored (may be NULL).  Host only.
+ */
+int cg_gauge_control(int32_t kind, int64_t n, int32_t g, const double *M_host, float *G_host);
+
+/* Device scratch needed by cg_second_moment (host only). */
+int cg_second_moment_workspace_bytes(const cg_shape *shape, int32_t g, size_t *bytes);
+
+/*
+ * Uncentered second moments per gauge group (input of the KLT control):
+ *   M[l][s][h][r] = sum over the batch and rows [0, tokens) of x_t[r] x_t[r]^T
+ * kv: device, storage format, KV layout; g in {8, 16, 32, 128}; M_host fp64
+ * [layers][kv][heads][d/g][g][g] (host, overwritten).  Products and sums in
+ * fp64, reduced in a fixed order.  Synchronous.
+ */
+int cg_second_moment(const cg_shape *shape, const void *kv, int32_t g, void *workspace,
+                     size_t ws_bytes, double *M_host, void *stream);
+
 /* Write the fixed-size shape header of one (layer, kv) tensor into a host
    buffer of >= CG_HEADER_BYTES bytes. */
 int cg_write_header(const cg_shape *shape, const cg_codec *codec, int32_t layer, int32_t kv,
