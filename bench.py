@@ -149,14 +149,17 @@ def cpu_baseline(s, n_fields=64):
 # the other workloads (one JSON line each with --workload all)
 # ---------------------------------------------------------------------------
 
-def _gen(F, T, Tcap, rho, seed, outliers, bf16, scale_fields=None, windows=1):
+def _gen(F, T, Tcap, rho, seed, outliers, bf16, scale_seed=None, windows=1):
+    """Synthetic cache: per-field channel scales from scale_seed (default: seed),
+    token noise from seed -- equal scale seeds give the same 'model' with
+    different text."""
     import torch
 
     from fixed_rate_compression_amd import synth
     D = 128
     x = torch.zeros((F * windows, Tcap // windows, D), dtype=torch.bfloat16 if bf16 else torch.float32,
                     device="cuda")
-    sc = synth.channel_scales_many(seed, range(F), D, outliers)
+    sc = synth.channel_scales_many(seed if scale_seed is None else scale_seed, range(F), D, outliers)
     if windows > 1:
         sc = np.repeat(sc, windows, axis=0)
     synth.generate_gpu(x, T // windows, rho, seed, np.arange(F * windows), sc)
@@ -321,7 +324,47 @@ def workload_lines(steps, warmup):
                   "kv_GBs_with_grad": round(N * 2 / wall / 1e9, 2),
                   "kv_GBs_stats_only": round(N * 2 / wall_nograd / 1e9, 2),
                   "mean_L_freq": float(np.mean(st["L_freq"])), "mean_L": float(np.mean(st["L"]))})
+    lines.append(fit_line())
     return lines
+
+
+def fit_line(epochs=25):
+    """Gauge training on synthetic windows and the zfp coordinate-control
+    comparison: 2 layers x K/V x 8 heads, 16 training windows of 4096 tokens
+    (AdamW, one step per window, 25 epochs, g = 16), 4 held-out windows; each
+    condition's spectral concentration and zfp KV NRMSE at 3, 4, 6 b/v."""
+    import torch
+
+    from fixed_rate_compression_amd import fit
+    L, KV, B, H, Tw, W, We = 2, 2, 1, 8, 4096, 16, 4
+    x = _gen(L * KV * B * H, Tw * W, Tw * W, 0.95, 6, 4, True)
+    held = _gen(L * KV * B * H, Tw * We, Tw * We, 0.95, 206, 4, True, scale_seed=6)  # same channel scales
+    tr = fit.GaugeTrainer(x, L, KV, B, H, 16, window=Tw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tr.fit(epochs)
+    t_fit = time.perf_counter() - t0
+    conds = {"identity": None, "learned": tr.gauges(),
+             "hadamard": fit.control_gauges("hadamard", L, KV, H, 16),
+             "dct": fit.control_gauges("dct", L, KV, H, 16),
+             "klt": fit.control_gauges("klt", L, KV, H, 16, moments=fit.second_moments(x, L, KV, B, H, 16))}
+    for k in range(3):
+        conds[f"random{k}"] = fit.control_gauges("random", L, KV, H, 16, seed=300 + k)
+    res = {c: fit.evaluate(held, L, KV, B, H, 16, G) for c, G in conds.items()}
+    out = {"workload": "gauge_fit_controls",
+           "desc": f"{L} layers x K/V x {H} heads, g=16, AdamW {epochs} epochs x {W} windows of {Tw} tokens "
+                   f"(one step per window), evaluated on {We} held-out windows (same channel scales, "
+                   "new token noise)",
+           "steps": tr.t, "fit_s": round(t_fit, 3), "ms_per_step": round(t_fit / tr.t * 1e3, 3),
+           "objective_first_epoch": round(float(np.mean(tr.history[:W])), 6),
+           "objective_last_epoch": round(float(np.mean(tr.history[-W:])), 6),
+           "conditions": {c: {k: round(v, 6) for k, v in r.items()} for c, r in res.items()}}
+    for R in (3, 4, 6):
+        ident = res["identity"][f"zfp{R}_nrmse"]
+        out[f"learned_vs_identity_zfp{R}_nrmse_reduction"] = round(1.0 - res["learned"][f"zfp{R}_nrmse"] / ident, 4)
+    del x, held
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -330,8 +373,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "all"],
-                    help="all: also print one JSON line per other workload after the main line")
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "all", "fit"],
+                    help="all: also print one JSON line per other workload after the main line; "
+                         "fit: only the gauge-training / coordinate-control line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain device copy of the KV tensor (counter calibration)")
     args = ap.parse_args()
@@ -341,6 +385,9 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if args.workload == "fit":
+        print(json.dumps(fit_line()), flush=True)
+        return
     log("setup: generating the synthetic cache on the device")
     s = setup()
     if args.copy_probe:
