@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0
 # reports null once the hash of those sources differs.
 PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "zfp_block.hpp", "zfp_kernels.hpp", "zfp_r4.hip",
                "kernels_zfp.hip")
-PMC_TRAFFIC = {"sha256": "ac9521ce4653113bb6c83ef04f24cd78719ebbc0befc26b2a9a9db5b450d3e02",
-               "k_zfp_encode": 5436088576, "k_zfp_decode": 5436192768}
+PMC_TRAFFIC = {"sha256": "f241c44d88272663bb3d892c6a76a004a1b2c08280b84e72493e7375e56f3ace",
+               "k_zfp_encode": 5436089856, "k_zfp_decode": 5436185664}
 
 CFG = dict(layers=32, kv=2, batch=1, heads=8, tokens=32768, head_dim=128, g=16, rate=4,
            rho=0.95, outliers=4, seed=2)
