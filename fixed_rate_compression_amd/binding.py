@@ -25,7 +25,7 @@ EXPORTED = ["cg_encoded_bytes", "cg_encode", "cg_decode", "cg_roundtrip", "cg_ga
             "cg_stats_workspace_bytes", "cg_gauge_from_skew", "cg_gauge_apply", "cg_write_header",
             "cg_decode_error_workspace_bytes", "cg_decode_error", "cg_cache_error_summary",
             "cg_adamw_update", "cg_gauge_control", "cg_second_moment_workspace_bytes",
-            "cg_second_moment", "cg_last_error"]
+            "cg_second_moment", "cg_gauge_grad", "cg_last_error"]
 
 CG_CONTROL_IDENTITY, CG_CONTROL_HADAMARD, CG_CONTROL_DCT, CG_CONTROL_ORTHONORMALIZE, CG_CONTROL_KLT = range(5)
 
@@ -105,6 +105,7 @@ def lib():
             "cg_gauge_control": [I32, I64, I32, P, P],
             "cg_second_moment_workspace_bytes": [SP, I32, ctypes.POINTER(ctypes.c_size_t)],
             "cg_second_moment": [SP, P, I32, P, ctypes.c_size_t, P, P],
+            "cg_gauge_grad": [I64, I32, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -268,6 +269,17 @@ def cg_gauge_from_skew(A: np.ndarray) -> np.ndarray:
     G = np.empty((n, g, g), np.float32)
     _check("cg_gauge_from_skew", lib().cg_gauge_from_skew(n, g, A.ctypes.data, G.ctypes.data))
     return G
+
+
+def cg_gauge_grad(A: np.ndarray, dG: np.ndarray) -> np.ndarray:
+    """A, dG fp64 [n, g, g] (host) -> dL/dA fp64 [n, g, g] for G = exp(A - A^T)."""
+    A = np.ascontiguousarray(A, np.float64)
+    dG = np.ascontiguousarray(dG, np.float64)
+    n, g, _ = A.shape
+    assert dG.shape == A.shape
+    dA = np.empty_like(A)
+    _check("cg_gauge_grad", lib().cg_gauge_grad(n, g, A.ctypes.data, dG.ctypes.data, dA.ctypes.data))
+    return dA
 
 
 def cg_stats_workspace_bytes(shape, g, T_b):

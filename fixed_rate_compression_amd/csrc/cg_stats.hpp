@@ -7,6 +7,8 @@
 
 namespace cgh {
 bool expm(int n, const double *M, double *E);
+// R = exp(M) (may be NULL) and L = the Frechet derivative of exp at M in direction D
+bool expm_frechet(int n, const double *M, const double *D, double *R, double *L);
 void set_error(const char *msg);
 }  // namespace cgh
 

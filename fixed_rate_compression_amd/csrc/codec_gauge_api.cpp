@@ -252,11 +252,101 @@ bool expm_pade13(int n, const double *M, double *E) {
   return true;
 }
 
+// R = exp(M) and L = L_exp(M, D), the Frechet derivative of exp at M in the
+// direction D, n x n fp64, from one [13/13] Pade evaluation with scaling and
+// squaring (Al-Mohy and Higham 2009, "Computing the Frechet derivative of the
+// matrix exponential": the Pade numerator/denominator parts U, V and their
+// directional derivatives Lu, Lv are built from the same powers of M; then
+// (V - U) R = V + U, (V - U) L = Lu + Lv + (Lu - Lv) R, and each squaring
+// R <- R R takes L <- R L + L R).
+bool expm_frechet_pade13(int n, const double *M, const double *D, double *Rout, double *Lout) {
+  double b[14];
+  b[13] = 1.0;
+  for (int j = 12; j >= 0; j--) b[j] = b[j + 1] * (double)(j + 1) * (double)(26 - j) / (double)(13 - j);
+  const size_t nn = (size_t)n * n;
+  double norm1 = 0.0;
+  for (int j = 0; j < n; j++) {
+    double cs = 0.0;
+    for (int i = 0; i < n; i++) cs += fabs(M[(size_t)i * n + j]);
+    norm1 = cs > norm1 ? cs : norm1;
+  }
+  const double theta13 = 5.371920351148152;
+  int s = 0;
+  if (norm1 > theta13) s = (int)ceil(log2(norm1 / theta13));
+  const double scale = ldexp(1.0, -s);
+  std::vector<double> A(nn), E(nn), A2(nn), A4(nn), A6(nn), M2(nn), M4(nn), M6(nn), T1(nn), T2(nn);
+  for (size_t k = 0; k < nn; k++) {
+    A[k] = M[k] * scale;
+    E[k] = D[k] * scale;
+  }
+  matmul(n, A.data(), A.data(), A2.data());
+  matmul(n, A2.data(), A2.data(), A4.data());
+  matmul(n, A4.data(), A2.data(), A6.data());
+  // M2 = A E + E A, M4 = A2 M2 + M2 A2, M6 = A4 M2 + M4 A2 (derivatives of A2, A4, A6)
+  matmul(n, A.data(), E.data(), M2.data());
+  matmul(n, E.data(), A.data(), T1.data());
+  for (size_t k = 0; k < nn; k++) M2[k] += T1[k];
+  matmul(n, A2.data(), M2.data(), M4.data());
+  matmul(n, M2.data(), A2.data(), T1.data());
+  for (size_t k = 0; k < nn; k++) M4[k] += T1[k];
+  matmul(n, A4.data(), M2.data(), M6.data());
+  matmul(n, M4.data(), A2.data(), T1.data());
+  for (size_t k = 0; k < nn; k++) M6[k] += T1[k];
+  std::vector<double> W1(nn), Z1(nn), W(nn), U(nn), V(nn), Lw(nn), Lu(nn), Lv(nn);
+  // W = A6 W1 + W2 (U = A W); V = A6 Z1 + Z2
+  for (size_t k = 0; k < nn; k++) {
+    W1[k] = b[13] * A6[k] + b[11] * A4[k] + b[9] * A2[k];
+    Z1[k] = b[12] * A6[k] + b[10] * A4[k] + b[8] * A2[k];
+  }
+  matmul(n, A6.data(), W1.data(), W.data());
+  for (size_t k = 0; k < nn; k++) W[k] += b[7] * A6[k] + b[5] * A4[k] + b[3] * A2[k];
+  for (int i = 0; i < n; i++) W[(size_t)i * n + i] += b[1];
+  matmul(n, A.data(), W.data(), U.data());
+  matmul(n, A6.data(), Z1.data(), V.data());
+  for (size_t k = 0; k < nn; k++) V[k] += b[6] * A6[k] + b[4] * A4[k] + b[2] * A2[k];
+  for (int i = 0; i < n; i++) V[(size_t)i * n + i] += b[0];
+  // Lw = A6 Lw1 + M6 W1 + Lw2;  Lu = A Lw + E W;  Lv = A6 Lz1 + M6 Z1 + Lz2
+  for (size_t k = 0; k < nn; k++) T1[k] = b[13] * M6[k] + b[11] * M4[k] + b[9] * M2[k];
+  matmul(n, A6.data(), T1.data(), Lw.data());
+  matmul(n, M6.data(), W1.data(), T2.data());
+  for (size_t k = 0; k < nn; k++) Lw[k] += T2[k] + b[7] * M6[k] + b[5] * M4[k] + b[3] * M2[k];
+  matmul(n, A.data(), Lw.data(), Lu.data());
+  matmul(n, E.data(), W.data(), T2.data());
+  for (size_t k = 0; k < nn; k++) Lu[k] += T2[k];
+  for (size_t k = 0; k < nn; k++) T1[k] = b[12] * M6[k] + b[10] * M4[k] + b[8] * M2[k];
+  matmul(n, A6.data(), T1.data(), Lv.data());
+  matmul(n, M6.data(), Z1.data(), T2.data());
+  for (size_t k = 0; k < nn; k++) Lv[k] += T2[k] + b[6] * M6[k] + b[4] * M4[k] + b[2] * M2[k];
+  std::vector<double> P(nn), R(nn), L(nn);
+  for (size_t k = 0; k < nn; k++) {
+    P[k] = V[k] - U[k];
+    R[k] = V[k] + U[k];
+  }
+  if (!solve(n, P, R)) return false;
+  matmul(n, Lu.data(), R.data(), T1.data());   // (Lu - Lv) R
+  matmul(n, Lv.data(), R.data(), T2.data());
+  for (size_t k = 0; k < nn; k++) L[k] = Lu[k] + Lv[k] + T1[k] - T2[k];
+  if (!solve(n, P, L)) return false;
+  for (int k = 0; k < s; k++) {
+    matmul(n, R.data(), L.data(), T1.data());
+    matmul(n, L.data(), R.data(), T2.data());
+    for (size_t i = 0; i < nn; i++) L[i] = T1[i] + T2[i];
+    matmul(n, R.data(), R.data(), T1.data());
+    R.swap(T1);
+  }
+  if (Rout) memcpy(Rout, R.data(), nn * sizeof(double));
+  memcpy(Lout, L.data(), nn * sizeof(double));
+  return true;
+}
+
 }  // namespace
 
 // exported for the statistics path (cg_stats.cpp)
 namespace cgh {
 bool expm(int n, const double *M, double *E) { return expm_pade13(n, M, E); }
+bool expm_frechet(int n, const double *M, const double *D, double *R, double *L) {
+  return expm_frechet_pade13(n, M, D, R, L);
+}
 void set_error(const char *msg) { g_err = msg; }
 }  // namespace cgh
 

@@ -144,11 +144,13 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
         const float e = u * u;
         se += e;
         sre += rr[nt][i] * e;
-        slog += log1pf(e * a.inv_tau2);
+        // log2(1 + U^2/tau^2) with the hardware log2 (~1 ulp; the argument is
+        // >= 1, so no cancellation near 0 matters for the sum); times ln 2 below
+        slog += __builtin_amdgcn_logf(1.0f + e * a.inv_tau2);
       }
     se = wave_sum(se);
     sre = wave_sum(sre);
-    slog = wave_sum(slog);
+    slog = wave_sum(slog) * 0.693147180559945309f;
     const float Lb = se > 0.f ? sre / se : 0.f;
     if (active) {
       sLb += (double)Lb;
@@ -162,7 +164,8 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const float u = U[nt][i];
-          y[nt][i] = cf * u * (rr[nt][i] - Lb) + a.lam_r_nc * 2.0f * u / (a.tau2 + u * u);
+          // d/dU of (lambda_r / N_c) log(1 + U^2/tau^2), with a ~1-ulp reciprocal
+          y[nt][i] = cf * u * (rr[nt][i] - Lb) + a.lam_r_nc * 2.0f * u * __builtin_amdgcn_rcpf(a.tau2 + u * u);
         }
       // adjoint token DCT: Z = C16^T dU
       f4 Z[8];

@@ -4,8 +4,9 @@
 // tables in fp64 (rounded to fp32 for the device), launches the statistics
 // kernel and its fixed-order reduction, and finishes the gradient:
 // dL/dA = Psi - Psi^T with Psi = L_exp(S^T, Gamma), the Frechet derivative of
-// exp at S^T in the direction Gamma = dL/dG, taken as the upper-right block
-// of exp([[S^T, Gamma], [0, S^T]]) (Van Loan 1978; Higham 2008, Thm 3.6).
+// exp at S^T in the direction Gamma = dL/dG (the upper-right block of
+// exp([[S^T, Gamma], [0, S^T]]), Van Loan 1978; Higham 2008, Thm 3.6),
+// evaluated with exp itself in one Pade pass (Al-Mohy and Higham 2009).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <string.h>
@@ -37,6 +38,15 @@ struct Layout {
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// host worker threads for n independent items: at most 16 and at most n
+unsigned host_threads(int64_t n) {
+  unsigned nth = std::thread::hardware_concurrency();
+  nth = nth == 0 ? 1 : (nth > 16 ? 16 : nth);
+  if (n < 1) return 1;
+  if ((int64_t)nth > n) nth = (unsigned)n;
+  return nth;
+}
 
 Layout layout(const cg_shape *s, int g) {
   Layout L{};
@@ -72,20 +82,10 @@ int validate(const cg_shape *s, int g, int T_b) {
   return CG_OK;
 }
 
-// Psi = upper-right block of exp([[M, E], [0, M]]), n x n blocks
+// Psi = L_exp(M, E), the Frechet derivative of exp at M in the direction E
+// (equal to the upper-right block of exp([[M, E], [0, M]]))
 bool frechet(int n, const double *M, const double *E, double *Psi) {
-  const int m = 2 * n;
-  std::vector<double> big((size_t)m * m, 0.0), ex((size_t)m * m);
-  for (int i = 0; i < n; i++)
-    for (int j = 0; j < n; j++) {
-      big[(size_t)i * m + j] = M[i * n + j];
-      big[(size_t)i * m + n + j] = E[i * n + j];
-      big[(size_t)(n + i) * m + n + j] = M[i * n + j];
-    }
-  if (!cgh::expm(m, big.data(), ex.data())) return false;
-  for (int i = 0; i < n; i++)
-    for (int j = 0; j < n; j++) Psi[i * n + j] = ex[(size_t)i * m + n + j];
-  return true;
+  return cgh::expm_frechet(n, M, E, nullptr, Psi);
 }
 
 }  // namespace
@@ -118,15 +118,25 @@ extern "C" int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t
   // host tables: gauges (fp64 expm -> fp32), DCT matrices, normalized radius
   std::vector<float> Gh(g ? (size_t)ngauge * R * g * g : 0);
   std::vector<double> Sfull;
-  if (g) {
-    std::vector<double> S((size_t)g * g), E((size_t)g * g);
-    for (int64_t q = 0; q < ngauge * R; q++) {
-      const double *A = A_host + (size_t)q * g * g;
-      for (int i = 0; i < g; i++)
-        for (int j = 0; j < g; j++) S[(size_t)i * g + j] = A[(size_t)i * g + j] - A[(size_t)j * g + i];
-      if (!cgh::expm(g, S.data(), E.data())) return fail(CG_E_INTERNAL, "expm failed");
-      for (size_t k = 0; k < (size_t)g * g; k++) Gh[(size_t)q * g * g + k] = (float)E[k];
-    }
+  if (g) {  // G = exp(A - A^T) per group, spread over host threads
+    const int64_t nq = ngauge * R;
+    auto build = [&](int64_t q0, int64_t q1, int *bad) {
+      std::vector<double> S((size_t)g * g), E((size_t)g * g);
+      for (int64_t q = q0; q < q1; q++) {
+        const double *A = A_host + (size_t)q * g * g;
+        for (int i = 0; i < g; i++)
+          for (int j = 0; j < g; j++) S[(size_t)i * g + j] = A[(size_t)i * g + j] - A[(size_t)j * g + i];
+        if (!cgh::expm(g, S.data(), E.data())) { *bad = 1; return; }
+        for (size_t k = 0; k < (size_t)g * g; k++) Gh[(size_t)q * g * g + k] = (float)E[k];
+      }
+    };
+    const unsigned nth = host_threads(nq);
+    std::vector<std::thread> pool;
+    std::vector<int> bad(nth, 0);
+    for (unsigned t = 0; t < nth; t++) pool.emplace_back(build, nq * t / nth, nq * (t + 1) / nth, &bad[t]);
+    for (auto &th : pool) th.join();
+    for (int b : bad)
+      if (b) return fail(CG_E_INTERNAL, "expm failed");
   }
   std::vector<float> C128((size_t)kD * kD), C16(256), rt((size_t)16 * kD);
   const double pi = 3.14159265358979323846;
@@ -216,9 +226,7 @@ extern "C" int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t
       }
     }
   };
-  unsigned nth = std::thread::hardware_concurrency();
-  nth = nth == 0 ? 1 : (nth > 16 ? 16 : nth);
-  if ((int64_t)nth > F) nth = (unsigned)F;
+  const unsigned nth = host_threads(F);
   std::vector<std::thread> pool;
   std::vector<int> bad(nth, 0);
   for (unsigned t = 0; t < nth; t++) {
@@ -230,3 +238,24 @@ extern "C" int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t
     if (b) return fail(CG_E_INTERNAL, "Frechet derivative failed");
   return CG_OK;
 }
+
+/* dL/dA from dL/dG for G = exp(A - A^T), per matrix (host, fp64). */
+extern "C" int cg_gauge_grad(int64_t n, int32_t g, const double *A_host, const double *dG_host,
+                             double *dA_host) {
+  if (n < 0 || g < 1 || (n && (!A_host || !dG_host || !dA_host)))
+    return fail(CG_E_INVAL, "need n >= 0, g >= 1 and non-NULL arrays");
+  const int gg = g * g;
+  std::vector<double> St(gg), Psi(gg);
+  for (int64_t q = 0; q < n; q++) {
+    const double *A = A_host + (size_t)q * gg;
+    for (int i = 0; i < g; i++)
+      for (int j = 0; j < g; j++) St[i * g + j] = A[j * g + i] - A[i * g + j];  // S^T
+    if (!frechet(g, St.data(), dG_host + (size_t)q * gg, Psi.data()))
+      return fail(CG_E_INTERNAL, "Frechet derivative failed");
+    double *out = dA_host + (size_t)q * gg;
+    for (int i = 0; i < g; i++)
+      for (int j = 0; j < g; j++) out[i * g + j] = Psi[i * g + j] - Psi[j * g + i];
+  }
+  return CG_OK;
+}
+

@@ -236,6 +236,17 @@ int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t g, const d
 int cg_stats_workspace_bytes(const cg_shape *shape, int32_t g, int32_t T_b, size_t *bytes);
 
 /*
+ * Chain rule through the gauge parameterization (gauge-training paragraph,
+ * arXiv page): for G = exp(S), S = A - A^T, and a gradient dL/dG,
+ *   dL/dA = Psi - Psi^T,  Psi = L_exp(S^T, dL/dG)
+ * (the Frechet derivative of exp at S^T in the direction dL/dG), evaluated
+ * in fp64 with one [13/13] Pade pass with scaling and squaring.  A_host,
+ * dG_host, dA_host: host fp64 [n][g][g].  cg_gauge_fit_stats applies the
+ * same map to its device-side dL/dG.
+ */
+int cg_gauge_grad(int64_t n, int32_t g, const double *A_host, const double *dG_host, double *dA_host);
+
+/*
  * G = exp(A - A^T) for n matrices of size g x g (gauge parameterization,
  * arXiv page): host fp64 scaling and squaring with a [13/13] Pade
  * approximant, rounded to fp32.  A_host fp64 [n][g][g], G_host fp32
