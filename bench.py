@@ -229,13 +229,10 @@ def _codec_line(name, shape, x, G, g, codec, steps, warmup, esz, desc):
             "decode_hbm_frac": round(alg / td / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def workload_lines(steps, warmup):
-    import torch
-
+def small_lines(steps, warmup):
+    """small cache, fp32: zfp-4 and block-uniform 4-bit (32-token blocks), g = 16"""
     from fixed_rate_compression_amd import binding as cg
-    from fixed_rate_compression_amd.rolling import RollingHistory
     lines = []
-    # small cache, fp32: zfp-4 and block-uniform 4-bit (32-token blocks), g = 16
     L, KV, B, H, T = 1, 2, 1, 2, 4096
     x = _gen(L * KV * B * H, T, T, 0.9, 1, 2, False)
     G, _ = _gauge(L, KV, H, 16, 101)
@@ -244,8 +241,16 @@ def workload_lines(steps, warmup):
                       (cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, 4, 32), "bu4")):
         lines.append(_codec_line(f"small_fp32_{nm}", sh, x, G, 16, codec, steps, warmup, 4,
                                  "1 layer x K/V x 2 heads x 4096 tokens fp32, g=16 (cache-resident)"))
-    del x
-    # Llama-3-8B-class cache at 3 and 6 b/v (4 b/v is the headline line)
+    return lines
+
+
+def llama8b_lines(steps, warmup):
+    """Llama-3-8B-class cache at 3 and 6 b/v (4 b/v is the headline line), and
+    4 b/v with the other gauge groups"""
+    import torch
+
+    from fixed_rate_compression_amd import binding as cg
+    lines = []
     L, KV, B, H, T = 32, 2, 1, 8, 32768
     x = _gen(L * KV * B * H, T, T, 0.95, 2, 4, True)
     G, _ = _gauge(L, KV, H, 16, 102)
@@ -260,7 +265,15 @@ def workload_lines(steps, warmup):
                                  + (" (dense, matrix cores)" if g == 128 else "")))
     del x
     torch.cuda.empty_cache()
-    # full-head gauge (g = 128, MFMA): KIVI-2/4 (group 32, 128-token tail), block-uniform 3-bit
+    return lines
+
+
+def fullhead_lines(steps, warmup):
+    """full-head gauge (g = 128, MFMA): KIVI-2/4 (group 32, 128-token tail), block-uniform 3-bit"""
+    import torch
+
+    from fixed_rate_compression_amd import binding as cg
+    lines = []
     L, KV, B, H, T = 32, 2, 1, 8, 131072
     x = _gen(L * KV * B * H, T, T, 0.95, 3, 4, True)
     G, _ = _gauge(L, KV, H, 128, 103)
@@ -268,11 +281,19 @@ def workload_lines(steps, warmup):
     for codec, nm in ((cg.make_codec(cg.CG_BACKEND_KIVI, 2, 32, 128), "kivi2"),
                       (cg.make_codec(cg.CG_BACKEND_KIVI, 4, 32, 128), "kivi4"),
                       (cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64), "bu3")):
-        lines.append(_codec_line(f"fullhead_{nm}", sh, x, G, 128, codec, max(3, steps // 4), 1, 2,
+        lines.append(_codec_line(f"fullhead_{nm}", sh, x, G, 128, codec, steps, warmup, 2,
                                  "32 layers x K/V x 8 heads x 131072 tokens bf16, dense g=128"))
     del x
     torch.cuda.empty_cache()
-    # rolling history: 64 seq x 28 layers x 4 heads, 8192 -> 8192 + n tokens, g = 32, 4 b/v
+    return lines
+
+
+def rolling_line():
+    """rolling history: 64 seq x 28 layers x 4 heads, 8192 -> 8192 + n tokens, g = 32, 4 b/v"""
+    import torch
+
+    from fixed_rate_compression_amd import binding as cg
+    from fixed_rate_compression_amd.rolling import RollingHistory
     L, KV, B, H, T0, nsteps = 28, 2, 64, 4, 8192, 64
     cap = T0 + 256
     raw = _gen(L * KV * B * H, T0 + nsteps, cap, 0.95, 4, 4, True)
@@ -288,29 +309,45 @@ def workload_lines(steps, warmup):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / nsteps
     Nmean = L * KV * B * H * 128 * (T0 + nsteps / 2)
-    lines.append({"workload": "rolling_g32_zfp4", "desc": "64 seq x 28 layers x 4 heads, history 8192+, "
-                  f"{nsteps} appends (encode each completed 4-token block, decode whole history)",
-                  "ms_per_step": round(ms, 4), "history_values_mean": int(Nmean),
-                  "decode_kv_GBs": round(Nmean * 2 / (ms * 1e-3) / 1e9, 2),
-                  "decode_hbm_frac": round(Nmean * 2.5 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    line = {"workload": "rolling_g32_zfp4", "desc": "64 seq x 28 layers x 4 heads, history 8192+, "
+            f"{nsteps} appends (encode each completed 4-token block, decode whole history)",
+            "ms_per_step": round(ms, 4), "history_values_mean": int(Nmean),
+            "decode_kv_GBs": round(Nmean * 2 / (ms * 1e-3) / 1e9, 2),
+            "decode_hbm_frac": round(Nmean * 2.5 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del raw, rh
     torch.cuda.empty_cache()
-    # 27B-class cache (zfp-3, g = 16) + gauge-fit statistics over 64 x 4096-token windows
+    return line
+
+
+def b27_codec_line(steps, warmup):
+    """27B-class cache, zfp-3, g = 16"""
+    import torch
+
+    from fixed_rate_compression_amd import binding as cg
     L, KV, B, H, T = 46, 2, 1, 16, 65536
-    F = L * KV * B * H
-    x = _gen(F, T, T, 0.95, 5, 4, True)
-    G, A = _gauge(L, KV, H, 16, 105)
+    x = _gen(L * KV * B * H, T, T, 0.95, 5, 4, True)
+    G, _ = _gauge(L, KV, H, 16, 105)
     sh = cg.make_shape(L, KV, B, H, T, T, 128, cg.CG_DTYPE_BF16)
-    lines.append(_codec_line("27b_zfp3", sh, x, G, 16, cg.make_codec(cg.CG_BACKEND_ZFP, 3), steps, warmup, 2,
-                             "46 layers x K/V x 16 heads x 65536 tokens bf16, g=16"))
+    line = _codec_line("27b_zfp3", sh, x, G, 16, cg.make_codec(cg.CG_BACKEND_ZFP, 3), steps, warmup, 2,
+                       "46 layers x K/V x 16 heads x 65536 tokens bf16, g=16")
     del x
     torch.cuda.empty_cache()
+    return line
+
+
+def stats_line():
+    """27B-class gauge-fit statistics over 64 x 4096-token windows of every head"""
+    import torch
+
+    from fixed_rate_compression_amd import binding as cg
+    L, KV, B, H = 46, 2, 1, 16
+    F = L * KV * B * H
+    _, A = _gauge(L, KV, H, 16, 105)
     W, Tw = 64, 4096
     xw = _gen(F, W * Tw, W * Tw, 0.95, 205, 4, True, windows=W)
     shw = cg.make_shape(L, KV, B, H, W * Tw, W * Tw, 128, cg.CG_DTYPE_BF16)
     ws = torch.empty(cg.cg_stats_workspace_bytes(shw, 16, 16), dtype=torch.uint8, device="cuda")
-    for _ in range(1):
-        cg.cg_gauge_fit_stats(shw, xw, 16, A, 16, 0.04, 1.0, 0.02, ws, grad=True)
+    cg.cg_gauge_fit_stats(shw, xw, 16, A, 16, 0.04, 1.0, 0.02, ws, grad=True)
     t0 = time.perf_counter()
     st, dA = cg.cg_gauge_fit_stats(shw, xw, 16, A, 16, 0.04, 1.0, 0.02, ws, grad=True)
     wall = time.perf_counter() - t0
@@ -318,13 +355,38 @@ def workload_lines(steps, warmup):
     cg.cg_gauge_fit_stats(shw, xw, 16, A, 16, 0.04, 1.0, 0.02, ws, grad=False)
     wall_nograd = time.perf_counter() - t1
     N = xw.numel()
-    lines.append({"workload": "27b_stats_windows", "desc": "1472 heads x 64 windows x 4096 tokens bf16, "
-                  "g=16, T_b=16, tau=0.04; statistics + dL/dA (synchronous, includes host Frechet)",
-                  "values": N, "wall_s_with_grad": round(wall, 4), "wall_s_stats_only": round(wall_nograd, 4),
-                  "kv_GBs_with_grad": round(N * 2 / wall / 1e9, 2),
-                  "kv_GBs_stats_only": round(N * 2 / wall_nograd / 1e9, 2),
-                  "mean_L_freq": float(np.mean(st["L_freq"])), "mean_L": float(np.mean(st["L"]))})
-    lines.append(fit_line())
+    line = {"workload": "27b_stats_windows", "desc": "1472 heads x 64 windows x 4096 tokens bf16, "
+            "g=16, T_b=16, tau=0.04; statistics + dL/dA (synchronous, includes the host exp and "
+            "Frechet adjoint)",
+            "values": N, "wall_s_with_grad": round(wall, 4), "wall_s_stats_only": round(wall_nograd, 4),
+            "kv_GBs_with_grad": round(N * 2 / wall / 1e9, 2),
+            "kv_GBs_stats_only": round(N * 2 / wall_nograd / 1e9, 2),
+            "mean_L_freq": float(np.mean(st["L_freq"])), "mean_L": float(np.mean(st["L"]))}
+    del xw
+    torch.cuda.empty_cache()
+    return line
+
+
+WORKLOADS = ("small", "llama8b-rates", "fullhead", "rolling", "27b", "stats", "fit")
+
+
+def workload_lines(names, steps, warmup):
+    lines = []
+    for nm in names:
+        if nm == "small":
+            lines += small_lines(steps, warmup)
+        elif nm == "llama8b-rates":
+            lines += llama8b_lines(steps, warmup)
+        elif nm == "fullhead":
+            lines += fullhead_lines(max(3, steps // 4), 1)
+        elif nm == "rolling":
+            lines.append(rolling_line())
+        elif nm == "27b":
+            lines.append(b27_codec_line(steps, warmup))
+        elif nm == "stats":
+            lines.append(stats_line())
+        elif nm == "fit":
+            lines.append(fit_line())
     return lines
 
 
@@ -373,9 +435,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "all", "fit"],
-                    help="all: also print one JSON line per other workload after the main line; "
-                         "fit: only the gauge-training / coordinate-control line")
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "all"] + list(WORKLOADS),
+                    help="llama8b: the headline line only; all: the headline line, then one JSON "
+                         "line per other workload; any other name: only that workload's lines")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain device copy of the KV tensor (counter calibration)")
     args = ap.parse_args()
@@ -385,8 +447,9 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
-    if args.workload == "fit":
-        print(json.dumps(fit_line()), flush=True)
+    if args.workload in WORKLOADS:
+        for line in workload_lines([args.workload], max(3, args.steps // 2), 1):
+            print(json.dumps(line), flush=True)
         return
     log("setup: generating the synthetic cache on the device")
     s = setup()
@@ -444,7 +507,7 @@ def main():
     if args.workload == "all":
         del s
         torch.cuda.empty_cache()
-        for line in workload_lines(max(3, args.steps // 2), 1):
+        for line in workload_lines(WORKLOADS, max(3, args.steps // 2), 1):
             print(json.dumps(line), flush=True)
 
 

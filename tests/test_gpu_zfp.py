@@ -202,6 +202,36 @@ def test_llama8b_class_full_size_sampled_fields():
         assert np.array_equal(to_host(out[f]), y_ref), f
 
 
+def test_27b_class_full_size_sampled_fields():
+    """The 27B-class codec workload at full size: 46 layers x K/V x 16 KV heads
+    x 65536 tokens, bf16, g = 16, 3 b/v (12.35 G values, 24.7 GB), in one
+    encode and one decode launch.  Sampled fields (layers 0, 23, 45; K and V;
+    heads 0 and 15) bit-exact against the oracle, plus the last field."""
+    import torch
+    L, KV, B, H, T = 46, 2, 1, 16, 65536
+    R, g = 3, 16
+    x = kv_gpu(5, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    G = gauges_for(105, L, KV, H, g)
+    shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16)
+    codec = cg.make_codec(cg.CG_BACKEND_ZFP, R)
+    nbytes = cg.cg_encoded_bytes(shape, codec)[0]
+    assert nbytes == L * KV * H * T * D * R // 8
+    pay = empty_u8(nbytes)
+    out = torch.empty_like(x)
+    gauge = cg.make_gauge(g, to_dev(G))
+    cg.cg_encode(shape, x, gauge, codec, 0, T, pay)
+    cg.cg_decode(shape, pay, None, gauge, codec, 0, T, out)
+    torch.cuda.synchronize()
+    per = T * D * R // 8
+    fields = [(l * KV + s) * H + h for l in (0, 23, 45) for s in (0, 1) for h in (0, 15)]
+    fields.append(n_fields(L, KV, B, H) - 1)
+    for f in sorted(set(fields)):
+        xf = to_host(x[f])
+        p_ref, y_ref = zfp_oracle_field(xf, gauge_of_field(G, f, KV, B, H), g, R, T, T)
+        assert np.array_equal(to_host(pay[f * per:(f + 1) * per]), p_ref), f
+        assert np.array_equal(to_host(out[f]), y_ref), f
+
+
 @pytest.mark.parametrize("R", [3, 4, 8])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_dense_gauge_zfp_staged(R, bf16):
