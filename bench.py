@@ -34,7 +34,9 @@ HBM_PEAK_GBS = 8000.0
 PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "zfp_block.hpp", "zfp_kernels.hpp", "zfp_r4.hip",
                "kernels_zfp.hip")
 PMC_TRAFFIC = {"sha256": "f241c44d88272663bb3d892c6a76a004a1b2c08280b84e72493e7375e56f3ace",
-               "k_zfp_encode": 5436089856, "k_zfp_decode": 5436185664}
+               "k_zfp_encode": 5436089856, "k_zfp_decode": 5436185664,
+               # SQ_INSTS_VALU per launch (rocprofv3 --pmc, same sources)
+               "valu_k_zfp_encode": 2112515480, "valu_k_zfp_decode": 2755951630}
 
 CFG = dict(layers=32, kv=2, batch=1, heads=8, tokens=32768, head_dim=128, g=16, rate=4,
            rho=0.95, outliers=4, seed=2)
@@ -51,6 +53,12 @@ def kernel_sources_sha() -> str:
 
 def measured_traffic(kernel: str):
     return PMC_TRAFFIC.get(kernel) if kernel_sources_sha() == PMC_TRAFFIC["sha256"] else None
+
+
+def valu_rate(kernel: str, seconds: float):
+    """counted VALU wave-instructions per launch and their issue rate (G/s)"""
+    n = measured_traffic("valu_" + kernel)
+    return (n, round(n / seconds / 1e9, 1)) if n else (None, None)
 
 
 def log(msg):
@@ -498,6 +506,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(f"k_zfp_{dom}"),
+                     "valu_instr_per_launch": valu_rate(f"k_zfp_{dom}", t_dom)[0],
+                     "valu_ginstr_per_s": valu_rate(f"k_zfp_{dom}", t_dom)[1],
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline:
