@@ -294,11 +294,13 @@ __host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Ra
   const uint32_t below = E >= 32u ? ~0u : (1u << E) - 1u;
   uint32_t term = W & ~P & below;
   uint32_t y = 0u, bias = 1u;
-  while (term) {                        // one step per newly significant coefficient
-    const uint32_t low = term & (0u - term);
-    y |= low >> bias;
-    term ^= low;
-    bias += 1u;
+  while (term) {                        // two newly significant coefficients per step
+    const uint32_t low1 = term & (0u - term);
+    const uint32_t rest = term ^ low1;
+    const uint32_t low2 = rest & (0u - rest);   // 0 when only one was left
+    y |= (low1 >> bias) | (low2 >> (bias + 1u));
+    term = rest ^ low2;
+    bias += 2u;
   }
   const uint32_t cnt = E - (uint32_t)__builtin_popcount(tests & below);  // bits scanned before E
   uint32_t used;
