@@ -303,16 +303,18 @@ __host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Ra
     bias += 2u;
   }
   const uint32_t cnt = E - (uint32_t)__builtin_popcount(tests & below);  // bits scanned before E
-  uint32_t used;
-  if (cnt > m) {                        // the scan reaches coefficient 15: implicit 1
-    y = (y & ((1u << m) - 1u)) | (1u << m);
-    used = m + (uint32_t)__builtin_popcount(y);
-  } else if (ef < room) {               // failed group test at ef
-    used = ef + 1u;
-  } else {                              // budget ends at room (<= ef <= 32)
-    if ((P >> (room - 1u)) & 1u) y |= 1u << cnt;   // inside a scan: set the scanned index
-    used = room;
-  }
+  // three ways the part ends, selected without branches (lanes diverge here):
+  //  cap    the scan reaches coefficient 15, whose 1 is implicit;
+  //  fail   a failed group test at ef;
+  //  budget the budget ends at room (<= ef <= 32); inside a scan the scanned
+  //         index is set
+  const bool cap = cnt > m;
+  const bool fail = ef < room;
+  const uint32_t ycap = (y & ((1u << m) - 1u)) | (1u << m);
+  const uint32_t inscan = (P >> ((room - 1u) & 31u)) & 1u;
+  const uint32_t ybud = y | (inscan << (cnt & 31u));
+  y = cap ? ycap : (fail ? y : ybud);
+  const uint32_t used = cap ? m + (uint32_t)__builtin_popcount(ycap) : (fail ? ef + 1u : room);
   pos += (int)used;
   n += y ? 32 - clz32(y) : 0;           // every index up to the last new one is now verbatim
   return y;
