@@ -9,6 +9,13 @@ namespace cgk {
 
 constexpr int TILE_T = 64;  // tokens per workgroup tile of the rows kernels
 constexpr int ZFP128_CHUNK = 16;  // tiles per workgroup with the dense (g = 128) gauge
+constexpr int ZFP_CHUNK = 4;      // tiles per workgroup with the VALU gauges, given enough work
+
+// tiles per workgroup of the VALU-gauge zfp kernels: ZFP_CHUNK when the call
+// still gives at least 8192 workgroups (8 per CU-slot), else 1
+inline int zfp_chunk_tiles(int64_t fields, int64_t tiles) {
+  return fields * ((tiles + ZFP_CHUNK - 1) / ZFP_CHUNK) >= 8192 ? ZFP_CHUNK : 1;
+}
 
 // geometry of a rows launch over every field: one workgroup per
 // (field, 64-token tile) of rows [t0, t0 + nt)
@@ -20,7 +27,8 @@ struct TileArgs {
   int32_t tiles;  // tiles per field = ceil(nt / 64)
   int32_t batch;  // B (gauges are shared across the batch)
   int32_t heads;  // H
-  int32_t chunks; // dense gauge: workgroups per field = ceil(tiles / ZFP128_CHUNK)
+  int32_t chunks;       // zfp kernels: workgroups per field = ceil(tiles / chunk_tiles)
+  int32_t chunk_tiles;  // zfp kernels: tiles per workgroup (set by the launcher)
   // decode only: reference rows in the output layout (or null) and the
   // per-workgroup error partials [grid][3] they produce
   const void *ref;

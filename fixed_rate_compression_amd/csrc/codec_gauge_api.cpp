@@ -437,10 +437,13 @@ int cg_encode(const cg_shape *shape, const void *kv, const cg_gauge *gauge, cons
 namespace {
 
 // error partials per field of a decode launch (one per workgroup)
-int64_t err_per_field(const cg_codec *c, int g, int64_t nt) {
+int64_t err_per_field(const cg_shape *s, const cg_codec *c, int g, int64_t nt) {
   const int64_t tiles = (nt + cgk::TILE_T - 1) / cgk::TILE_T;
   if (g == 128) return (tiles + cgk::ZFP128_CHUNK - 1) / cgk::ZFP128_CHUNK;
-  (void)c;
+  if (c->backend == CG_BACKEND_ZFP) {
+    const int ct = cgk::zfp_chunk_tiles(n_fields(s), tiles);
+    return (tiles + ct - 1) / ct;
+  }
   return tiles;
 }
 
@@ -508,7 +511,7 @@ int cg_decode_error_workspace_bytes(const cg_shape *shape, const cg_gauge *gauge
   if ((rc = check_codec(codec, shape))) return rc;
   if ((rc = check_gauge(gauge, shape, codec))) return rc;
   if ((rc = check_rows(shape, codec, t0, nt))) return rc;
-  *bytes = (size_t)n_fields(shape) * (size_t)err_per_field(codec, gauge->group, nt) * 3 * sizeof(double);
+  *bytes = (size_t)n_fields(shape) * (size_t)err_per_field(shape, codec, gauge->group, nt) * 3 * sizeof(double);
   return CG_OK;
 }
 
@@ -533,7 +536,7 @@ int cg_decode_error(const cg_shape *shape, const void *payload, uint64_t payload
   rc = decode_impl(shape, payload, payload_cap, meta, meta_cap, gauge, codec, t0, nt, kv_out, kv_ref,
                    epart, stream);
   if (rc) return rc;
-  hipError_t e = cgk::error_reduce_launch(epart, n_fields(shape), err_per_field(codec, gauge->group, nt),
+  hipError_t e = cgk::error_reduce_launch(epart, n_fields(shape), err_per_field(shape, codec, gauge->group, nt),
                                           (double)nt * shape->head_dim, (double *)err, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "cg_decode_error reduce");
   return CG_OK;

@@ -114,6 +114,21 @@ struct TileFetch {
     }
   }
 
+  // -> the fp32 LDS tile (pitch PITCH floats), bf16 widened exactly
+  __device__ __forceinline__ void put_f32(float *xs) const {
+#pragma unroll
+    for (int k = 0; k < N; k++) {
+      const int i = threadIdx.x + NT * k;
+      if (BF16) {
+        float *d = xs + (i >> 4) * PITCH + 8 * (i & 15);
+        *(float4 *)d = make_float4(bf16lo(r[k].x), bf16hi(r[k].x), bf16lo(r[k].y), bf16hi(r[k].y));
+        *(float4 *)(d + 4) = make_float4(bf16lo(r[k].z), bf16hi(r[k].z), bf16lo(r[k].w), bf16hi(r[k].w));
+      } else {
+        *(uint4 *)(xs + (i >> 5) * PITCH + 4 * (i & 31)) = r[k];
+      }
+    }
+  }
+
   // -> split tiles (bf16 inputs are their own hi part; lo is not used)
   __device__ __forceinline__ void put(uint16_t *sh, uint16_t *sl) const {
 #pragma unroll

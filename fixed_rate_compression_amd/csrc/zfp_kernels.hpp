@@ -56,6 +56,9 @@ __device__ __forceinline__ void unstage_block(const uint32_t *os, int b, uint64_
   }
 }
 
+// VALU gauges (g <= 32): a workgroup walks a.chunk_tiles consecutive tiles of
+// one field and loads tile i+1 (KV rows, or code words) into registers while
+// it codes tile i.
 template <int R, bool BF16, int G>
 __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
                                                    const float *__restrict__ gauges,
@@ -63,37 +66,67 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
   __shared__ float xs[TILE_T * PITCH];
   __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
   __shared__ uint16_t dbl[256];
-  const int64_t field = (int64_t)blockIdx.x / a.tiles;
-  const int tile = (int)((int64_t)blockIdx.x % a.tiles);
-  const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
-  const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
-  const int64_t row0 = field * a.tcap + tb;
+  const int64_t field = (int64_t)blockIdx.x / a.chunks;
+  const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * a.chunk_tiles;
+  const int tend = min(a.tiles, tile0 + a.chunk_tiles);
   const size_t esz = BF16 ? 2 : 4;
+  const float *Gf = G ? gauges + gauge_index(field, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   dbl[threadIdx.x] = cgz::dbl8_entry(threadIdx.x);
-  load_tile<BF16>((const uint8_t *)kv + (size_t)row0 * D * esz, nrows, xs);
-  __syncthreads();
-  if constexpr (G != 0) {
-    gauge_tile<G, false>(xs, nrows, gauges + gauge_index(field, a.batch, a.heads) * D * G);
+  const uint8_t *src_f = (const uint8_t *)kv + (size_t)field * a.tcap * D * esz;
+  auto rows = [&](int tile) { return (int)min((int64_t)TILE_T, a.nt - (int64_t)tile * TILE_T); };
+  TileFetch<BF16> pre;
+  if (tile0 < tend) pre.fetch(src_f + (size_t)(a.t0 + (int64_t)tile0 * TILE_T) * D * esz, rows(tile0));
+  for (int tile = tile0; tile < tend; tile++) {
+    const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
+    const int nrows = rows(tile);
+    pre.put_f32(xs);
     __syncthreads();
-  }
-  const int nblk = (nrows / 4) * 32;
-  for (int b = threadIdx.x; b < nblk; b += NT) {
-    const float *src = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
-    float v[16];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const float4 t = *(const float4 *)(src + j * PITCH);
-      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    if (tile + 1 < tend) pre.fetch(src_f + (size_t)(tb + TILE_T) * D * esz, rows(tile + 1));
+    if constexpr (G != 0) {
+      gauge_tile<G, false>(xs, nrows, Gf);
+      __syncthreads();
     }
-    uint64_t acc[cgz::Rate<R>::kAcc];
-    cgz::encode_block<R>(v, acc, dbl);
-    stage_block<R>(os, b, acc);
+    const int nblk = (nrows / 4) * 32;
+    for (int b = threadIdx.x; b < nblk; b += NT) {
+      const float *src = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float4 t = *(const float4 *)(src + j * PITCH);
+        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+      }
+      uint64_t acc[cgz::Rate<R>::kAcc];
+      cgz::encode_block<R>(v, acc, dbl);
+      stage_block<R>(os, b, acc);
+    }
+    __syncthreads();  // codes staged; every thread is done with xs
+    uint4 *dst = (uint4 *)(payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R);
+    const int n16 = nblk * 2 * R / 16;
+    for (int i = threadIdx.x; i < n16; i += NT) dst[i] = ((const uint4 *)os)[i];
   }
-  __syncthreads();
-  uint4 *dst = (uint4 *)(payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R);
-  const int n16 = nblk * 2 * R / 16;
-  for (int i = threadIdx.x; i < n16; i += NT) dst[i] = ((const uint4 *)os)[i];
 }
+
+// the code words of one tile held in registers between their global load
+// and their LDS store (16-B pieces i, i + NT, ...)
+template <int R>
+struct CodeFetch {
+  static constexpr int NC = (TILE_T / 4 * 32 * 2 * R / 16 + NT - 1) / NT;
+  uint4 r[NC];
+  __device__ __forceinline__ void fetch(const uint4 *__restrict__ src, int n16) {
+#pragma unroll
+    for (int k = 0; k < NC; k++) {
+      const int i = threadIdx.x + NT * k;
+      if (i < n16) r[k] = src[i];
+    }
+  }
+  __device__ __forceinline__ void put(uint32_t *os, int n16) const {
+#pragma unroll
+    for (int k = 0; k < NC; k++) {
+      const int i = threadIdx.x + NT * k;
+      if (i < n16) ((uint4 *)os)[i] = r[k];
+    }
+  }
+};
 
 template <int R, bool BF16, int G>
 __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ payload,
@@ -101,40 +134,49 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
                                                    void *__restrict__ out, TileArgs a) {
   __shared__ float xs[TILE_T * PITCH];
   __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
-  const int64_t field = (int64_t)blockIdx.x / a.tiles;
-  const int tile = (int)((int64_t)blockIdx.x % a.tiles);
-  const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
-  const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);
-  const int64_t row0 = field * a.tcap + tb;
-  const int nblk = (nrows / 4) * 32;
-  const uint4 *src = (const uint4 *)(payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R);
-  const int n16 = nblk * 2 * R / 16;
-  for (int i = threadIdx.x; i < n16; i += NT) ((uint4 *)os)[i] = src[i];
-  __syncthreads();
-  for (int b = threadIdx.x; b < nblk; b += NT) {
-    uint64_t acc[cgz::Rate<R>::kAcc];
-    unstage_block<R>(os, b, acc);
-    float v[16];
-    cgz::decode_block<R>(acc, v);
-    float *dst = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-      *(float4 *)(dst + j * PITCH) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-  }
-  __syncthreads();
-  if constexpr (G != 0) {
-    gauge_tile<G, true>(xs, nrows, gauges + gauge_index(field, a.batch, a.heads) * D * G);
-    __syncthreads();
-  }
+  const int64_t field = (int64_t)blockIdx.x / a.chunks;
+  const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * a.chunk_tiles;
+  const int tend = min(a.tiles, tile0 + a.chunk_tiles);
   const size_t esz = BF16 ? 2 : 4;
-  if (a.ref) {
-    ErrAcc e;
-    store_tile_err<BF16>((uint8_t *)out + (size_t)row0 * D * esz, nrows, xs,
-                         (const uint8_t *)a.ref + (size_t)row0 * D * esz, e);
-    write_err(e, a.epart);
-  } else {
-    store_tile<BF16>((uint8_t *)out + (size_t)row0 * D * esz, nrows, xs);
+  const float *Gf = G ? gauges + gauge_index(field, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
+  auto rows = [&](int tile) { return (int)min((int64_t)TILE_T, a.nt - (int64_t)tile * TILE_T); };
+  auto codes = [&](int tile) {
+    return (const uint4 *)(payload + (size_t)(field * (a.tcap / 4) + (a.t0 + (int64_t)tile * TILE_T) / 4) * 32 * 2 * R);
+  };
+  auto n16 = [&](int tile) { return (rows(tile) / 4) * 32 * 2 * R / 16; };
+  CodeFetch<R> pre;
+  if (tile0 < tend) pre.fetch(codes(tile0), n16(tile0));
+  ErrAcc err;
+  for (int tile = tile0; tile < tend; tile++) {
+    const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
+    const int nrows = rows(tile);
+    const int nblk = (nrows / 4) * 32;
+    pre.put(os, n16(tile));
+    __syncthreads();
+    if (tile + 1 < tend) pre.fetch(codes(tile + 1), n16(tile + 1));
+    for (int b = threadIdx.x; b < nblk; b += NT) {
+      uint64_t acc[cgz::Rate<R>::kAcc];
+      unstage_block<R>(os, b, acc);
+      float v[16];
+      cgz::decode_block<R>(acc, v);
+      float *dst = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        *(float4 *)(dst + j * PITCH) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+    }
+    __syncthreads();
+    if constexpr (G != 0) {
+      gauge_tile<G, true>(xs, nrows, Gf);
+      __syncthreads();
+    }
+    const size_t off = (size_t)(field * a.tcap + tb) * D * esz;
+    if (a.ref)
+      store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
+    else
+      store_tile<BF16>((uint8_t *)out + off, nrows, xs);
+    __syncthreads();  // xs and os are rewritten by the next tile
   }
+  if (a.ref) write_err(err, a.epart);
 }
 
 // Dense (g = 128) gauge on the matrix cores (gauge128.hpp): a workgroup walks
@@ -265,15 +307,20 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
 template <int R>
 hipError_t zfp_launch_rate(bool encode, bool bf16, int g, const void *src, const float *gauges,
                            void *dst, const TileArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)a.grid), block(NT);
+  const dim3 block(NT);
+  const int64_t fields = a.grid / a.tiles;
+  TileArgs v = a;
+  v.chunk_tiles = zfp_chunk_tiles(fields, a.tiles);
+  v.chunks = (a.tiles + v.chunk_tiles - 1) / v.chunk_tiles;
+  const dim3 grid((unsigned)(fields * v.chunks));
 #define CG_L(BF, GG)                                                                             \
   if (bf16 == BF && g == GG) {                                                                   \
     if (encode)                                                                                  \
       hipLaunchKernelGGL((k_zfp_encode<R, BF, GG>), grid, block, 0, s, src, gauges,             \
-                         (uint8_t *)dst, a);                                                     \
+                         (uint8_t *)dst, v);                                                     \
     else                                                                                         \
       hipLaunchKernelGGL((k_zfp_decode<R, BF, GG>), grid, block, 0, s, (const uint8_t *)src,    \
-                         gauges, dst, a);                                                        \
+                         gauges, dst, v);                                                        \
     return hipGetLastError();                                                                    \
   }
   CG_L(true, 0) CG_L(true, 8) CG_L(true, 16) CG_L(true, 32)
@@ -281,8 +328,8 @@ hipError_t zfp_launch_rate(bool encode, bool bf16, int g, const void *src, const
 #undef CG_L
   if (g == 128) {
     TileArgs c = a;
-    const int64_t fields = a.grid / a.tiles;
     c.chunks = (a.tiles + ZFP128_CHUNK - 1) / ZFP128_CHUNK;
+    c.chunk_tiles = ZFP128_CHUNK;
     const dim3 grid128((unsigned)(fields * c.chunks));
 #define CG_L128(BF)                                                                              \
   if (bf16 == BF) {                                                                              \
