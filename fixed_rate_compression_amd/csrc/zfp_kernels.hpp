@@ -3,14 +3,16 @@
 // tensor is zfp-encoded at a fixed rate as a 2D field with n_x = d_l, decoded,
 // and the inverse gauge restores the cache before attention).
 //
-// One workgroup (256 threads) owns a tile of 64 tokens x 128 channels of one
-// field: 16 block rows x 32 blocks = 512 blocks, whose 16R-bit codes are one
-// contiguous 1024R-byte span of the stream.
+// A tile is 64 tokens x 128 channels of one field: 16 block rows x 32 blocks =
+// 512 blocks, whose 16R-bit codes are one contiguous 1024R-byte span of the
+// stream.  A workgroup (256 threads) walks a chunk of consecutive tiles of one
+// field, loading tile i+1 into registers while it works on tile i:
 //   encode: coalesced tile load -> LDS (fp32) -> gauge in place (lane = token,
-//           wave-uniform group, SGPR matrix) -> one block per thread-iteration
-//           (zfp_block.hpp, all in VGPRs) -> codes staged in LDS -> coalesced
-//           16-byte stores of the span.
-//   decode: the mirror image.
+//           wave-uniform group, SGPR matrix; or the MFMA routine for g = 128)
+//           -> one block per thread-iteration (zfp_block.hpp, all in VGPRs)
+//           -> codes staged in LDS -> coalesced 16-byte stores of the span.
+//   decode: the mirror image; with a reference pointer the store also
+//           accumulates the cache-side error sums.
 // Stream layout: field f, block (bx, by) (bx = channel block, fastest) sits at
 // bits [((f * Tcap/4 + by) * 32 + bx) * 16R, +16R), stream bit p = bit p%8 of
 // byte p/8 -- the pages' whole-tensor 2D field with the fields in order,
