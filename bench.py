@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # reports null once the hash of those sources differs.
 PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "zfp_block.hpp", "zfp_kernels.hpp", "zfp_r4.hip",
                "kernels_zfp.hip")
-PMC_TRAFFIC = {"sha256": "a27088a9bc3a67c1f450faeb68a88c4517a7f4506973a64618067e38738aa20e",
+PMC_TRAFFIC = {"sha256": "454b58ee71a2426f815c803ad0b626b5b791ffd759d6217c65436c9e92199343",
                "k_zfp_encode": 5442109850, "k_zfp_decode": 5438379930,
                # SQ_INSTS_VALU per launch (rocprofv3 --pmc, same sources)
                "valu_k_zfp_encode": 2043571608, "valu_k_zfp_decode": 2732200968}
