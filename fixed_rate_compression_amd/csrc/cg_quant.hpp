@@ -21,6 +21,15 @@ struct QuantArgs {
   double *epart;     // decode: per-workgroup error partials [grid][3]
 };
 
+// tiles per workgroup: the dense gauge walks 16 tiles (1024 tokens) so each
+// workgroup turns its 64 KB gauge into fragments once; the others walk 4 when
+// the call still gives at least 8192 workgroups, else 1.  Every workgroup
+// fetches tile i+1 while it works on tile i.
+inline int quant_chunk_tiles(int g, int64_t fields, int64_t ntiles) {
+  if (g == 128) return 16;
+  return fields * ((ntiles + 3) / 4) >= 8192 ? 4 : 1;
+}
+
 bool bits_built(int bits);
 bool bu_block_built(int bt);
 

@@ -444,6 +444,10 @@ int64_t err_per_field(const cg_shape *s, const cg_codec *c, int g, int64_t nt) {
     const int ct = cgk::zfp_chunk_tiles(n_fields(s), tiles);
     return (tiles + ct - 1) / ct;
   }
+  if (c->backend == CG_BACKEND_BLOCK_UNIFORM || c->backend == CG_BACKEND_KIVI) {
+    const int ct = cgq::quant_chunk_tiles(g, n_fields(s), tiles);
+    return (tiles + ct - 1) / ct;
+  }
   return tiles;
 }
 

@@ -8,7 +8,7 @@ hipError_t gauge128_rows_launch(bool bf16, bool inverse, const void *kv, const f
                                 float *out, int64_t tcap, int64_t tokens, int64_t fields, int batch,
                                 int heads, hipStream_t s) {
   QuantArgs q = make_args(tcap, tokens, 0, tokens, fields, batch, heads, 0, 0, 0, 0, 1);
-  const QK a = make_qk(q, tiles_per_chunk(128));
+  const QK a = make_qk(q, quant_chunk_tiles(128, fields, (tokens + TILE_T - 1) / TILE_T));
   const dim3 grid((unsigned)(fields * a.chunks)), block(NT);
   if (bf16) {
     if (inverse) hipLaunchKernelGGL((k_gauge128_rows<true, true>), grid, block, 0, s, kv, gauges, out, a);

@@ -161,17 +161,17 @@ __device__ __forceinline__ void write32(float *xs, int t, int j, const float (&v
   for (int k = 0; k < 32; k += 4) *(float4 *)(d + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
 }
 
-// Forward-gauged tiles of one workgroup's chunk.  next() loads the tile at
-// token tb (rows [0, nrows)) and applies the forward gauge; the fp32 result is
-// in the tile view of `lds` (PITCH floats per row; rows past nrows are zero
-// for the dense gauge).  With the dense gauge the global loads of the
-// following tile (prefetch()) are in flight during the matrix work.
+// Forward-gauged tiles of one workgroup's chunk.  next() stores the fetched
+// tile (rows [0, nrows); rows past nrows are zero) and applies the forward
+// gauge; the fp32 result is in the tile view of `lds` (PITCH floats per row).
+// The global loads of the following tile are issued before the gauge, so
+// they are in flight during the gauge and the quantizer work.
 template <int G, bool BF16>
 struct GaugedTiles {
   TileFetch<BF16> pre;
 
   __device__ __forceinline__ void prefetch(const void *__restrict__ src, int nrows) {
-    if constexpr (G == 128) pre.fetch(src, nrows);
+    pre.fetch(src, nrows);
   }
 
   // next_src/next_rows: the tile after this one (next_rows = 0: none)
@@ -186,8 +186,10 @@ struct GaugedTiles {
       if (next_rows > 0) pre.fetch(next_src, next_rows);
       gauge128_tile<BF16>(sh, sl, xs, fr);
     } else {
-      load_tile<BF16>(src, nrows, xs);
+      (void)src;
+      pre.put_f32(xs);
       __syncthreads();
+      if (next_rows > 0) pre.fetch(next_src, next_rows);
       if constexpr (G != 0) {
         gauge_tile<G, false>(xs, nrows, Gf);
         __syncthreads();

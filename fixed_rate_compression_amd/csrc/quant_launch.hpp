@@ -11,8 +11,8 @@ inline QK make_qk(const QuantArgs &q, int tiles_per_chunk) {
   a.tokens = q.tokens;
   a.t0 = q.t0;
   a.nt = q.nt;
-  a.tiles_per_chunk = tiles_per_chunk;
   const int64_t ntiles = (q.nt + TILE_T - 1) / TILE_T;
+  a.tiles_per_chunk = tiles_per_chunk;
   a.chunks = (ntiles + tiles_per_chunk - 1) / tiles_per_chunk;
   a.batch = q.batch;
   a.heads = q.heads;
@@ -24,15 +24,13 @@ inline QK make_qk(const QuantArgs &q, int tiles_per_chunk) {
   return a;
 }
 
-// workgroups with the dense gauge walk 16 tiles (1024 tokens) so each loads
-// its 64 KB gauge once; the others take one tile each
-inline int tiles_per_chunk(int g) { return g == 128 ? 16 : 1; }
+
 
 template <int BITS>
 hipError_t quant_launch_bits(bool encode, bool bf16, int g, int backend, const void *src,
                              const float *gauges, void *dst, const void *meta_in, float *meta_out,
                              const QuantArgs &q, hipStream_t s) {
-  const QK a = make_qk(q, tiles_per_chunk(g));
+  const QK a = make_qk(q, quant_chunk_tiles(g, q.fields, (q.nt + TILE_T - 1) / TILE_T));
   const dim3 grid((unsigned)(q.fields * a.chunks)), block(NT);
   const bool bu = backend == 2;
 #define CG_Q(BF, GG)                                                                                 \
