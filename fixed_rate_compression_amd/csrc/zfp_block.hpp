@@ -94,9 +94,23 @@ __host__ __device__ __forceinline__ void swap_stage(uint32_t &a, uint32_t &b, in
   b = nb;
 }
 
+// the 8-bit stage of swap_stage: a' = (a0, b0, a2, b2), b' = (a1, b1, a3, b3)
+// (bytes from least significant); one byte permute per output on the GPU
+__host__ __device__ __forceinline__ void swap_bytes(uint32_t &a, uint32_t &b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t na = __builtin_amdgcn_perm(a, b, 0x02060004u);
+  const uint32_t nb = __builtin_amdgcn_perm(a, b, 0x03070105u);
+#else
+  const uint32_t na = (a & 0x00FF00FFu) | ((b << 8) & 0xFF00FF00u);
+  const uint32_t nb = ((a >> 8) & 0x00FF00FFu) | (b & 0xFF00FF00u);
+#endif
+  a = na;
+  b = nb;
+}
+
 __host__ __device__ __forceinline__ void transpose16x2(uint32_t (&w)[16]) {
 #pragma unroll
-  for (int i = 0; i < 8; i++) swap_stage(w[i], w[i + 8], 8, 0x00FF00FFu);
+  for (int i = 0; i < 8; i++) swap_bytes(w[i], w[i + 8]);
 #pragma unroll
   for (int i = 0; i < 16; i++)
     if (!(i & 4)) swap_stage(w[i], w[i + 4], 4, 0x0F0F0F0Fu);
