@@ -245,27 +245,53 @@ def zfp_field_bytes(T: int, d: int, R: int) -> int:
     return T * d * R // 8
 
 
+def zfp_pad_rows(x: np.ndarray, end: int) -> np.ndarray:
+    """Rows [0, end) of x with a partial last 4-row block row completed by
+    repeating row end-1 (the reading used for fields whose token count is
+    not a multiple of 4; the page does not say how partial blocks are
+    filled)."""
+    e4 = (end + 3) // 4 * 4
+    xp = np.zeros((e4, x.shape[1]), np.float32)
+    xp[:end] = x[:end]
+    xp[end:e4] = x[end - 1]
+    return xp
+
+
 def zfp_encode_field(x: np.ndarray, R: int, t0: int = 0, nt: int | None = None,
-                     out: np.ndarray | None = None) -> np.ndarray:
-    """x [T, d] fp32 (already gauged) -> payload bytes [T*d*R/8]."""
+                     out: np.ndarray | None = None, T_payload: int | None = None) -> np.ndarray:
+    """x [T, d] fp32 (already gauged) -> payload bytes [T_payload*d*R/8]
+    (T_payload: the field's row capacity, a multiple of 4; default T).
+    Rows [t0, t0+nt) are encoded; t0 is a multiple of 4, and when t0+nt is
+    not, the last block row is padded (zfp_pad_rows)."""
     x = _f32(x)
     T, d = x.shape
-    assert T % 4 == 0 and d % 4 == 0
     if nt is None:
         nt = T - t0
+    Tp = T if T_payload is None else T_payload
+    assert Tp % 4 == 0 and d % 4 == 0 and t0 % 4 == 0
+    if (t0 + nt) % 4:
+        x = zfp_pad_rows(x, t0 + nt)
+        nt = x.shape[0] - t0
+    assert x.shape[0] % 4 == 0 and t0 + nt <= Tp
     if out is None:
-        out = np.zeros(zfp_field_bytes(T, d, R), np.uint8)
+        out = np.zeros(zfp_field_bytes(Tp, d, R), np.uint8)
     lib().oracle_zfp_encode_field(t0, nt, d, R, _p(x), _p(out))
     return out
 
 
 def zfp_decode_field(payload: np.ndarray, T: int, d: int, R: int, t0: int = 0,
                      nt: int | None = None) -> np.ndarray:
+    """payload of a field of T rows (T a multiple of 4) -> [T, d] with rows
+    [t0, t0+nt) decoded (whole block rows are decoded; rows past t0+nt of a
+    partial last block row are left zero)."""
     payload = np.ascontiguousarray(payload, dtype=np.uint8)
     if nt is None:
         nt = T - t0
+    assert T % 4 == 0 and t0 % 4 == 0
+    n4 = (nt + 3) // 4 * 4
     x = np.zeros((T, d), np.float32)
-    lib().oracle_zfp_decode_field(t0, nt, d, R, _p(payload), _p(x))
+    lib().oracle_zfp_decode_field(t0, n4, d, R, _p(payload), _p(x))
+    x[t0 + nt:t0 + n4] = 0.0
     return x
 
 

@@ -81,10 +81,8 @@ def zfp_oracle_field(field, Gf, g, R, T, Tcap):
     rest left zero) and its decoded rows in the storage format."""
     x = oracle.to_f32(field[:T])
     xg = oracle.gauge_forward(x, Gf, g)
-    full = np.zeros((Tcap, D), np.float32)
-    full[:T] = xg
     payload = np.zeros(Tcap * D * R // 8, np.uint8)
-    oracle.zfp_encode_field(full, R, t0=0, nt=T, out=payload)
+    oracle.zfp_encode_field(xg, R, t0=0, nt=T, out=payload, T_payload=Tcap)
     yg = oracle.zfp_decode_field(payload, Tcap, D, R, t0=0, nt=T)[:T]
     y = oracle.gauge_inverse(yg, Gf, g)
     return payload, oracle.from_f32(y, field.dtype)

@@ -211,3 +211,37 @@ def test_bytes_independent_of_gauge():
     p0 = oracle.zfp_encode_field(oracle.gauge_forward(x, None, 0), 4)
     p1 = oracle.zfp_encode_field(oracle.gauge_forward(x, G, 16), 4)
     assert p0.size == p1.size == 64 * 128 * 4 // 8
+
+
+@pytest.mark.parametrize("T", [1, 5, 6, 7, 130])
+def test_partial_block_row_constant_field_is_exact(T):
+    # padding repeats the last token row: a constant field stays constant in
+    # every padded block, and constants decode exactly for R >= 4
+    for R in (4, 8):
+        x = np.full((T, 16), -2.75, np.float32)
+        Tp = (T + 3) // 4 * 4
+        p = oracle.zfp_encode_field(x, R, t0=0, nt=T, T_payload=Tp)
+        y = oracle.zfp_decode_field(p, Tp, 16, R, t0=0, nt=T)
+        assert np.array_equal(y[:T], x)
+        assert np.all(y[T:] == 0.0)
+
+
+def test_partial_block_row_equals_data_that_already_repeats():
+    # when the rows after the valid ones already repeat the last valid row,
+    # the padded encode of [0, T) is the plain encode of [0, ceil4(T))
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((12, 32)).astype(np.float32)
+    x[9:12] = x[8]
+    p_part = oracle.zfp_encode_field(x[:9], 4, t0=0, nt=9, T_payload=12)
+    p_full = oracle.zfp_encode_field(x, 4)
+    assert np.array_equal(p_part, p_full)
+
+
+def test_partial_block_row_is_overwritten_by_the_completed_row():
+    # rolling growth: encode [0, 6) (padded), then re-encode block row [4, 8)
+    # once rows 6, 7 exist: equal to encoding [0, 8) in one shot
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((8, 32)).astype(np.float32)
+    p = oracle.zfp_encode_field(x[:6], 3, t0=0, nt=6, T_payload=8)
+    oracle.zfp_encode_field(x, 3, t0=4, nt=4, out=p)
+    assert np.array_equal(p, oracle.zfp_encode_field(x, 3))
