@@ -318,7 +318,7 @@ def rolling_line():
     ms = a.elapsed_time(b) / nsteps
     Nmean = L * KV * B * H * 128 * (T0 + nsteps / 2)
     line = {"workload": "rolling_g32_zfp4", "desc": "64 seq x 28 layers x 4 heads, history 8192+, "
-            f"{nsteps} appends (encode each completed 4-token block, decode whole history)",
+            f"{nsteps} appends (every token: re-encode its block row, partial rows padded; decode whole history)",
             "ms_per_step": round(ms, 4), "history_values_mean": int(Nmean),
             "decode_kv_GBs": round(Nmean * 2 / (ms * 1e-3) / 1e9, 2),
             "decode_hbm_frac": round(Nmean * 2.5 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -142,8 +142,10 @@ int check_rows(const cg_shape *s, const cg_codec *c, int64_t t0, int64_t nt) {
   if (t0 < 0 || nt < 0 || t0 + nt > s->tokens)
     return fail(CG_E_SHAPE, "rows [%lld, %lld) outside [0, tokens=%lld)", (long long)t0,
                 (long long)(t0 + nt), (long long)s->tokens);
-  if (c->backend == CG_BACKEND_ZFP && ((t0 | nt) % 4))
-    return fail(CG_E_SHAPE, "zfp rows must start and end on multiples of 4");
+  // zfp: 4-token block rows; a partial last block row only where the valid
+  // tokens end (it is padded by repeating the last token)
+  if (c->backend == CG_BACKEND_ZFP && (t0 % 4 || (nt % 4 && t0 + nt != s->tokens)))
+    return fail(CG_E_SHAPE, "zfp rows must start on a multiple of 4 and end on one or at tokens");
   if (c->backend == CG_BACKEND_BLOCK_UNIFORM && ((t0 % c->block_tokens) || (nt % c->block_tokens)))
     return fail(CG_E_SHAPE, "block-uniform rows must be multiples of block_tokens");
   if (c->backend == CG_BACKEND_KIVI && (t0 != 0 || nt != s->tokens))

@@ -61,6 +61,17 @@ __device__ __forceinline__ void unstage_block(const uint32_t *os, int b, uint64_
 // VALU gauges (g <= 32): a workgroup walks a.chunk_tiles consecutive tiles of
 // one field and loads tile i+1 (KV rows, or code words) into registers while
 // it codes tile i.
+// A partial last block row (nrows % 4 != 0, only at the end of a field's
+// valid tokens) is completed by repeating the tile's last valid row.  The
+// gauge acts on each row alone, so padding the gauged rows equals padding
+// the inputs.  The decoder stores the valid rows only.
+__device__ __forceinline__ void pad_block_row(float *xs, int nrows) {
+  const int pad = (4 - (nrows & 3)) & 3;
+  for (int i = threadIdx.x; i < pad * 32; i += NT)
+    *(float4 *)(xs + (nrows + (i >> 5)) * PITCH + (i & 31) * 4) =
+        *(const float4 *)(xs + (nrows - 1) * PITCH + (i & 31) * 4);
+}
+
 template <int R, bool BF16, int G>
 __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
                                                    const float *__restrict__ gauges,
@@ -88,7 +99,11 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
       gauge_tile<G, false>(xs, nrows, Gf);
       __syncthreads();
     }
-    const int nblk = (nrows / 4) * 32;
+    if (nrows & 3) {
+      pad_block_row(xs, nrows);
+      __syncthreads();
+    }
+    const int nblk = ((nrows + 3) / 4) * 32;
     for (int b = threadIdx.x; b < nblk; b += NT) {
       const float *src = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
       float v[16];
@@ -145,14 +160,14 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
   auto codes = [&](int tile) {
     return (const uint4 *)(payload + (size_t)(field * (a.tcap / 4) + (a.t0 + (int64_t)tile * TILE_T) / 4) * 32 * 2 * R);
   };
-  auto n16 = [&](int tile) { return (rows(tile) / 4) * 32 * 2 * R / 16; };
+  auto n16 = [&](int tile) { return ((rows(tile) + 3) / 4) * 32 * 2 * R / 16; };
   CodeFetch<R> pre;
   if (tile0 < tend) pre.fetch(codes(tile0), n16(tile0));
   ErrAcc err;
   for (int tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
     const int nrows = rows(tile);
-    const int nblk = (nrows / 4) * 32;
+    const int nblk = ((nrows + 3) / 4) * 32;
     pre.put(os, n16(tile));
     __syncthreads();
     if (tile + 1 < tend) pre.fetch(codes(tile + 1), n16(tile + 1));
@@ -212,7 +227,11 @@ __global__ __launch_bounds__(NT) void k_zfp_encode128(const void *__restrict__ k
     __syncthreads();
     if (tile + 1 < tend) pre.fetch(src_f + (size_t)(tb + TILE_T) * D * esz, rows(tile + 1));
     gauge128_tile<BF16>(sh, sl, xs, fr);
-    const int nblk = (nrows / 4) * 32;
+    if (nrows & 3) {
+      pad_block_row(xs, nrows);
+      __syncthreads();
+    }
+    const int nblk = ((nrows + 3) / 4) * 32;
     for (int b = threadIdx.x; b < nblk; b += NT) {
       const float *src = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
       float v[16];
@@ -254,7 +273,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
   uint4 pre[NC];
   auto fetch = [&](int tile) {
     const uint4 *src = codes(tile);
-    const int n16 = (rows(tile) / 4) * 32 * 2 * R / 16;
+    const int n16 = ((rows(tile) + 3) / 4) * 32 * 2 * R / 16;
 #pragma unroll
     for (int k = 0; k < NC; k++) {
       const int i = threadIdx.x + NT * k;
@@ -266,7 +285,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
   for (int tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
     const int nrows = rows(tile);
-    const int nblk = (nrows / 4) * 32;
+    const int nblk = ((nrows + 3) / 4) * 32;
     const int n16 = nblk * 2 * R / 16;
 #pragma unroll
     for (int k = 0; k < NC; k++) {

@@ -4,12 +4,20 @@ histories, so every new KV token passes through gauge -> backend -> decode ->
 inverse gauge).
 
 One history buffer [fields, capacity, 128] (storage format) is the cache the
-attention reads.  The model writes each new token's K/V into row t.  When a
-4-token block row completes, cg_encode writes its fixed-rate codes at their
-fixed stream offset (an append: no other codes move); then cg_decode rewrites
-every encoded row [0, 4 floor(t/4)) with its reconstruction.  Rows of the
-incomplete block stay as written (at most 3 per field).  All arithmetic runs
-in the HIP library; this class only chooses rows and owns buffers.
+attention reads.  The model writes each new token's K/V into row t.
+
+every_token=True (default; the protocol above): after each append the 4-token
+block row that holds the new token is encoded from its raw tokens (a partial
+block row is padded by repeating its last token; a small side buffer keeps the
+raw tokens of the current block row, since the history rows hold
+reconstructions), its codes overwrite that block row's fixed stream offset,
+and cg_decode rewrites every row [0, t+1) with its reconstruction.
+
+every_token=False: only completed block rows are encoded and decoded; the at
+most 3 rows of the incomplete block stay as written.
+
+All arithmetic runs in the HIP library; this class only chooses rows and owns
+buffers.
 """
 from __future__ import annotations
 
@@ -18,7 +26,7 @@ from . import binding as cg
 
 class RollingHistory:
     def __init__(self, layers, kv, batch, heads, capacity, gauge, rate, dtype=cg.CG_DTYPE_BF16,
-                 head_dim=128):
+                 head_dim=128, every_token=True):
         import torch
 
         assert capacity % 4 == 0
@@ -27,10 +35,12 @@ class RollingHistory:
         self.head_dim = head_dim
         self.dtype = dtype
         self.gauge = gauge
+        self.every_token = every_token
         self.codec = cg.make_codec(cg.CG_BACKEND_ZFP, rate)
         self.fields = layers * kv * batch * heads
         tdt = torch.bfloat16 if dtype == cg.CG_DTYPE_BF16 else torch.float32
         self.history = torch.zeros((self.fields, capacity, head_dim), dtype=tdt, device="cuda")
+        self.raw_row = torch.zeros((self.fields, 4, head_dim), dtype=tdt, device="cuda")
         nbytes = cg.cg_encoded_bytes(self.shape(capacity), self.codec)[0]
         self.payload = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
         self.t = 0
@@ -40,10 +50,12 @@ class RollingHistory:
         return cg.make_shape(L, KV, B, H, tokens, self.capacity, self.head_dim, self.dtype)
 
     def prefill(self, kv, T0):
-        """Take rows [0, T0) of kv [fields, >=T0, d] as the initial history
-        (T0 % 4 == 0): encode them once and decode them."""
-        assert T0 % 4 == 0
+        """Take rows [0, T0) of kv [fields, >=T0, d] as the initial history:
+        encode them once and decode them (T0 % 4 == 0 unless every_token)."""
+        assert self.every_token or T0 % 4 == 0
         self.history[:, :T0].copy_(kv[:, :T0])
+        b = 4 * (T0 // 4)
+        self.raw_row[:, :T0 - b].copy_(kv[:, b:T0])
         self.t = T0
         sh = self.shape(T0)
         cg.cg_encode(sh, self.history, self.gauge, self.codec, 0, T0, self.payload)
@@ -53,9 +65,17 @@ class RollingHistory:
         """One decoding step: token_kv [fields, d] is the new token."""
         t = self.t
         assert t < self.capacity
-        self.history[:, t].copy_(token_kv)
         self.t = t + 1
         sh = self.shape(self.t)
+        b = 4 * (t // 4)
+        if self.every_token:
+            # the block row [b, t+1) from its raw tokens, padded when partial
+            self.raw_row[:, t - b].copy_(token_kv)
+            self.history[:, b:t + 1].copy_(self.raw_row[:, :t + 1 - b])
+            cg.cg_encode(sh, self.history, self.gauge, self.codec, b, t + 1 - b, self.payload)
+            cg.cg_decode(sh, self.payload, None, self.gauge, self.codec, 0, self.t, self.history)
+            return
+        self.history[:, t].copy_(token_kv)
         if self.t % 4 == 0:
             cg.cg_encode(sh, self.history, self.gauge, self.codec, self.t - 4, 4, self.payload)
         enc = 4 * (self.t // 4)

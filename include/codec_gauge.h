@@ -138,7 +138,10 @@ int cg_encoded_bytes(const cg_shape *shape, const cg_codec *codec, uint64_t *pay
  *            field sit at fixed offsets, so appends (t0 > 0) only write the
  *            rows they encode
  *   meta     device metadata buffer (quantizers), or NULL when meta_cap == 0
- * ZFP: t0, nt multiples of 4.  BLOCK_UNIFORM: multiples of block_tokens.
+ * ZFP: t0 a multiple of 4 and nt too, except where t0 + nt == tokens: a
+ * partial last block row is completed by repeating the last token (gauged)
+ * row, and decoding it returns the valid rows only.  BLOCK_UNIFORM:
+ * multiples of block_tokens.
  * KIVI: t0 == 0 and nt == tokens (whole fields).  t0 + nt <= tokens.
  */
 int cg_encode(const cg_shape *shape, const void *kv, const cg_gauge *gauge,

@@ -95,6 +95,24 @@ def test_codec_and_row_validation_before_launch():
     assert enc(cg.make_codec(cg.CG_BACKEND_ZFP, 4), 0, 0) == cg.CG_OK
 
 
+def test_zfp_partial_block_row_only_at_the_end():
+    # a zfp row range may end off a block-row boundary only at the field's
+    # last valid token (the partial last block row is padded)
+    shape = cg.make_shape(1, 2, 1, 2, 62, 64, 128, cg.CG_DTYPE_BF16)
+    dummy = ctypes.c_void_p(16)
+    L = cg.lib()
+    codec = cg.make_codec(cg.CG_BACKEND_ZFP, 4)
+
+    def enc(t0, nt):
+        return L.cg_encode(ctypes.byref(shape), dummy, ctypes.byref(cg.make_gauge(0)),
+                           ctypes.byref(codec), t0, nt, dummy, 1 << 30, None, 0, None)
+
+    assert enc(0, 61) == cg.CG_E_SHAPE
+    assert enc(0, 30) == cg.CG_E_SHAPE
+    assert enc(2, 60) == cg.CG_E_SHAPE
+    assert enc(0, 63) == cg.CG_E_SHAPE      # past the valid tokens
+
+
 def test_gauge_from_skew_matches_oracle():
     for g in (2, 16, 32, 128):
         A = synth.gauge_params(g, 3, g)

@@ -18,10 +18,10 @@ def as_f64(a):
         else a.astype(np.float64)
 
 
-def run(x, G, g, codec, L, KV, B, H, T, bf16, t0=0, nt=None):
+def run(x, G, g, codec, L, KV, B, H, T, bf16, t0=0, nt=None, Tcap=None):
     import torch
     nt = T if nt is None else nt
-    shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16 if bf16 else cg.CG_DTYPE_F32)
+    shape = cg.make_shape(L, KV, B, H, T, T if Tcap is None else Tcap, D, cg.CG_DTYPE_BF16 if bf16 else cg.CG_DTYPE_F32)
     gauge = cg.make_gauge(g, to_dev(np.ascontiguousarray(G)) if G is not None else None)
     xd = to_dev(x)
     pb, mb, _ = cg.cg_encoded_bytes(shape, codec)
@@ -70,6 +70,21 @@ def test_zfp_error_sums_fp32_partial_rows():
     _, o1, o2, err = run(x, G, 32, cg.make_codec(cg.CG_BACKEND_ZFP, 4), L, KV, B, H, T, False,
                          t0=64, nt=132)
     check(x, o1, o2, err, L, KV, B, H, 64, 132)
+
+
+@pytest.mark.parametrize("g", [16, 128])
+def test_zfp_error_sums_partial_last_block_row(g):
+    # T % 4 == 2: the padded rows of the last block row are decoded but
+    # neither stored nor counted
+    L, KV, B, H, T = 1, 2, 1, 1, 64 * 17 + 10
+    x = kv_cpu(530 + g, L, KV, B, H, T, T + 2, 0.95, 4, bf16=True)
+    G = gauges_for(531 + g, L, KV, H, g)
+    shape, o1, o2, err = run(x, G, g, cg.make_codec(cg.CG_BACKEND_ZFP, 4), L, KV, B, H, T, True,
+                             Tcap=T + 2)
+    check(x, o1, o2, err, L, KV, B, H, 0, T)
+    assert not np.any(o2[:, T:])
+    s = cg.cg_cache_error_summary(shape, err)
+    assert s["values"] == n_fields(L, KV, B, H) * T * D
 
 
 @pytest.mark.parametrize("backend,bits,blk,res,g", [

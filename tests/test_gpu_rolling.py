@@ -2,9 +2,11 @@
 evaluation-protocol paragraph: each compressed condition keeps its own
 history; every new token passes through gauge, backend, decode and inverse
 gauge).  After any number of appends the payload must equal a one-shot
-encode of the completed rows (bit-exact, since 4x4 blocks are independent and
-sit at fixed offsets), and the history must equal the oracle's decode of those
-rows followed by the raw pending rows."""
+encode of the same rows (bit-exact, since 4x4 blocks are independent and sit
+at fixed offsets).  Every-token mode: all t rows, a partial last block row
+padded by repeating its last token; the history equals their decode.
+Completed-rows mode: the rows of completed block rows, followed by the raw
+pending rows."""
 import numpy as np
 import pytest
 
@@ -39,6 +41,40 @@ def check(rh, raw_host, G, g, R, fields):
         assert np.array_equal(hist[enc:t], xf[enc:t]), (f, t)
 
 
+def check_every_token(rh, raw_host, G, g, R, fields):
+    import torch
+    torch.cuda.synchronize()
+    t = rh.t
+    L, KV, B, H = rh.dims
+    per = rh.capacity * D * R // 8
+    for f in fields:
+        xf = raw_host(f)
+        Gf = gauge_of_field(G, f, KV, B, H)
+        xg = oracle.gauge_forward(oracle.to_f32(xf[:t]), Gf, g)
+        p_ref = oracle.zfp_encode_field(xg, R, t0=0, nt=t, T_payload=rh.capacity)
+        assert np.array_equal(to_host(rh.payload[f * per:(f + 1) * per]), p_ref), (f, t)
+        yg = oracle.zfp_decode_field(p_ref, rh.capacity, D, R, 0, t)[:t]
+        y = oracle.f32_to_bf16(oracle.gauge_inverse(yg, Gf, g))
+        assert np.array_equal(to_host(rh.history[f])[:t], y), (f, t)
+
+
+@pytest.mark.parametrize("T0", [64, 66])
+def test_rolling_every_token_g16_rate3(T0):
+    L, KV, B, H, steps, cap = 1, 2, 2, 2, 11, 80
+    g, R = 16, 3
+    raw = kv_cpu(46 + T0, L, KV, B, H, T0 + steps, cap, 0.95, 4, bf16=True)
+    rawd = to_dev(raw)
+    G = gauges_for(47, L, KV, H, g)
+    gauge = cg.make_gauge(g, to_dev(np.ascontiguousarray(G)))
+    rh = RollingHistory(L, KV, B, H, cap, gauge, R)
+    rh.prefill(rawd, T0)
+    F = n_fields(L, KV, B, H)
+    check_every_token(rh, lambda f: raw[f], G, g, R, range(F))
+    for k in range(steps):
+        rh.append(rawd[:, T0 + k])
+        check_every_token(rh, lambda f: raw[f], G, g, R, range(F))
+
+
 def test_rolling_small_g32_rate4():
     L, KV, B, H, T0, steps, cap = 2, 2, 2, 2, 64, 14, 80
     g, R = 32, 4
@@ -46,7 +82,7 @@ def test_rolling_small_g32_rate4():
     rawd = to_dev(raw)
     G = gauges_for(45, L, KV, H, g)
     gauge = cg.make_gauge(g, to_dev(np.ascontiguousarray(G)))
-    rh = RollingHistory(L, KV, B, H, cap, gauge, R)
+    rh = RollingHistory(L, KV, B, H, cap, gauge, R, every_token=False)
     rh.prefill(rawd, T0)
     F = n_fields(L, KV, B, H)
     check(rh, lambda f: raw[f], G, g, R, range(F))
@@ -58,8 +94,9 @@ def test_rolling_small_g32_rate4():
 
 def test_rolling_decode_config_sampled():
     """Rolling-history workload: 64 sequences x 28 layers x 4 KV heads x 128,
-    history 8192 tokens (bf16), gauge g = 32, 4 b/v; 9 appends (two block
-    rows complete); sampled fields checked against the oracle."""
+    history 8192 tokens (bf16), gauge g = 32, 4 b/v; 9 appends in
+    every-token mode (two block rows complete, one partial); sampled fields
+    checked against the oracle."""
     import torch
     L, KV, B, H, T0, cap = 28, 2, 64, 4, 8192, 8448
     g, R = 32, 4
@@ -72,4 +109,4 @@ def test_rolling_decode_config_sampled():
         rh.append(raw[:, T0 + k])
     F = n_fields(L, KV, B, H)
     fields = [0, 1234, F // 2 + 7, F - 1]
-    check(rh, lambda f: to_host(raw[f]), G, g, R, fields)
+    check_every_token(rh, lambda f: to_host(raw[f]), G, g, R, fields)

@@ -80,6 +80,39 @@ def test_fp32_other_groups_batch(g):
     check_against_oracle(x, G, g, 3, L, KV, B, H, T, T, pay, out)
 
 
+@pytest.mark.parametrize("T,g,bf16", [(201, 16, True), (130, 0, False), (67, 32, True), (1, 8, True)])
+def test_partial_last_block_row(T, g, bf16):
+    # token counts that are not multiples of 4: the last block row is padded
+    # by repeating the last token; codes and decoded rows bit-exact
+    L, KV, B, H, Tcap = 1, 2, 1, 2, 256
+    x = kv_cpu(60 + T, L, KV, B, H, T, Tcap, 0.95, 4, bf16=bf16)
+    G = gauges_for(61, L, KV, H, g)
+    for R in (3, 4):
+        pay, out = run_zfp(x, G, g, R, L, KV, B, H, T, Tcap, bf16)
+        check_against_oracle(x, G, g, R, L, KV, B, H, T, Tcap, pay, out)
+        assert not np.any(out[:, T:])          # rows past the valid tokens untouched
+
+
+def test_partial_rows_dense_gauge():
+    # full-head gauge with a partial last block row: staged like the other
+    # dense-gauge test (gauged values from cg_gauge_apply, codes bit-exact)
+    t = __import__("torch")
+    L, KV, B, H, T = 1, 1, 1, 2, 64 * 17 + 6
+    x = kv_cpu(62, L, KV, B, H, T, T + 2, 0.95, 4, bf16=True)
+    G = gauges_for(63, L, KV, H, 128)
+    pay, out = run_zfp(x, G, 128, 4, L, KV, B, H, T, T + 2, True)
+    shape = cg.make_shape(L, KV, B, H, T, T + 2, D, cg.CG_DTYPE_BF16)
+    gauge = cg.make_gauge(128, to_dev(np.ascontiguousarray(G)))
+    xg_d = t.zeros((2, T + 2, D), dtype=t.float32, device="cuda")
+    cg.cg_gauge_apply(shape, to_dev(x), gauge, 0, xg_d)
+    t.cuda.synchronize()
+    xg = to_host(xg_d)
+    per = (T + 2) * D * 4 // 8
+    for f in range(2):
+        p_ref = oracle.zfp_encode_field(xg[f, :T], 4, t0=0, nt=T, T_payload=T + 2)
+        assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f
+
+
 def test_appends_equal_one_shot():
     L, KV, B, H, T, Tcap = 1, 2, 1, 2, 200, 256
     x = kv_cpu(9, L, KV, B, H, T, Tcap, 0.95, 4, bf16=True)
