@@ -223,6 +223,12 @@ def _codec_line(name, shape, x, G, g, codec, steps, warmup, esz, desc):
     dece = lambda: cg.cg_decode_error(shape, pay, meta, gauge, codec, 0, T, out, x, ws, err)
     tde = _time(dece, steps, warmup)
     summ = cg.cg_cache_error_summary(shape, err.cpu().numpy())
+    # recovery folded into the consumer: values (or keys and values) left gauged
+    folded = {}
+    if g:
+        for nm, keep in (("values", cg.CG_KEEP_VALUES), ("both", cg.CG_KEEP_KEYS | cg.CG_KEEP_VALUES)):
+            fn = lambda keep=keep: cg.cg_decode_gauged(shape, pay, meta, gauge, codec, 0, T, keep, out)
+            folded[f"decode_folded_{nm}_ms"] = round(_time(fn, steps, warmup) * 1e3, 4)
     N = x.numel()
     alg = N * esz + pb + mb
     del pay, meta, out, ws
@@ -234,7 +240,7 @@ def _codec_line(name, shape, x, G, g, codec, steps, warmup, esz, desc):
             "encode_ms": round(te * 1e3, 4), "decode_ms": round(td * 1e3, 4),
             "encode_kv_GBs": round(N * esz / te / 1e9, 2), "decode_kv_GBs": round(N * esz / td / 1e9, 2),
             "encode_hbm_frac": round(alg / te / 1e9 / HBM_PEAK_GBS, 4),
-            "decode_hbm_frac": round(alg / td / 1e9 / HBM_PEAK_GBS, 4)}
+            "decode_hbm_frac": round(alg / td / 1e9 / HBM_PEAK_GBS, 4), **folded}
 
 
 def small_lines(steps, warmup):
@@ -253,8 +259,8 @@ def small_lines(steps, warmup):
 
 
 def llama8b_lines(steps, warmup):
-    """Llama-3-8B-class cache at 3 and 6 b/v (4 b/v is the headline line), and
-    4 b/v with the other gauge groups"""
+    """Llama-3-8B-class cache at 3, 4 and 6 b/v with g = 16 (with the error
+    sums and the folded-recovery decodes), and 4 b/v with the other groups"""
     import torch
 
     from fixed_rate_compression_amd import binding as cg
@@ -263,7 +269,7 @@ def llama8b_lines(steps, warmup):
     x = _gen(L * KV * B * H, T, T, 0.95, 2, 4, True)
     G, _ = _gauge(L, KV, H, 16, 102)
     sh = cg.make_shape(L, KV, B, H, T, T, 128, cg.CG_DTYPE_BF16)
-    for R in (3, 6):
+    for R in (3, 4, 6):
         lines.append(_codec_line(f"llama8b_zfp{R}", sh, x, G, 16, cg.make_codec(cg.CG_BACKEND_ZFP, R),
                                  steps, warmup, 2, "32 layers x K/V x 8 heads x 32768 tokens bf16, g=16"))
     for g in (8, 32, 128):
@@ -306,23 +312,31 @@ def rolling_line():
     cap = T0 + 256
     raw = _gen(L * KV * B * H, T0 + nsteps, cap, 0.95, 4, 4, True)
     G, _ = _gauge(L, KV, H, 32, 104)
-    rh = RollingHistory(L, KV, B, H, cap, cg.make_gauge(32, G), 4)
-    rh.prefill(raw, T0)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for k in range(nsteps):
-        rh.append(raw[:, T0 + k])
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / nsteps
+
+    def run(keep):
+        rh = RollingHistory(L, KV, B, H, cap, cg.make_gauge(32, G), 4, keep=keep)
+        rh.prefill(raw, T0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for k in range(nsteps):
+            rh.append(raw[:, T0 + k])
+        b.record()
+        torch.cuda.synchronize()
+        del rh
+        torch.cuda.empty_cache()
+        return a.elapsed_time(b) / nsteps
+
+    ms = run(0)
+    ms_folded = run(cg.CG_KEEP_KEYS | cg.CG_KEEP_VALUES)
     Nmean = L * KV * B * H * 128 * (T0 + nsteps / 2)
     line = {"workload": "rolling_g32_zfp4", "desc": "64 seq x 28 layers x 4 heads, history 8192+, "
             f"{nsteps} appends (every token: re-encode its block row, partial rows padded; decode whole history)",
             "ms_per_step": round(ms, 4), "history_values_mean": int(Nmean),
             "decode_kv_GBs": round(Nmean * 2 / (ms * 1e-3) / 1e9, 2),
-            "decode_hbm_frac": round(Nmean * 2.5 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del raw, rh
+            "decode_hbm_frac": round(Nmean * 2.5 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_per_step_folded": round(ms_folded, 4)}
+    del raw
     torch.cuda.empty_cache()
     return line
 

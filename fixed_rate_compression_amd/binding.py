@@ -21,12 +21,14 @@ CG_DTYPE_F32, CG_DTYPE_BF16 = 0, 1
 CG_BACKEND_NONE, CG_BACKEND_ZFP, CG_BACKEND_BLOCK_UNIFORM, CG_BACKEND_KIVI = 0, 1, 2, 3
 CG_HEADER_BYTES = 64
 
-EXPORTED = ["cg_encoded_bytes", "cg_encode", "cg_decode", "cg_roundtrip", "cg_gauge_fit_stats",
-            "cg_stats_workspace_bytes", "cg_gauge_from_skew", "cg_gauge_apply", "cg_write_header",
-            "cg_decode_error_workspace_bytes", "cg_decode_error", "cg_cache_error_summary",
-            "cg_adamw_update", "cg_gauge_control", "cg_second_moment_workspace_bytes",
-            "cg_second_moment", "cg_gauge_grad", "cg_last_error"]
+EXPORTED = ["cg_encoded_bytes", "cg_encode", "cg_decode", "cg_decode_gauged", "cg_roundtrip",
+            "cg_gauge_fit_stats", "cg_stats_workspace_bytes", "cg_gauge_from_skew",
+            "cg_gauge_apply", "cg_write_header", "cg_decode_error_workspace_bytes",
+            "cg_decode_error", "cg_cache_error_summary", "cg_adamw_update", "cg_gauge_control",
+            "cg_second_moment_workspace_bytes", "cg_second_moment", "cg_gauge_grad", "cg_gauge_heads",
+            "cg_last_error"]
 
+CG_KEEP_KEYS, CG_KEEP_VALUES = 1, 2
 CG_CONTROL_IDENTITY, CG_CONTROL_HADAMARD, CG_CONTROL_DCT, CG_CONTROL_ORTHONORMALIZE, CG_CONTROL_KLT = range(5)
 
 
@@ -90,6 +92,8 @@ def lib():
             "cg_encoded_bytes": [SP, CP, U64P, U64P, U64P],
             "cg_encode": [SP, P, GP, CP, I64, I64, P, U64, P, U64, P],
             "cg_decode": [SP, P, U64, P, U64, GP, CP, I64, I64, P, P],
+            "cg_decode_gauged": [SP, P, U64, P, U64, GP, CP, I64, I64, I32, P, P],
+            "cg_gauge_heads": [SP, GP, I32, I32, I32, I64, I32, P, P, P],
             "cg_roundtrip": [SP, P, GP, CP, P, U64, P, U64, P, P],
             "cg_gauge_fit_stats": [SP, P, I32, P, I32, ctypes.c_float, ctypes.c_float,
                                    ctypes.c_float, P, ctypes.c_size_t, P, P, P],
@@ -185,6 +189,20 @@ def cg_decode(shape, payload, meta, gauge, codec, t0, nt, kv_out, stream=None):
                                         _ptr(meta), _nbytes(meta), ctypes.byref(gauge),
                                         ctypes.byref(codec), t0, nt, _ptr(kv_out),
                                         _stream(stream)))
+
+
+def cg_decode_gauged(shape, payload, meta, gauge, codec, t0, nt, keep, kv_out, stream=None):
+    """cg_decode leaving the kinds in `keep` (CG_KEEP_KEYS | CG_KEEP_VALUES) gauged."""
+    _check("cg_decode_gauged", lib().cg_decode_gauged(
+        ctypes.byref(shape), _ptr(payload), _nbytes(payload), _ptr(meta), _nbytes(meta),
+        ctypes.byref(gauge), ctypes.byref(codec), t0, nt, keep, _ptr(kv_out), _stream(stream)))
+
+
+def cg_gauge_heads(shape, gauge, layer, kind, q_heads, rows, dtype, x, y, stream=None):
+    """Forward gauge of (layer, kind) on the head segments of x [rows][q_heads*d] -> y."""
+    _check("cg_gauge_heads", lib().cg_gauge_heads(
+        ctypes.byref(shape), ctypes.byref(gauge), layer, kind, q_heads, rows, dtype, _ptr(x),
+        _ptr(y), _stream(stream)))
 
 
 def cg_decode_error_workspace_bytes(shape, gauge, codec, t0, nt):

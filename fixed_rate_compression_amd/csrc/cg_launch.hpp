@@ -33,6 +33,9 @@ struct TileArgs {
   // per-workgroup error partials [grid][3] they produce
   const void *ref;
   double *epart;
+  // decode only: the fields a launch covers, runs of fsel consecutive fields
+  // every fstep fields from field fbase (all fields: fsel = fstep = count)
+  int64_t fsel, fstep, fbase;
 };
 
 bool zfp_rate_built(int R);
@@ -40,6 +43,11 @@ hipError_t zfp_encode_launch(int R, bool bf16, int g, const void *kv, const floa
                              uint8_t *payload, const TileArgs &a, hipStream_t s);
 hipError_t zfp_decode_launch(int R, bool bf16, int g, const uint8_t *payload, const float *gauges,
                              void *out, const TileArgs &a, hipStream_t s);
+// forward gauge of (layer, kind) on head_dim segments of rows x, y
+// [rows][q_heads * 128] (query head h uses gauge head h / group_ratio); gk
+// points at the (layer, kind) gauges
+hipError_t gauge_heads_launch(int g, bool bf16, const void *x, const float *gk, void *y,
+                              int64_t rows, int q_heads, int group_ratio, hipStream_t s);
 hipError_t gauge_rows_launch(bool src_bf16, bool dst_bf16, bool inverse, int g, const void *src,
                              const float *gauges, void *dst, const TileArgs &a, hipStream_t s);
 // per-group second moments: part[field][moment_chunks(tokens)][D * g] (fp64)

@@ -19,6 +19,9 @@ struct QuantArgs {
   int32_t residual;  // KIVI tail rows
   const void *ref;   // decode: reference rows for the error sums (or null)
   double *epart;     // decode: per-workgroup error partials [grid][3]
+  // decode: fields covered, runs of fsel fields every fstep from fbase
+  // (`fields` is then the number covered)
+  int64_t fsel, fstep, fbase;
 };
 
 // tiles per workgroup: the dense gauge walks 16 tiles (1024 tokens) so each
@@ -40,6 +43,7 @@ inline QuantArgs make_args(int64_t tcap, int64_t tokens, int64_t t0, int64_t nt,
   q.tcap = tcap; q.tokens = tokens; q.t0 = t0; q.nt = nt; q.fields = fields;
   q.batch = batch; q.heads = heads; q.kv = kv; q.backend = backend; q.bits = bits;
   q.block = block; q.residual = residual;
+  q.fsel = q.fstep = fields; q.fbase = 0;
   return q;
 }
 

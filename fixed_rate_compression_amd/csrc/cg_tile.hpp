@@ -19,6 +19,12 @@ constexpr int D = 128;        // head_dim this build is specialized for
 constexpr int PITCH = D + 4;  // LDS row pitch in floats
 constexpr int NT = 256;       // threads per workgroup (4 waves)
 
+// field of launch field i when a launch covers runs of `sel` consecutive
+// fields every `step` fields, starting at field `base`
+__device__ __forceinline__ int64_t launch_field(int64_t i, int64_t sel, int64_t step, int64_t base) {
+  return (i / sel) * step + base + i % sel;
+}
+
 // gauge set index of a field: fields are (layer, kv, batch, head) row-major,
 // gauges (layer, kv, head) -- shared by every sequence of the batch
 __device__ __forceinline__ int64_t gauge_index(int64_t field, int B, int H) {

@@ -135,6 +135,8 @@ cgk::TileArgs tile_args(const cg_shape *s, int64_t t0, int64_t nt) {
   a.grid = n_fields(s) * a.tiles;
   a.batch = s->batch;
   a.heads = s->heads;
+  a.fsel = a.fstep = n_fields(s);
+  a.fbase = 0;
   return a;
 }
 
@@ -453,9 +455,11 @@ int64_t err_per_field(const cg_shape *s, const cg_codec *c, int g, int64_t nt) {
   return tiles;
 }
 
+// keep: bit s set = fields with K/V index s are written in gauged coordinates
+// (their inverse gauge is skipped); only without error sums
 int decode_impl(const cg_shape *shape, const void *payload, uint64_t payload_cap, const void *meta,
                 uint64_t meta_cap, const cg_gauge *gauge, const cg_codec *codec, int64_t t0,
-                int64_t nt, void *kv_out, const void *ref, double *epart, void *stream) {
+                int64_t nt, void *kv_out, const void *ref, double *epart, int keep, void *stream) {
   int rc;
   if ((rc = check_shape(shape))) return rc;
   if ((rc = check_codec(codec, shape))) return rc;
@@ -471,28 +475,46 @@ int decode_impl(const cg_shape *shape, const void *payload, uint64_t payload_cap
   if (nt == 0) return CG_OK;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = shape->dtype == CG_DTYPE_BF16;
-  const int g = gauge->group;
-  hipError_t e = hipSuccess;
-  cgk::TileArgs ta = tile_args(shape, t0, nt);
-  ta.ref = ref;
-  ta.epart = epart;
-  switch (codec->backend) {
-    case CG_BACKEND_NONE:
-      e = cgk::gauge_rows_launch(false, bf16, true, g, payload, gauge->G, kv_out, ta, s);
-      break;
-    case CG_BACKEND_ZFP:
-      e = cgk::zfp_decode_launch(codec->bits, bf16, g, (const uint8_t *)payload, gauge->G, kv_out, ta, s);
-      break;
-    case CG_BACKEND_BLOCK_UNIFORM:
-    case CG_BACKEND_KIVI: {
-      cgq::QuantArgs q = cgq::make_args(shape->token_capacity, shape->tokens, t0, nt, n_fields(shape),
-                                        shape->batch, shape->heads, codec->backend, codec->bits,
-                                        codec->block_tokens, codec->residual_tokens, shape->kv);
-      q.ref = ref;
-      q.epart = epart;
-      e = cgq::decode_launch(q, bf16, g, (const uint8_t *)payload, (const float *)meta, gauge->G, kv_out, s);
-      break;
+  const int64_t F = n_fields(shape), BH = (int64_t)shape->batch * shape->heads;
+  // one launch over the fields {(i / sel) * step + base + i % sel : i < count}
+  auto launch = [&](int g, int64_t count, int64_t sel, int64_t step, int64_t base) {
+    switch (codec->backend) {
+      case CG_BACKEND_NONE:
+      case CG_BACKEND_ZFP: {
+        cgk::TileArgs ta = tile_args(shape, t0, nt);
+        ta.grid = count * ta.tiles;
+        ta.fsel = sel; ta.fstep = step; ta.fbase = base;
+        ta.ref = ref;
+        ta.epart = epart;
+        if (codec->backend == CG_BACKEND_NONE)
+          return cgk::gauge_rows_launch(false, bf16, true, g, payload, gauge->G, kv_out, ta, s);
+        return cgk::zfp_decode_launch(codec->bits, bf16, g, (const uint8_t *)payload, gauge->G,
+                                      kv_out, ta, s);
+      }
+      default: {
+        cgq::QuantArgs q = cgq::make_args(shape->token_capacity, shape->tokens, t0, nt, count,
+                                          shape->batch, shape->heads, codec->backend, codec->bits,
+                                          codec->block_tokens, codec->residual_tokens, shape->kv);
+        q.fsel = sel; q.fstep = step; q.fbase = base;
+        q.ref = ref;
+        q.epart = epart;
+        return cgq::decode_launch(q, bf16, g, (const uint8_t *)payload, (const float *)meta,
+                                  gauge->G, kv_out, s);
+      }
     }
+  };
+  const int all = (1 << shape->kv) - 1;
+  hipError_t e;
+  if (gauge->group == 0 || keep == 0) {
+    e = launch(gauge->group, F, F, F, 0);
+  } else if (keep == all) {
+    e = launch(0, F, F, F, 0);
+  } else {
+    // two kinds, one kept: per layer, B*H fields of each kind
+    const int kept = keep == 1 ? 0 : 1;
+    const int64_t per = F / 2;
+    e = launch(gauge->group, per, BH, 2 * BH, (1 - kept) * BH);
+    if (e == hipSuccess) e = launch(0, per, BH, 2 * BH, kept * BH);
   }
   if (e != hipSuccess) return hip_fail(e, "cg_decode launch");
   return CG_OK;
@@ -505,7 +527,21 @@ int cg_decode(const cg_shape *shape, const void *payload, uint64_t payload_cap, 
               int64_t nt, void *kv_out, void *stream) {
   g_err.clear();
   return decode_impl(shape, payload, payload_cap, meta, meta_cap, gauge, codec, t0, nt, kv_out,
-                     nullptr, nullptr, stream);
+                     nullptr, nullptr, 0, stream);
+}
+
+int cg_decode_gauged(const cg_shape *shape, const void *payload, uint64_t payload_cap,
+                     const void *meta, uint64_t meta_cap, const cg_gauge *gauge,
+                     const cg_codec *codec, int64_t t0, int64_t nt, int32_t keep, void *kv_out,
+                     void *stream) {
+  g_err.clear();
+  if (!shape) return fail(CG_E_INVAL, "shape is NULL");
+  if (keep < 0 || keep > CG_KEEP_KEYS + CG_KEEP_VALUES)
+    return fail(CG_E_INVAL, "keep %d: use CG_KEEP_KEYS | CG_KEEP_VALUES", keep);
+  if ((keep & CG_KEEP_VALUES) && shape->kv != 2)
+    return fail(CG_E_INVAL, "CG_KEEP_VALUES needs a shape with kv = 2");
+  return decode_impl(shape, payload, payload_cap, meta, meta_cap, gauge, codec, t0, nt, kv_out,
+                     nullptr, nullptr, keep, stream);
 }
 
 int cg_decode_error_workspace_bytes(const cg_shape *shape, const cg_gauge *gauge,
@@ -540,7 +576,7 @@ int cg_decode_error(const cg_shape *shape, const void *payload, uint64_t payload
   }
   double *epart = (double *)workspace;
   rc = decode_impl(shape, payload, payload_cap, meta, meta_cap, gauge, codec, t0, nt, kv_out, kv_ref,
-                   epart, stream);
+                   epart, 0, stream);
   if (rc) return rc;
   hipError_t e = cgk::error_reduce_launch(epart, n_fields(shape), err_per_field(shape, codec, gauge->group, nt),
                                           (double)nt * shape->head_dim, (double *)err, (hipStream_t)stream);
@@ -605,6 +641,36 @@ int cg_gauge_apply(const cg_shape *shape, const void *kv, const cg_gauge *gauge,
     e = cgk::gauge_rows_launch(bf16, false, direction == 1, gauge->group, kv, gauge->G, out,
                                tile_args(shape, 0, shape->tokens), s);
   if (e != hipSuccess) return hip_fail(e, "cg_gauge_apply launch");
+  return CG_OK;
+}
+
+int cg_gauge_heads(const cg_shape *shape, const cg_gauge *gauge, int32_t layer, int32_t kind,
+                   int32_t q_heads, int64_t rows, int32_t dtype, const void *x, void *y,
+                   void *stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if ((rc = check_gauge(gauge, shape, nullptr))) return rc;
+  if (layer < 0 || layer >= shape->layers || kind < 0 || kind >= shape->kv)
+    return fail(CG_E_SHAPE, "layer %d / kind %d outside the cache shape", layer, kind);
+  if (q_heads <= 0 || q_heads % shape->heads || q_heads > 65535)
+    return fail(CG_E_SHAPE, "q_heads %d must be a positive multiple of heads %d", q_heads,
+                shape->heads);
+  if (rows < 0) return fail(CG_E_SHAPE, "rows < 0");
+  if (dtype != CG_DTYPE_F32 && dtype != CG_DTYPE_BF16) return fail(CG_E_INVAL, "bad dtype %d", dtype);
+  if (rows == 0) return CG_OK;
+  if (!x || !y) return fail(CG_E_INVAL, "x or y is NULL");
+  if ((rows + 63) / 64 >= ((int64_t)1 << 31)) return fail(CG_E_SHAPE, "too many rows");
+  const int64_t esz = dtype == CG_DTYPE_BF16 ? 2 : 4, bytes = rows * q_heads * shape->head_dim * esz;
+  const char *xb = (const char *)x, *yb = (const char *)y;
+  if (xb < yb + bytes && yb < xb + bytes) return fail(CG_E_INVAL, "x and y overlap");
+  const int g = gauge->group;
+  const float *gk = g ? gauge->G + ((int64_t)layer * shape->kv + kind) * shape->heads *
+                                       shape->head_dim * g
+                      : nullptr;
+  hipError_t e = cgk::gauge_heads_launch(g, dtype == CG_DTYPE_BF16, x, gk, y, rows, q_heads,
+                                         q_heads / shape->heads, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cg_gauge_heads launch");
   return CG_OK;
 }
 

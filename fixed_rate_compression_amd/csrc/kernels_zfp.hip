@@ -52,7 +52,7 @@ __global__ __launch_bounds__(NT) void k_gauge_rows(const void *__restrict__ src,
                                                    const float *__restrict__ gauges,
                                                    void *__restrict__ dst, TileArgs a) {
   __shared__ float xs[TILE_T * PITCH];
-  const int64_t field = (int64_t)blockIdx.x / a.tiles;
+  const int64_t field = launch_field((int64_t)blockIdx.x / a.tiles, a.fsel, a.fstep, a.fbase);
   const int tile = (int)((int64_t)blockIdx.x % a.tiles);
   const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
   const int nrows = (int)min((int64_t)TILE_T, a.t0 + a.nt - tb);

@@ -40,6 +40,7 @@ struct QK {
   int32_t residual;         // KIVI: tail rows kept in the storage format
   const void *ref;          // decode: reference rows for the error sums (or null)
   double *epart;            // decode: per-workgroup error partials [grid][3]
+  int64_t fsel, fstep, fbase;  // decode: fields covered (launch_field)
 };
 
 // valid rows of tile `tile` of the call's row range
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
                                                   void *__restrict__ out, QK a) {
   __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
   float *xs = (float *)lds;
-  const int64_t f = (int64_t)blockIdx.x / a.chunks;
+  const int64_t f = launch_field((int64_t)blockIdx.x / a.chunks, a.fsel, a.fstep, a.fbase);
   const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
   float *xs = (float *)lds;
   __shared__ float pmn[2 * D], psc[2 * D];
   constexpr size_t ESZ = BF16 ? 2 : 4;
-  const int64_t f = (int64_t)blockIdx.x / a.chunks;
+  const int64_t f = launch_field((int64_t)blockIdx.x / a.chunks, a.fsel, a.fstep, a.fbase);
   const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;

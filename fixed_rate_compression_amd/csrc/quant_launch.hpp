@@ -21,6 +21,9 @@ inline QK make_qk(const QuantArgs &q, int tiles_per_chunk) {
   a.residual = q.residual;
   a.ref = q.ref;
   a.epart = q.epart;
+  a.fsel = q.fsel;
+  a.fstep = q.fstep;
+  a.fbase = q.fbase;
   return a;
 }
 

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
                                                    void *__restrict__ out, TileArgs a) {
   __shared__ float xs[TILE_T * PITCH];
   __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
-  const int64_t field = (int64_t)blockIdx.x / a.chunks;
+  const int64_t field = launch_field((int64_t)blockIdx.x / a.chunks, a.fsel, a.fstep, a.fbase);
   const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * a.chunk_tiles;
   const int tend = min(a.tiles, tile0 + a.chunk_tiles);
   const size_t esz = BF16 ? 2 : 4;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
   constexpr int NC = (TILE_T / 4 * 32 * 2 * R / 16 + NT - 1) / NT;  // 16-B code pieces per thread
   float *xs = (float *)lds;
   uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
-  const int64_t field = (int64_t)blockIdx.x / a.chunks;
+  const int64_t field = launch_field((int64_t)blockIdx.x / a.chunks, a.fsel, a.fstep, a.fbase);
   const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * ZFP128_CHUNK;
   const int tend = min(a.tiles, tile0 + ZFP128_CHUNK);
   const size_t esz = BF16 ? 2 : 4;

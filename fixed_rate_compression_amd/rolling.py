@@ -16,6 +16,11 @@ and cg_decode rewrites every row [0, t+1) with its reconstruction.
 every_token=False: only completed block rows are encoded and decoded; the at
 most 3 rows of the incomplete block stay as written.
 
+keep (CG_KEEP_KEYS | CG_KEEP_VALUES, every-token mode only): the history
+holds those kinds in gauged coordinates (cg_decode_gauged), for a consumer
+that folds the recovery into its query and output projection
+(cg_gauge_heads).
+
 All arithmetic runs in the HIP library; this class only chooses rows and owns
 buffers.
 """
@@ -26,7 +31,7 @@ from . import binding as cg
 
 class RollingHistory:
     def __init__(self, layers, kv, batch, heads, capacity, gauge, rate, dtype=cg.CG_DTYPE_BF16,
-                 head_dim=128, every_token=True):
+                 head_dim=128, every_token=True, keep=0):
         import torch
 
         assert capacity % 4 == 0
@@ -36,6 +41,8 @@ class RollingHistory:
         self.dtype = dtype
         self.gauge = gauge
         self.every_token = every_token
+        assert every_token or not keep, "a gauged history needs every-token mode"
+        self.keep = keep
         self.codec = cg.make_codec(cg.CG_BACKEND_ZFP, rate)
         self.fields = layers * kv * batch * heads
         tdt = torch.bfloat16 if dtype == cg.CG_DTYPE_BF16 else torch.float32
@@ -49,6 +56,10 @@ class RollingHistory:
         L, KV, B, H = self.dims
         return cg.make_shape(L, KV, B, H, tokens, self.capacity, self.head_dim, self.dtype)
 
+    def _decode(self, sh, n):
+        cg.cg_decode_gauged(sh, self.payload, None, self.gauge, self.codec, 0, n, self.keep,
+                            self.history)
+
     def prefill(self, kv, T0):
         """Take rows [0, T0) of kv [fields, >=T0, d] as the initial history:
         encode them once and decode them (T0 % 4 == 0 unless every_token)."""
@@ -59,7 +70,7 @@ class RollingHistory:
         self.t = T0
         sh = self.shape(T0)
         cg.cg_encode(sh, self.history, self.gauge, self.codec, 0, T0, self.payload)
-        cg.cg_decode(sh, self.payload, None, self.gauge, self.codec, 0, T0, self.history)
+        self._decode(sh, T0)
 
     def append(self, token_kv):
         """One decoding step: token_kv [fields, d] is the new token."""
@@ -73,7 +84,7 @@ class RollingHistory:
             self.raw_row[:, t - b].copy_(token_kv)
             self.history[:, b:t + 1].copy_(self.raw_row[:, :t + 1 - b])
             cg.cg_encode(sh, self.history, self.gauge, self.codec, b, t + 1 - b, self.payload)
-            cg.cg_decode(sh, self.payload, None, self.gauge, self.codec, 0, self.t, self.history)
+            self._decode(sh, self.t)
             return
         self.history[:, t].copy_(token_kv)
         if self.t % 4 == 0:

@@ -159,6 +159,26 @@ int cg_decode(const cg_shape *shape, const void *payload, uint64_t payload_cap,
               const cg_codec *codec, int64_t t0, int64_t nt, void *kv_out, void *stream);
 
 /*
+ * Recovery folded into the consumer (gauge-parameterization paragraph, arXiv
+ * page: some recovery operations can move into the downstream projections;
+ * on the key side that depends on the positional encoding).  cg_decode_gauged
+ * is cg_decode, except that fields whose K/V index s has bit s set in `keep`
+ * are written in gauged coordinates, x' = G x: their inverse gauge is
+ * skipped.  The consumer then applies G on its side with cg_gauge_heads:
+ *   keys    q . (G^T k') = (G q) . k'    gauge each query after its RoPE
+ *   values  W_o (G^T u) = (W_o G^T) u    gauge the rows of W_o once
+ * keep: 0 (same as cg_decode), CG_KEEP_KEYS, CG_KEEP_VALUES (shape kv = 2)
+ * or both; other values give CG_E_INVAL.  Same layout, alignment and error
+ * behaviour as cg_decode; one launch per kind that differs in treatment.
+ */
+#define CG_KEEP_KEYS 1   /* K/V index 0 */
+#define CG_KEEP_VALUES 2 /* K/V index 1 */
+int cg_decode_gauged(const cg_shape *shape, const void *payload, uint64_t payload_cap,
+                     const void *meta, uint64_t meta_cap, const cg_gauge *gauge,
+                     const cg_codec *codec, int64_t t0, int64_t nt, int32_t keep, void *kv_out,
+                     void *stream);
+
+/*
  * Cache-side error (evaluation protocol, arXiv page: compressed bytes, actual
  * bits/value, KV MSE, KV NRMSE, key/value NRMSE and maximum absolute error;
  * the evaluator keeps raw sums and counts).  Per field, over the decoded rows
@@ -265,6 +285,26 @@ int cg_gauge_from_skew(int64_t n, int32_t g, const double *A_host, float *G_host
  */
 int cg_gauge_apply(const cg_shape *shape, const void *kv, const cg_gauge *gauge,
                    int32_t direction, float *out, void *stream);
+
+/*
+ * Consumer side of the folded recovery (see cg_decode_gauged): the forward
+ * gauge of cache layer `layer`, K/V index `kind`, on the head_dim segments
+ * of `rows` rows,
+ *   y[r][h d + c] = sum_k G[h / (q_heads / heads)][c / g][c % g][k] * x[r][h d + (c / g) g + k]
+ * as an fp32 fmaf chain over k = 0..g-1 from +0 (the fused gauge's order);
+ * group 0 copies.  Query head h uses the gauge of KV head h / (q_heads /
+ * heads) (grouped-query attention).
+ *   shape    the cache shape the gauges belong to (layers, kv, heads, head_dim)
+ *   x, y     device [rows][q_heads * head_dim], both CG_DTYPE_F32 or both
+ *            CG_DTYPE_BF16 (`dtype`; bf16 output rounded to nearest even);
+ *            they must not overlap (CG_E_INVAL)
+ *   q_heads  a positive multiple of shape->heads (CG_E_SHAPE otherwise)
+ * Queries: x = post-RoPE queries, kind 0.  Output projection: x = W_o
+ * ([d_model][q_heads * head_dim], row-major), kind 1.  Asynchronous on stream.
+ */
+int cg_gauge_heads(const cg_shape *shape, const cg_gauge *gauge, int32_t layer, int32_t kind,
+                   int32_t q_heads, int64_t rows, int32_t dtype, const void *x, void *y,
+                   void *stream);
 
 /*
  * Gauge training and coordinate controls.

@@ -183,6 +183,29 @@ def gauge_inverse_f64(y: np.ndarray, G: np.ndarray, g: int) -> np.ndarray:
     return np.einsum("rik,tri->trk", np.asarray(G, np.float64), yr).reshape(T, d)
 
 
+def gauge_heads(x: np.ndarray, G_lk: np.ndarray | None, g: int, q_heads: int) -> np.ndarray:
+    """Consumer side of recovery folded into the downstream projection
+    ("Codec-Gauge", arXiv HTML, gauge-parameterization paragraph): with the
+    cache kept gauged, q . (G^T k') = (G q) . k' and W_o G^T has rows G w.
+    x [rows, q_heads*d] fp32 -> the forward gauge (fmaf chain, as
+    gauge_forward) on every head segment, query head h taking the gauges
+    G_lk[h // (q_heads // H)] of its KV head; G_lk [H, d/g, g, g]."""
+    x = _f32(x)
+    rows, width = x.shape
+    d = width // q_heads
+    y = np.empty_like(x)
+    if g == 0:
+        y[...] = x
+        return y
+    H = G_lk.shape[0]
+    ratio = q_heads // H
+    assert q_heads % H == 0 and width == q_heads * d
+    for h in range(q_heads):
+        seg = slice(h * d, (h + 1) * d)
+        y[:, seg] = gauge_forward(np.ascontiguousarray(x[:, seg]), G_lk[h // ratio], g)
+    return y
+
+
 # --------------------------------------------------------------------------
 # zfp-style fixed-rate coder
 # --------------------------------------------------------------------------

@@ -139,3 +139,35 @@ def test_header_layout():
     vals = np.frombuffer(h[4:48], np.int32)
     assert list(vals) == [1, 1, 4, 0, 0, 1, 1, 0, 1, 8, 128]
     assert list(np.frombuffer(h[48:64], np.int64)) == [100, 128]
+
+
+def test_decode_gauged_and_gauge_heads_validation():
+    dummy = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    L = cg.lib()
+    codec = cg.make_codec(cg.CG_BACKEND_ZFP, 4)
+    G = np.zeros(1, np.float32)
+
+    def dec(shape, keep):
+        return L.cg_decode_gauged(ctypes.byref(shape), dummy, 1 << 30, None, 0,
+                                  ctypes.byref(cg.make_gauge(16, G)), ctypes.byref(codec), 0, 64,
+                                  keep, dummy, None)
+
+    s2 = cg.make_shape(1, 2, 1, 2, 64, 64, 128, cg.CG_DTYPE_BF16)
+    s1 = cg.make_shape(1, 1, 1, 2, 64, 64, 128, cg.CG_DTYPE_BF16)
+    assert dec(s2, 4) == cg.CG_E_INVAL and "keep" in cg.cg_last_error()
+    assert dec(s2, -1) == cg.CG_E_INVAL
+    assert dec(s1, cg.CG_KEEP_VALUES) == cg.CG_E_INVAL
+
+    def heads(layer, kind, q_heads, rows, dtype=cg.CG_DTYPE_F32, x=16, y=1 << 40, g=16):
+        return L.cg_gauge_heads(ctypes.byref(s2), ctypes.byref(cg.make_gauge(g, G)), layer, kind,
+                                q_heads, rows, dtype, ctypes.c_void_p(x), ctypes.c_void_p(y), None)
+
+    assert heads(1, 0, 8, 4) == cg.CG_E_SHAPE         # layer outside the cache
+    assert heads(0, 2, 8, 4) == cg.CG_E_SHAPE         # kind outside the cache
+    assert heads(0, 0, 3, 4) == cg.CG_E_SHAPE         # q_heads not a multiple of heads
+    assert heads(0, 0, 8, -1) == cg.CG_E_SHAPE
+    assert heads(0, 0, 8, 4, dtype=7) == cg.CG_E_INVAL
+    assert heads(0, 0, 8, 4, x=4096, y=4096 + 1024) == cg.CG_E_INVAL   # overlapping x and y
+    assert "overlap" in cg.cg_last_error()
+    assert heads(0, 0, 8, 4, g=64) == cg.CG_E_UNSUPPORTED
+    assert heads(0, 0, 8, 0) == cg.CG_OK               # no rows: nothing launched

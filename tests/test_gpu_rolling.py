@@ -54,7 +54,8 @@ def check_every_token(rh, raw_host, G, g, R, fields):
         p_ref = oracle.zfp_encode_field(xg, R, t0=0, nt=t, T_payload=rh.capacity)
         assert np.array_equal(to_host(rh.payload[f * per:(f + 1) * per]), p_ref), (f, t)
         yg = oracle.zfp_decode_field(p_ref, rh.capacity, D, R, 0, t)[:t]
-        y = oracle.f32_to_bf16(oracle.gauge_inverse(yg, Gf, g))
+        kept = (rh.keep >> ((f // (B * H)) % KV)) & 1     # kind left in gauged coordinates
+        y = oracle.f32_to_bf16(yg if kept else oracle.gauge_inverse(yg, Gf, g))
         assert np.array_equal(to_host(rh.history[f])[:t], y), (f, t)
 
 
@@ -67,6 +68,24 @@ def test_rolling_every_token_g16_rate3(T0):
     G = gauges_for(47, L, KV, H, g)
     gauge = cg.make_gauge(g, to_dev(np.ascontiguousarray(G)))
     rh = RollingHistory(L, KV, B, H, cap, gauge, R)
+    rh.prefill(rawd, T0)
+    F = n_fields(L, KV, B, H)
+    check_every_token(rh, lambda f: raw[f], G, g, R, range(F))
+    for k in range(steps):
+        rh.append(rawd[:, T0 + k])
+        check_every_token(rh, lambda f: raw[f], G, g, R, range(F))
+
+
+@pytest.mark.parametrize("keep", [cg.CG_KEEP_VALUES, cg.CG_KEEP_KEYS | cg.CG_KEEP_VALUES])
+def test_rolling_every_token_gauged_history(keep):
+    # recovery folded into the consumer: the kept kinds stay gauged in the history
+    L, KV, B, H, T0, steps, cap = 2, 2, 1, 2, 62, 7, 72
+    g, R = 32, 4
+    raw = kv_cpu(48 + keep, L, KV, B, H, T0 + steps, cap, 0.95, 4, bf16=True)
+    rawd = to_dev(raw)
+    G = gauges_for(49, L, KV, H, g)
+    gauge = cg.make_gauge(g, to_dev(np.ascontiguousarray(G)))
+    rh = RollingHistory(L, KV, B, H, cap, gauge, R, keep=keep)
     rh.prefill(rawd, T0)
     F = n_fields(L, KV, B, H)
     check_every_token(rh, lambda f: raw[f], G, g, R, range(F))
