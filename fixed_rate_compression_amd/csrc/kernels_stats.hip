@@ -74,7 +74,8 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
   const int64_t f = (int64_t)blockIdx.x / a.chunks;
   const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
   const int64_t ntiles = (a.tokens + TILE_T - 1) / TILE_T;
-  const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
+  TileGauge<G, false> tg;
+  if constexpr (G != 0) tg.load(gauges + gauge_index(f, a.batch, a.heads) * D * G);
 
   for (int i = threadIdx.x; i < D * D; i += NT) {
     const int v = i >> 7, c = i & 127;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
     }
     __syncthreads();
     if constexpr (G != 0) {
-      gauge_tile<G, false>(xs, nrows, Gf);
+      tg.apply(xs, nrows);
       __syncthreads();
     }
     const bool active = 16 * wave < nrows;

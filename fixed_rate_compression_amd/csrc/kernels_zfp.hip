@@ -60,7 +60,9 @@ __global__ __launch_bounds__(NT) void k_gauge_rows(const void *__restrict__ src,
   load_tile<SRC_BF16>((const uint8_t *)src + (size_t)row0 * D * (SRC_BF16 ? 2 : 4), nrows, xs);
   __syncthreads();
   if constexpr (G != 0) {
-    gauge_tile<G, INV>(xs, nrows, gauges + gauge_index(field, a.batch, a.heads) * D * G);
+    TileGauge<G, INV> tg;
+    tg.load(gauges + gauge_index(field, a.batch, a.heads) * D * G);
+    tg.apply(xs, nrows);
     __syncthreads();
   }
   const size_t off = (size_t)row0 * D * (DST_BF16 ? 2 : 4);

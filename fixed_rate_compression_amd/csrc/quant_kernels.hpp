@@ -178,7 +178,8 @@ struct GaugedTiles {
   // next_src/next_rows: the tile after this one (next_rows = 0: none)
   __device__ __forceinline__ void next(const void *__restrict__ src, int nrows,
                                        const void *__restrict__ next_src, int next_rows,
-                                       unsigned char *lds, const float *Gf, const G128Frags &fr) {
+                                       unsigned char *lds, const TileGauge<G, false> &tg,
+                                       const G128Frags &fr) {
     float *xs = (float *)lds;
     if constexpr (G == 128) {
       uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
@@ -192,7 +193,7 @@ struct GaugedTiles {
       __syncthreads();
       if (next_rows > 0) pre.fetch(next_src, next_rows);
       if constexpr (G != 0) {
-        gauge_tile<G, false>(xs, nrows, Gf);
+        tg.apply(xs, nrows);
         __syncthreads();
       }
     }
@@ -204,7 +205,8 @@ struct GaugedTiles {
 template <int G>
 __device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, int j,
                                                     const float (&v)[32], int nrows,
-                                                    const float *Gf, const G128Frags &fr) {
+                                                    const TileGauge<G, true> &tg,
+                                                    const G128Frags &fr) {
   float *xs = (float *)lds;
   if constexpr (G == 128) {
     uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
@@ -215,7 +217,7 @@ __device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, i
     write32(xs, t, j, v);
     __syncthreads();
     if constexpr (G != 0) {
-      gauge_tile<G, true>(xs, nrows, Gf);
+      tg.apply(xs, nrows);
       __syncthreads();
     }
   }
@@ -278,6 +280,8 @@ __global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
   if constexpr (G == 128) load_g128<false>(Gf, fr);
+  TileGauge<G, false> tg;
+  if constexpr (G != 0 && G != 128) tg.load(Gf);
   const int BT = a.block;
   const int64_t nblk_f = a.tcap / BT;
   const int t = threadIdx.x >> 2, j = threadIdx.x & 3, w = threadIdx.x >> 6;
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
     const int64_t tb = a.t0 + tile * TILE_T;
     const int nrows = tile_rows(a, tile);
     tiles.next(src_f + (size_t)tb * D * ESZ, nrows, src_f + (size_t)(tb + TILE_T) * D * ESZ,
-               tile + 1 < tend ? tile_rows(a, tile + 1) : 0, lds, Gf, fr);
+               tile + 1 < tend ? tile_rows(a, tile + 1) : 0, lds, tg, fr);
     const bool active = t < nrows;
     float v[32];
     float mn = INFINITY, mx = -INFINITY;
@@ -347,6 +351,8 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
   if constexpr (G == 128) load_g128<true>(Gf, fr);
+  TileGauge<G, true> tg;
+  if constexpr (G != 0 && G != 128) tg.load(Gf);
   const int BT = a.block;
   const int64_t nblk_f = a.tcap / BT;
   const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
     if (tile + 1 < tend) fetch(tile + 1);
-    inverse_gauged_tile<G>(lds, t, j, v, nrows, Gf, fr);
+    inverse_gauged_tile<G>(lds, t, j, v, nrows, tg, fr);
     const size_t off = (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
     if (a.ref)
       store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
@@ -416,6 +422,8 @@ __global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
   if constexpr (G == 128) load_g128<false>(Gf, fr);
+  TileGauge<G, false> tg;
+  if constexpr (G != 0 && G != 128) tg.load(Gf);
   const int64_t Tq = a.tokens - a.residual, Tcq = a.tcap - a.residual;
   const size_t Pf = (size_t)Tcq * 16 * BITS + (size_t)a.residual * D * ESZ;
   uint8_t *pf = payload + (size_t)f * Pf;
@@ -431,7 +439,7 @@ __global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
     const int64_t tb = a.t0 + tile * TILE_T;
     const int nrows = tile_rows(a, tile);
     tiles.next(src_f + (size_t)tb * D * ESZ, nrows, src_f + (size_t)(tb + TILE_T) * D * ESZ,
-               tile + 1 < tend ? tile_rows(a, tile + 1) : 0, lds, Gf, fr);
+               tile + 1 < tend ? tile_rows(a, tile + 1) : 0, lds, tg, fr);
     if (keys) {
       const int gi = threadIdx.x >> 7, c = threadIdx.x & 127;
       const int r0 = 32 * gi;
@@ -507,6 +515,8 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
   if constexpr (G == 128) load_g128<true>(Gf, fr);
+  TileGauge<G, true> tg;
+  if constexpr (G != 0 && G != 128) tg.load(Gf);
   const int64_t Tq = a.tokens - a.residual, Tcq = a.tcap - a.residual;
   const size_t Pf = (size_t)Tcq * 16 * BITS + (size_t)a.residual * D * ESZ;
   const uint8_t *pf = payload + (size_t)f * Pf;
@@ -572,7 +582,7 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
     if (tile + 1 < tend) fetch(tile + 1);
-    inverse_gauged_tile<G>(lds, t, j, v, nrows, Gf, fr);
+    inverse_gauged_tile<G>(lds, t, j, v, nrows, tg, fr);
     const size_t off = (size_t)(f * a.tcap + tb) * D * ESZ;
     if (a.ref)
       store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);

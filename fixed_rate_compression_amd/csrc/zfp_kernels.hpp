@@ -83,7 +83,8 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
   const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * a.chunk_tiles;
   const int tend = min(a.tiles, tile0 + a.chunk_tiles);
   const size_t esz = BF16 ? 2 : 4;
-  const float *Gf = G ? gauges + gauge_index(field, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
+  TileGauge<G, false> tg;
+  if constexpr (G != 0) tg.load(gauges + gauge_index(field, a.batch, a.heads) * D * G);
   dbl[threadIdx.x] = cgz::dbl8_entry(threadIdx.x);
   const uint8_t *src_f = (const uint8_t *)kv + (size_t)field * a.tcap * D * esz;
   auto rows = [&](int tile) { return (int)min((int64_t)TILE_T, a.nt - (int64_t)tile * TILE_T); };
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
     __syncthreads();
     if (tile + 1 < tend) pre.fetch(src_f + (size_t)(tb + TILE_T) * D * esz, rows(tile + 1));
     if constexpr (G != 0) {
-      gauge_tile<G, false>(xs, nrows, Gf);
+      tg.apply(xs, nrows);
       __syncthreads();
     }
     if (nrows & 3) {
@@ -155,7 +156,8 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
   const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * a.chunk_tiles;
   const int tend = min(a.tiles, tile0 + a.chunk_tiles);
   const size_t esz = BF16 ? 2 : 4;
-  const float *Gf = G ? gauges + gauge_index(field, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
+  TileGauge<G, true> tg;
+  if constexpr (G != 0) tg.load(gauges + gauge_index(field, a.batch, a.heads) * D * G);
   auto rows = [&](int tile) { return (int)min((int64_t)TILE_T, a.nt - (int64_t)tile * TILE_T); };
   auto codes = [&](int tile) {
     return (const uint4 *)(payload + (size_t)(field * (a.tcap / 4) + (a.t0 + (int64_t)tile * TILE_T) / 4) * 32 * 2 * R);
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
     }
     __syncthreads();
     if constexpr (G != 0) {
-      gauge_tile<G, true>(xs, nrows, Gf);
+      tg.apply(xs, nrows);
       __syncthreads();
     }
     const size_t off = (size_t)(field * a.tcap + tb) * D * esz;
