@@ -201,47 +201,45 @@ __device__ __forceinline__ void load_mfma_gauge(const float *__restrict__ Gf, Mf
   }
 }
 
-// Rows past nrows are computed from whatever the tile holds there and are
-// never stored by the callers.
+// Rows past nrows (up to the next 32-row boundary) are computed from
+// whatever the tile holds there and are never stored by the callers.
 template <int G>
 __device__ __forceinline__ void gauge_tile_mfma(float *xs, int nrows, const MfmaGaugeFrags<G> &f) {
   static_assert(G == 16 || G == 32, "matrix-core gauge handles g = 16 and 32");
   constexpr int KS = G / 4;
+  constexpr int TP = 2;  // 16-row blocks per pass: independent accumulation chains interleave
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, kr = lane >> 4, n = lane & 15;
-  for (int tb = 0; tb < TILE_T / 16 && 16 * tb < nrows; tb++) {
-    const float *arow = xs + (16 * tb + n) * PITCH + 32 * wave + kr;   // A[m = n][k = kr]
-    cg_f32x4_t acc[2];
-    if constexpr (G == 16) {
-      float a[2][KS];
+  for (int tb0 = 0; tb0 < TILE_T / 16 && 16 * tb0 < nrows; tb0 += TP) {
+    float a[TP][2][KS];   // A[m = n][k = 4s + kr] of row block tb0 + p, output block nb
+#pragma unroll
+    for (int p = 0; p < TP; p++) {
+      const float *arow = xs + (16 * (tb0 + p) + n) * PITCH + 32 * wave + kr;
 #pragma unroll
       for (int nb = 0; nb < 2; nb++)
 #pragma unroll
-        for (int s = 0; s < KS; s++) a[nb][s] = arow[16 * nb + 4 * s];
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) {
-        acc[nb] = cg_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
         for (int s = 0; s < KS; s++)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[nb][s], f.b[nb][s], acc[nb], 0, 0, 0);
-      }
-    } else {
-      float a[KS];  // both output blocks read the group's 32 inputs
-#pragma unroll
-      for (int s = 0; s < KS; s++) a[s] = arow[4 * s];
-#pragma unroll
-      for (int nb = 0; nb < 2; nb++) {
-        acc[nb] = cg_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < KS; s++)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], f.b[nb][s], acc[nb], 0, 0, 0);
-      }
+          a[p][nb][s] = G == 16 ? arow[16 * nb + 4 * s] : arow[4 * s];  // g = 32: both blocks read the group
     }
+    cg_f32x4_t acc[TP][2];
 #pragma unroll
-    for (int nb = 0; nb < 2; nb++)
+    for (int p = 0; p < TP; p++)
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        xs[(16 * tb + 4 * kr + j) * PITCH + 32 * wave + 16 * nb + n] = acc[nb][j];
+      for (int nb = 0; nb < 2; nb++) acc[p][nb] = cg_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+#pragma unroll
+      for (int p = 0; p < TP; p++)
+#pragma unroll
+        for (int nb = 0; nb < 2; nb++)
+          acc[p][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[p][nb][s], f.b[nb][s], acc[p][nb], 0, 0, 0);
+#pragma unroll
+    for (int p = 0; p < TP; p++)
+#pragma unroll
+      for (int nb = 0; nb < 2; nb++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          xs[(16 * (tb0 + p) + 4 * kr + j) * PITCH + 32 * wave + 16 * nb + n] = acc[p][nb][j];
   }
 }
 
