@@ -177,21 +177,34 @@ __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t
   for (int mt = 0; mt < 4; mt++) {
     acc[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int off = (16 * mt + (lane & 15)) * HP + 8 * (lane >> 4);
+  }
+  // k-step outermost: the eight accumulators advance together, so every
+  // instruction is eight issues away from the previous one on its accumulator
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-      const bf16x8_t ah = *(const bf16x8_t *)(sh + off + 32 * ks);
+  for (int ks = 0; ks < 4; ks++) {
+    bf16x8_t ah[4], al[4];
 #pragma unroll
-      for (int ntl = 0; ntl < 2; ntl++) {
-        acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
-        acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, f.lo[ntl][ks], acc[mt][ntl], 0, 0, 0);
-      }
-      if (!EXACT) {
-        const bf16x8_t al = *(const bf16x8_t *)(sl + off + 32 * ks);
+    for (int mt = 0; mt < 4; mt++) {
+      const int off = (16 * mt + (lane & 15)) * HP + 8 * (lane >> 4) + 32 * ks;
+      ah[mt] = *(const bf16x8_t *)(sh + off);
+      if (!EXACT) al[mt] = *(const bf16x8_t *)(sl + off);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int ntl = 0; ntl < 2; ntl++)
+        acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mt], f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int ntl = 0; ntl < 2; ntl++)
+        acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mt], f.lo[ntl][ks], acc[mt][ntl], 0, 0, 0);
+    if (!EXACT) {
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
 #pragma unroll
         for (int ntl = 0; ntl < 2; ntl++)
-          acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
-      }
+          acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mt], f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
     }
   }
   __syncthreads();  // every wave has read its operands: xs may overwrite them
