@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # reports null once the hash of those sources differs.
 PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "zfp_block.hpp", "zfp_kernels.hpp", "zfp_r4.hip",
                "kernels_zfp.hip")
-PMC_TRAFFIC = {"sha256": "52193d48f4a1fa91da7da46379eb9074d6a53c8b72f16af9fa26cada9a02c5d7",
+PMC_TRAFFIC = {"sha256": "b88e66d785258b6c4ab261930733f6784265e6859004377e53f3fc5a144f63cf",
                "k_zfp_encode": 5402382236, "k_zfp_decode": 5402639925,
                # SQ_INSTS_VALU per launch (rocprofv3 --pmc, same sources)
                "valu_k_zfp_encode": 1511943576, "valu_k_zfp_decode": 2086540296}

@@ -9,7 +9,7 @@ namespace cgk {
 
 constexpr int TILE_T = 64;  // tokens per workgroup tile of the rows kernels
 constexpr int ZFP128_CHUNK = 16;  // tiles per workgroup with the dense (g = 128) gauge
-constexpr int ZFP_CHUNK = 4;      // tiles per workgroup with the VALU gauges, given enough work
+constexpr int ZFP_CHUNK = 4;      // tiles per workgroup with the g <= 32 gauges, given enough work
 
 // tiles per workgroup of the VALU-gauge zfp kernels: ZFP_CHUNK when the call
 // still gives at least 8192 workgroups (8 per CU-slot), else 1

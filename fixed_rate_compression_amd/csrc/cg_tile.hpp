@@ -1,5 +1,6 @@
 // Device building blocks shared by the Codec-Gauge kernels: the LDS token
-// tile, storage-format conversion, and the VALU gauge (g <= 32).
+// tile, storage-format conversion, and the gauge for g <= 32 (matrix cores
+// for g = 16 and 32, VALU for g = 8; fmaf chains either way).
 //
 // Tile: TILE_T tokens x 128 channels of one field, held in LDS as fp32 with a
 // row pitch of 132 floats (the 4-float pad spreads the per-token rows of the
@@ -251,7 +252,7 @@ __device__ __forceinline__ void gauge_tile_mfma(float *xs, int nrows, const Mfma
 // matrix operand from an SGPR; lane = token row.
 template <int G, bool INV>
 __device__ __forceinline__ void gauge_tile(float *xs, int nrows, const float *__restrict__ Gf) {
-  static_assert(G == 8 || G == 16 || G == 32, "VALU gauge handles g = 8, 16 and 32");
+  static_assert(G == 8 || G == 16 || G == 32, "gauge_tile handles g = 8, 16 and 32");
   constexpr int NG = D / G;      // groups per head
   constexpr int GPW = NG / 4;    // groups per wave
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

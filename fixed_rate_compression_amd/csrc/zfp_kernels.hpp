@@ -7,8 +7,9 @@
 // 512 blocks, whose 16R-bit codes are one contiguous 1024R-byte span of the
 // stream.  A workgroup (256 threads) walks a chunk of consecutive tiles of one
 // field, loading tile i+1 into registers while it works on tile i:
-//   encode: coalesced tile load -> LDS (fp32) -> gauge in place (lane = token,
-//           wave-uniform group, SGPR matrix; or the MFMA routine for g = 128)
+//   encode: coalesced tile load -> LDS (fp32) -> gauge in place (TileGauge:
+//           matrix-core fmaf chains for g = 16/32, VALU for g = 8; the
+//           split-precision MFMA routine for g = 128)
 //           -> one block per thread-iteration (zfp_block.hpp, all in VGPRs)
 //           -> codes staged in LDS -> coalesced 16-byte stores of the span.
 //   decode: the mirror image; with a reference pointer the store also
@@ -58,7 +59,7 @@ __device__ __forceinline__ void unstage_block(const uint32_t *os, int b, uint64_
   }
 }
 
-// VALU gauges (g <= 32): a workgroup walks a.chunk_tiles consecutive tiles of
+// Gauges g <= 32: a workgroup walks a.chunk_tiles consecutive tiles of
 // one field and loads tile i+1 (KV rows, or code words) into registers while
 // it codes tile i.
 // A partial last block row (nrows % 4 != 0, only at the end of a field's
