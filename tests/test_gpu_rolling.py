@@ -111,21 +111,25 @@ def test_rolling_small_g32_rate4():
             check(rh, lambda f: raw[f], G, g, R, range(F))
 
 
-def test_rolling_decode_config_sampled():
+@pytest.mark.parametrize("every_token", [False, True])
+def test_rolling_decode_config_sampled(every_token):
     """Rolling-history workload: 64 sequences x 28 layers x 4 KV heads x 128,
-    history 8192 tokens (bf16), gauge g = 32, 4 b/v; 9 appends in
-    every-token mode (two block rows complete, one partial); sampled fields
-    checked against the oracle."""
+    history 8192 tokens (bf16), gauge g = 32, 4 b/v; 9 appends (two block
+    rows complete, one pending or partial), encoding each completed 4-token
+    block (the workload's mode) or every token; sampled fields checked
+    against the oracle."""
     import torch
     L, KV, B, H, T0, cap = 28, 2, 64, 4, 8192, 8448
     g, R = 32, 4
     raw = kv_gpu(4, L, KV, B, H, T0 + 16, cap, 0.95, 4, bf16=True)
     G = gauges_for(104, L, KV, H, g)
     gauge = cg.make_gauge(g, to_dev(np.ascontiguousarray(G)))
-    rh = RollingHistory(L, KV, B, H, cap, gauge, R)
+    rh = RollingHistory(L, KV, B, H, cap, gauge, R, every_token=every_token)
     rh.prefill(raw, T0)
     for k in range(9):
         rh.append(raw[:, T0 + k])
     F = n_fields(L, KV, B, H)
     fields = [0, 1234, F // 2 + 7, F - 1]
-    check_every_token(rh, lambda f: to_host(raw[f]), G, g, R, fields)
+    (check_every_token if every_token else check)(rh, lambda f: to_host(raw[f]), G, g, R, fields)
+    del rh, raw
+    torch.cuda.empty_cache()
