@@ -259,8 +259,9 @@ def small_lines(steps, warmup):
 
 
 def llama8b_lines(steps, warmup):
-    """Llama-3-8B-class cache at 3, 4 and 6 b/v with g = 16 (with the error
-    sums and the folded-recovery decodes), and 4 b/v with the other groups"""
+    """Llama-3-8B-class cache at 3, 4 and 6 b/v with g = 16 (zfp-style,
+    block-uniform and KIVI-style; with the error sums and the folded-recovery
+    decodes), and zfp-style 4 b/v with the other groups"""
     import torch
 
     from fixed_rate_compression_amd import binding as cg
@@ -272,6 +273,12 @@ def llama8b_lines(steps, warmup):
     for R in (3, 4, 6):
         lines.append(_codec_line(f"llama8b_zfp{R}", sh, x, G, 16, cg.make_codec(cg.CG_BACKEND_ZFP, R),
                                  steps, warmup, 2, "32 layers x K/V x 8 heads x 32768 tokens bf16, g=16"))
+    for bits in (3, 4, 6):
+        for codec, nm in ((cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, bits, 32), "bu"),
+                          (cg.make_codec(cg.CG_BACKEND_KIVI, bits, 32, 128), "kivi")):
+            lines.append(_codec_line(f"llama8b_{nm}{bits}", sh, x, G, 16, codec, steps, warmup, 2,
+                                     "32 layers x K/V x 8 heads x 32768 tokens bf16, g=16"
+                                     + (", 32-token blocks" if nm == "bu" else ", group 32, 128-token tail")))
     for g in (8, 32, 128):
         Gg, _ = _gauge(L, KV, H, g, 102 + g)
         lines.append(_codec_line(f"llama8b_zfp4_g{g}", sh, x, Gg, g, cg.make_codec(cg.CG_BACKEND_ZFP, 4),

@@ -77,7 +77,7 @@ int check_codec(const cg_codec *c, const cg_shape *s) {
       return CG_OK;
     case CG_BACKEND_BLOCK_UNIFORM:
       if (!cgq::bits_built(c->bits))
-        return fail(CG_E_UNSUPPORTED, "block-uniform bits %d not built (2,3,4,8)", c->bits);
+        return fail(CG_E_UNSUPPORTED, "block-uniform bits %d not built (2,3,4,6,8)", c->bits);
       if (!cgq::bu_block_built(c->block_tokens))
         return fail(CG_E_UNSUPPORTED, "block-uniform block_tokens %d not built (16,32,64)",
                     c->block_tokens);
@@ -86,7 +86,7 @@ int check_codec(const cg_codec *c, const cg_shape *s) {
       return CG_OK;
     case CG_BACKEND_KIVI:
       if (!cgq::bits_built(c->bits))
-        return fail(CG_E_UNSUPPORTED, "KIVI bits %d not built (2,3,4,8)", c->bits);
+        return fail(CG_E_UNSUPPORTED, "KIVI bits %d not built (2,3,4,6,8)", c->bits);
       if (c->block_tokens != 32) return fail(CG_E_UNSUPPORTED, "KIVI group must be 32");
       if (c->residual_tokens < 0 || c->residual_tokens > s->tokens ||
           (s->tokens - c->residual_tokens) % 32 || c->residual_tokens % 4)

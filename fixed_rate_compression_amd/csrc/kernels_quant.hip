@@ -11,7 +11,7 @@ hipError_t quant_launch_bits(bool encode, bool bf16, int g, int backend, const v
                              const float *gauges, void *dst, const void *meta_in, float *meta_out,
                              const QuantArgs &q, hipStream_t s);
 
-bool bits_built(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8; }
+bool bits_built(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 6 || bits == 8; }
 bool bu_block_built(int bt) { return bt == 16 || bt == 32 || bt == 64; }
 
 static hipError_t launch(bool encode, bool bf16, int g, const void *src, const float *gauges,
@@ -22,6 +22,7 @@ static hipError_t launch(bool encode, bool bf16, int g, const void *src, const f
     case 2: return quant_launch_bits<2>(encode, bf16, g, q.backend, src, gauges, dst, meta_in, meta_out, q, s);
     case 3: return quant_launch_bits<3>(encode, bf16, g, q.backend, src, gauges, dst, meta_in, meta_out, q, s);
     case 4: return quant_launch_bits<4>(encode, bf16, g, q.backend, src, gauges, dst, meta_in, meta_out, q, s);
+    case 6: return quant_launch_bits<6>(encode, bf16, g, q.backend, src, gauges, dst, meta_in, meta_out, q, s);
     case 8: return quant_launch_bits<8>(encode, bf16, g, q.backend, src, gauges, dst, meta_in, meta_out, q, s);
   }
   return hipErrorInvalidValue;

@@ -100,7 +100,7 @@ typedef struct cg_gauge {
 typedef struct cg_codec {
   int32_t backend;         /* CG_BACKEND_* */
   int32_t bits;            /* ZFP: bits per value R in {2,3,4,6,8};
-                              quantizers: code bits in {2,3,4,8} */
+                              quantizers: code bits in {2,3,4,6,8} */
   int32_t block_tokens;    /* BLOCK_UNIFORM: tokens per range block (T_b);
                               KIVI: group size (tokens per key range, channels
                               per value range) */

@@ -51,7 +51,7 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got.astype(np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
 @pytest.mark.parametrize("Bt", [16, 32, 64])
 @pytest.mark.parametrize("g", [0, 8, 16, 32])
 def test_block_uniform_bit_exact(bits, Bt, g):
@@ -100,7 +100,7 @@ def kivi_split(pay, meta, f, T, res, bits, esz):
     return pf[:Tq * D * bits // 8], pf[Tq * D * bits // 8:], mf
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6])
 @pytest.mark.parametrize("g", [0, 8, 16, 32])
 @pytest.mark.parametrize("bf16", [True, False])
 def test_kivi_bit_exact(bits, g, bf16):
@@ -146,6 +146,8 @@ def test_kivi_all_tail_and_constant_groups():
     (cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64, 0),
     (cg.CG_BACKEND_KIVI, 2, 32, 128),
     (cg.CG_BACKEND_KIVI, 4, 32, 128),
+    (cg.CG_BACKEND_KIVI, 6, 32, 128),
+    (cg.CG_BACKEND_BLOCK_UNIFORM, 6, 32, 0),
 ])
 def test_dense_gauge_staged(backend, bits, blk, res):
     L, KV, B, H, T = 1, 2, 1, 2, 1152 + 64 * 3    # more than one 16-tile chunk, ragged chunk

@@ -74,7 +74,7 @@ def test_tiny_range_does_not_overflow():
 
 
 @pytest.mark.parametrize("kind", [0, 1])
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6])
 def test_kivi_grouping_and_tail(kind, bits):
     T, d, group, residual = 192, 128, 32, 128
     x = synth.kv_field_cpu(3, kind, T, d, 0.95, 4)
