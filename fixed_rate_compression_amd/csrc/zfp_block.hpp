@@ -255,8 +255,10 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
       const uint32_t rest = w >> n;
       const int hb = 31 - clz32(w | 1u);
       const int e14 = hb < 14 ? hb : 14;
-      const int L = e14 - n + 1;          // scanned positions n..e14 (when rest != 0)
-      const uint32_t S = L > 0 ? (rest & ((1u << L) - 1u)) : 0u;
+      // scanned positions n..e14; when rest == 0 the count can be negative,
+      // but then the code below is replaced by the failed test
+      const int L = max(e14 - n + 1, 0);
+      const uint32_t S = rest & ((1u << L) - 1u);
       const uint32_t lo = S & 0xFFu, hi = S >> 8;
       const int pclo = __builtin_popcount(lo), pc = pclo + __builtin_popcount(hi);
       const uint32_t D = (uint32_t)dbl[lo] | ((uint32_t)dbl[hi] << (8 + pclo));

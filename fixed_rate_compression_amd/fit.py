@@ -109,6 +109,50 @@ class GaugeTrainer:
         g = self.g
         return cg.cg_gauge_from_skew(self.A.reshape(-1, g, g)).reshape(self.A.shape).astype(np.float32)
 
+    def save(self, path):
+        """Checkpoint of the training state (parameters, AdamW moments, step
+        count, settings, loss history) as an .npz file (no pickled objects)."""
+        np.savez(path, A=self.A, m=self.m, v=self.v, t=np.int64(self.t), g=np.int32(self.g),
+                 window=np.int64(self.Tw), history=np.asarray(self.history, np.float64),
+                 hyper=np.array([self.hyper[k] for k in _HYPER], np.float64),
+                 obj=np.array([self.obj[k] for k in _OBJ], np.float64))
+
+    def load(self, path):
+        """Resume from save(): the same cache shape, group and window are required."""
+        with np.load(path, allow_pickle=False) as z:
+            if int(z["g"]) != self.g or int(z["window"]) != self.Tw or z["A"].shape != self.A.shape:
+                raise ValueError("checkpoint does not match this trainer's shape, group or window")
+            self.A, self.m, self.v = (np.array(z[k], np.float64) for k in ("A", "m", "v"))
+            self.t = int(z["t"])
+            self.history = [float(h) for h in z["history"]]
+            self.hyper = dict(zip(_HYPER, (float(h) for h in z["hyper"])))
+            self.obj = dict(zip(_OBJ, (float(o) for o in z["obj"])))
+        return self
+
+
+_HYPER = ("lr", "beta1", "beta2", "eps", "weight_decay")
+_OBJ = ("T_b", "tau", "lambda_f", "lambda_r")
+
+
+def save_gauges(path, A: np.ndarray, g: int):
+    """A gauge set as a model-side file: the skew parameters A (fp64) and the
+    fp32 gauges G = exp(A - A^T) the kernels use, [L, KV, H, D/g, g, g] each."""
+    A = np.asarray(A, np.float64)
+    G = cg.cg_gauge_from_skew(A.reshape(-1, g, g)).reshape(A.shape).astype(np.float32)
+    np.savez(path, A=A, G=G, g=np.int32(g))
+
+
+def load_gauges(path):
+    """-> (A fp64, G fp32, g) from save_gauges; G is checked against exp(A - A^T)."""
+    with np.load(path, allow_pickle=False) as z:
+        A, G, g = np.array(z["A"], np.float64), np.array(z["G"], np.float32), int(z["g"])
+    if A.shape != G.shape or A.shape[-2:] != (g, g):
+        raise ValueError("gauge file: A and G shapes do not match the group size")
+    G_ref = cg.cg_gauge_from_skew(A.reshape(-1, g, g)).reshape(A.shape).astype(np.float32)
+    if not np.array_equal(G.view(np.uint32), G_ref.view(np.uint32)):
+        raise ValueError("gauge file: G is not exp(A - A^T) of the stored A")
+    return A, G, g
+
 
 def evaluate(x, L, KV, B, H, g, G, rates=(3, 4, 6), T_b=16, tau=0.04, lambda_f=1.0, lambda_r=0.02):
     """Spectral concentration 1 - L_freq of the gauged cache and the zfp-style

@@ -86,8 +86,55 @@ class RollingHistory:
             cg.cg_encode(sh, self.history, self.gauge, self.codec, b, t + 1 - b, self.payload)
             self._decode(sh, self.t)
             return
+        self.raw_row[:, t - b].copy_(token_kv)
         self.history[:, t].copy_(token_kv)
         if self.t % 4 == 0:
             cg.cg_encode(sh, self.history, self.gauge, self.codec, self.t - 4, 4, self.payload)
         enc = 4 * (self.t // 4)
         cg.cg_decode(sh, self.payload, None, self.gauge, self.codec, 0, enc, self.history)
+
+    # ------------------------------------------------------------------
+    # checkpoint / resume: the fixed-rate stream, the raw tokens of the
+    # current block row and the token count are the whole state; the history
+    # is rebuilt by decoding
+    # ------------------------------------------------------------------
+    def save(self, path):
+        """Write the history's state to an .npz file (no pickled objects)."""
+        import numpy as np
+        import torch
+        torch.cuda.synchronize()
+        raw = self.raw_row.cpu()
+        if raw.dtype == torch.bfloat16:
+            raw = raw.view(torch.int16)
+        np.savez(path, payload=self.payload.cpu().numpy(), raw_row=raw.numpy(), t=np.int64(self.t),
+                 dims=np.array(self.dims, np.int64), capacity=np.int64(self.capacity),
+                 rate=np.int32(self.codec.bits), dtype=np.int32(self.dtype),
+                 head_dim=np.int32(self.head_dim), every_token=np.int32(self.every_token),
+                 keep=np.int32(self.keep))
+
+    @classmethod
+    def restore(cls, path, gauge):
+        """Rebuild a history saved by save(); `gauge` is the model-side gauge
+        set it was built with (not part of the state)."""
+        import numpy as np
+        import torch
+        with np.load(path, allow_pickle=False) as z:
+            L, KV, B, H = (int(v) for v in z["dims"])
+            rh = cls(L, KV, B, H, int(z["capacity"]), gauge, int(z["rate"]), int(z["dtype"]),
+                     int(z["head_dim"]), bool(z["every_token"]), int(z["keep"]))
+            payload, raw, t = z["payload"], z["raw_row"], int(z["t"])
+        if payload.size != rh.payload.numel() or raw.shape != tuple(rh.raw_row.shape):
+            raise ValueError("saved state does not match the history's shape")
+        rh.payload.copy_(torch.from_numpy(payload))
+        raw_t = torch.from_numpy(raw)
+        rh.raw_row.copy_(raw_t.view(torch.bfloat16) if rh.raw_row.dtype == torch.bfloat16 else raw_t)
+        rh.t = t
+        if t:
+            b = 4 * (t // 4)
+            if rh.every_token:
+                rh._decode(rh.shape(t), t)
+            else:
+                if b:
+                    cg.cg_decode(rh.shape(t), rh.payload, None, rh.gauge, rh.codec, 0, b, rh.history)
+                rh.history[:, b:t].copy_(rh.raw_row[:, :t - b])
+        return rh

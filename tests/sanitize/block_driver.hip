@@ -1,0 +1,44 @@
+// Drives the HIP library's block coder (zfp_block.hpp, host build) over
+// random, special-value and corrupted blocks at every rate, for a build under
+// AddressSanitizer and UndefinedBehaviorSanitizer
+// (tests/test_oracle_sanitize.py).  Test harness only.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../fixed_rate_compression_amd/csrc/zfp_block.hpp"
+
+static uint64_t rs = 0x9E3779B97F4A7C15ull;
+static uint32_t rnd() { rs ^= rs << 13; rs ^= rs >> 7; rs ^= rs << 17; return (uint32_t)rs; }
+static float rndf() { return ((float)(rnd() & 0xFFFFFF) / 8388608.0f) - 1.0f; }
+
+template <int R>
+static void run(const uint16_t *dbl) {
+  constexpr int NA = cgz::Rate<R>::kAcc;
+  for (int it = 0; it < 2000; it++) {
+    float v[16], w[16];
+    for (int i = 0; i < 16; i++) {
+      const uint32_t k = rnd() % 64;
+      v[i] = k == 0 ? 0.0f : k == 1 ? -0.0f : k == 2 ? 1e-40f * rndf() : k == 3 ? 3e37f * rndf()
+                                                                                  : 50.0f * rndf();
+    }
+    if (it % 7 == 0) for (int i = 0; i < 16; i++) v[i] = v[0];     // constant block
+    uint64_t acc[NA];
+    cgz::encode_block<R>(v, acc, dbl);
+    cgz::decode_block<R>(acc, w);
+    for (int a = 0; a < NA; a++) acc[a] = ((uint64_t)rnd() << 32) | rnd();   // corrupted stream
+    constexpr int top = 16 * R - 64 * (NA - 1);
+    if (top < 64) acc[NA - 1] &= (1ull << top) - 1ull;               // bits past 16R are zero
+    cgz::decode_block<R>(acc, w);
+  }
+}
+
+int main() {
+  uint16_t *dbl = (uint16_t *)malloc(256 * sizeof(uint16_t));
+  for (int i = 0; i < 256; i++) dbl[i] = cgz::dbl8_entry((uint32_t)i);
+  run<1>(dbl); run<2>(dbl); run<3>(dbl); run<4>(dbl); run<5>(dbl); run<6>(dbl); run<7>(dbl);
+  run<8>(dbl); run<12>(dbl); run<16>(dbl);
+  free(dbl);
+  printf("block driver done\n");
+  return 0;
+}

@@ -73,3 +73,18 @@ def test_gauge_grad_matches_oracle_frechet(g, scale):
     for b in range(4):
         ref = linalg.grad_A_from_grad_G(A[b], dG[b])
         assert np.max(np.abs(got[b] - ref)) <= 1e-11 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_gauge_file_round_trip_and_check(tmp_path):
+    from fixed_rate_compression_amd import fit
+    rng = np.random.default_rng(3)
+    A = 0.1 * rng.standard_normal((2, 2, 3, 8, 16, 16))
+    fit.save_gauges(tmp_path / "g.npz", A, 16)
+    A2, G2, g = fit.load_gauges(tmp_path / "g.npz")
+    assert g == 16 and np.array_equal(A2, A) and G2.dtype == np.float32
+    assert np.array_equal(G2.reshape(-1, 16, 16), cg.cg_gauge_from_skew(A.reshape(-1, 16, 16)))
+    # a G that is not exp(A - A^T) of the stored A is refused
+    G2.reshape(-1)[5] += 1e-3
+    np.savez(tmp_path / "bad.npz", A=A, G=G2, g=np.int32(16))
+    with pytest.raises(ValueError):
+        fit.load_gauges(tmp_path / "bad.npz")

@@ -67,3 +67,24 @@ def test_training_lowers_the_objective():
     ident = fit.evaluate(held, L, KV, B, H, 16, fit.control_gauges("identity", L, KV, H, 16), rates=(4,))
     assert ident["L"] == pytest.approx(before["L"], rel=1e-12)
     assert ident["zfp4_nrmse"] == pytest.approx(before["zfp4_nrmse"], rel=1e-12)
+
+
+def test_trainer_checkpoint_resume_is_exact(tmp_path):
+    # the statistics and the update are deterministic, so training 2 epochs,
+    # saving, and resuming in a new trainer for 1 more epoch gives exactly
+    # the parameters of 3 uninterrupted epochs
+    L, KV, B, H, Tw, W = 1, 2, 1, 2, 512, 3
+    x = kv_gpu(620, L, KV, B, H, Tw * W, Tw * W, 0.95, 4, bf16=True)
+    ref = fit.GaugeTrainer(x, L, KV, B, H, 16, window=Tw, lr=1e-2)
+    ref.fit(epochs=3)
+    tr = fit.GaugeTrainer(x, L, KV, B, H, 16, window=Tw, lr=1e-2)
+    tr.fit(epochs=2)
+    tr.save(tmp_path / "trainer.npz")
+    tr2 = fit.GaugeTrainer(x, L, KV, B, H, 16, window=Tw).load(tmp_path / "trainer.npz")
+    assert tr2.hyper["lr"] == 1e-2 and tr2.t == 2 * W
+    tr2.fit(epochs=1)
+    assert np.array_equal(tr2.A, ref.A) and np.array_equal(tr2.m, ref.m) and np.array_equal(tr2.v, ref.v)
+    assert tr2.history == ref.history
+    other = fit.GaugeTrainer(x, L, KV, B, H, 8, window=Tw)
+    with pytest.raises(ValueError):
+        other.load(tmp_path / "trainer.npz")

@@ -133,3 +133,33 @@ def test_rolling_decode_config_sampled(every_token):
     (check_every_token if every_token else check)(rh, lambda f: to_host(raw[f]), G, g, R, fields)
     del rh, raw
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("every_token", [False, True])
+def test_rolling_checkpoint_resume_is_exact(tmp_path, every_token):
+    # save after 6 appends (a pending or partial block row), restore into a
+    # new history and continue: payload and history equal an uninterrupted run
+    import torch
+    L, KV, B, H, T0, steps, cap = 1, 2, 2, 2, 62, 13, 80
+    g, R = 16, 3
+    raw = kv_cpu(70 + every_token, L, KV, B, H, T0 + steps, cap, 0.95, 4, bf16=True)
+    rawd = to_dev(raw)
+    G = gauges_for(71, L, KV, H, g)
+    gauge = cg.make_gauge(g, to_dev(np.ascontiguousarray(G)))
+    ref = RollingHistory(L, KV, B, H, cap, gauge, R, every_token=every_token)
+    ref.prefill(rawd, T0)
+    for k in range(steps):
+        ref.append(rawd[:, T0 + k])
+    rh = RollingHistory(L, KV, B, H, cap, gauge, R, every_token=every_token)
+    rh.prefill(rawd, T0)
+    for k in range(6):
+        rh.append(rawd[:, T0 + k])
+    rh.save(tmp_path / "hist.npz")
+    del rh
+    rh2 = RollingHistory.restore(tmp_path / "hist.npz", gauge)
+    assert rh2.t == T0 + 6 and rh2.every_token == every_token
+    for k in range(6, steps):
+        rh2.append(rawd[:, T0 + k])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(rh2.payload), to_host(ref.payload))
+    assert np.array_equal(to_host(rh2.history), to_host(ref.history))
