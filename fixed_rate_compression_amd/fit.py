@@ -127,6 +127,7 @@ class GaugeTrainer:
             self.history = [float(h) for h in z["history"]]
             self.hyper = dict(zip(_HYPER, (float(h) for h in z["hyper"])))
             self.obj = dict(zip(_OBJ, (float(o) for o in z["obj"])))
+            self.obj["T_b"] = int(self.obj["T_b"])
         return self
 
 

@@ -62,15 +62,17 @@ class RollingHistory:
 
     def prefill(self, kv, T0):
         """Take rows [0, T0) of kv [fields, >=T0, d] as the initial history:
-        encode them once and decode them (T0 % 4 == 0 unless every_token)."""
-        assert self.every_token or T0 % 4 == 0
+        encode them once and decode them (completed-block mode: the rows of a
+        partial last block row stay raw)."""
         self.history[:, :T0].copy_(kv[:, :T0])
         b = 4 * (T0 // 4)
         self.raw_row[:, :T0 - b].copy_(kv[:, b:T0])
         self.t = T0
         sh = self.shape(T0)
-        cg.cg_encode(sh, self.history, self.gauge, self.codec, 0, T0, self.payload)
-        self._decode(sh, T0)
+        n = T0 if self.every_token else b
+        if n:
+            cg.cg_encode(sh, self.history, self.gauge, self.codec, 0, n, self.payload)
+            self._decode(sh, n)
 
     def append(self, token_kv):
         """One decoding step: token_kv [fields, d] is the new token."""
