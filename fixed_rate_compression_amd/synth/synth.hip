@@ -81,6 +81,7 @@ __global__ void k_generate(void *out, int64_t n_fields, int64_t Tcap, int64_t T,
     box_muller(r.z, r.w, e[2], e[3]);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
+      if (t + j >= T) break;                       // T need not be a multiple of 4
       y = (t + j == 0) ? e[j] : rho * y + cc * e[j];
       float v = sig * y;
       int64_t idx = (f * Tcap + t + j) * d + c;
@@ -98,7 +99,7 @@ extern "C" int cgsynth_generate(void *out, int64_t n_fields, int64_t Tcap, int64
                                 float rho, uint32_t seed, const int64_t *field_ids,
                                 const float *scales, int dtype, hipStream_t stream) {
   if (!out || !field_ids || !scales || n_fields <= 0 || d <= 0 || T < 0 || T > Tcap ||
-      (T % 4) != 0 || (dtype != 0 && dtype != 1))
+      (dtype != 0 && dtype != 1))
     return -1;
   int64_t threads = n_fields * d;
   int block = 256;

@@ -235,6 +235,43 @@ def test_llama8b_class_full_size_sampled_fields():
         assert np.array_equal(to_host(out[f]), y_ref), f
 
 
+def test_fields_past_4gib_offsets():
+    """Maximum-size addressing: two fields of 17,825,798 tokens (bf16, 4.56 GB
+    each, so row offsets inside a field pass 2^32 bytes and the second field
+    starts past them; the last block row is partial).  Sampled segments at
+    the start, across the 4 GiB point and at the end are checked bit-exactly
+    against the oracle, codes and decoded rows."""
+    import torch
+    L, KV, B, H = 1, 2, 1, 1
+    T = (1 << 24) + (1 << 20) + 6
+    Tcap = T + 2
+    R, g = 4, 16
+    x = kv_gpu(77, L, KV, B, H, T, Tcap, 0.95, 4, bf16=True)
+    G = gauges_for(78, L, KV, H, g)
+    shape = cg.make_shape(L, KV, B, H, T, Tcap, D, cg.CG_DTYPE_BF16)
+    codec = cg.make_codec(cg.CG_BACKEND_ZFP, R)
+    per = Tcap * D * R // 8
+    pay = empty_u8(2 * per)
+    out = torch.zeros_like(x)
+    gauge = cg.make_gauge(g, to_dev(G))
+    cg.cg_encode(shape, x, gauge, codec, 0, T, pay)
+    cg.cg_decode(shape, pay, None, gauge, codec, 0, T, out)
+    torch.cuda.synchronize()
+    r_end = (T - 70) // 4 * 4
+    for f in range(2):
+        Gf = gauge_of_field(G, f, KV, B, H)
+        for r0, n in ((0, 64), ((1 << 24) - 32, 96), (r_end, T - r_end)):
+            xs = to_host(x[f, r0:r0 + n])
+            n4 = (n + 3) // 4 * 4
+            p_ref, y_ref = zfp_oracle_field(xs, Gf, g, R, n, n4)
+            base = f * per + (r0 // 4) * 32 * 2 * R
+            assert np.array_equal(to_host(pay[base:base + n4 // 4 * 32 * 2 * R]), p_ref), (f, r0)
+            assert np.array_equal(to_host(out[f, r0:r0 + n]), y_ref), (f, r0)
+        assert not torch.any(out[f, T:].view(torch.int16) != 0)
+    del x, out, pay
+    torch.cuda.empty_cache()
+
+
 def test_27b_class_full_size_sampled_fields():
     """The 27B-class codec workload at full size: 46 layers x K/V x 16 KV heads
     x 65536 tokens, bf16, g = 16, 3 b/v (12.35 G values, 24.7 GB), in one
