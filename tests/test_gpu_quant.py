@@ -73,6 +73,44 @@ def test_block_uniform_bit_exact(bits, Bt, g):
         assert np.array_equal(out[f], oracle.f32_to_bf16(y)), f
 
 
+def test_block_uniform_past_4gib_offsets():
+    """Maximum-size addressing for the quantizers: two fields of 17,825,856
+    tokens (bf16, 4.56 GB each), block-uniform 4-bit, 64-token blocks,
+    g = 16.  Segments at the start, across the 4 GiB point and at the end are
+    checked bit-exactly against the oracle (codes, metadata, decoded rows)."""
+    t = torch()
+    L, KV, B, H = 1, 2, 1, 1
+    T = (1 << 24) + (1 << 20) + 64
+    bits, Bt, g = 4, 64, 16
+    x = kv_gpu(79, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    G = gauges_for(80, L, KV, H, g)
+    shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16)
+    codec = cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, bits, Bt)
+    pb, mb, _ = cg.cg_encoded_bytes(shape, codec)
+    pay = empty_u8(pb)
+    meta = t.zeros(mb // 4, dtype=t.float32, device="cuda")
+    out = t.zeros_like(x)
+    gauge = cg.make_gauge(g, to_dev(np.ascontiguousarray(G)))
+    cg.cg_encode(shape, x, gauge, codec, 0, T, pay, meta)
+    cg.cg_decode(shape, pay, meta, gauge, codec, 0, T, out)
+    t.cuda.synchronize()
+    per, nb = T * D * bits // 8, T // Bt
+    for f in range(2):
+        Gf = gauge_of_field(G, f, KV, B, H)
+        for r0, n in ((0, 128), ((1 << 24) - 64, 192), (T - 128, 128)):
+            xg = oracle.gauge_forward(oracle.to_f32(to_host(x[f, r0:r0 + n])), Gf, g)
+            p_ref, m_ref = oracle.bu_encode_field(xg, Bt, bits)
+            base = f * per + r0 * D * bits // 8
+            assert np.array_equal(to_host(pay[base:base + n * D * bits // 8]), p_ref), (f, r0)
+            mbase = 2 * (f * nb + r0 // Bt)
+            assert np.array_equal(to_host(meta[mbase:mbase + 2 * (n // Bt)]).view(np.uint32),
+                                  m_ref.reshape(-1).view(np.uint32)), (f, r0)
+            y = oracle.gauge_inverse(oracle.bu_decode_field(p_ref, m_ref, n, D, Bt, bits), Gf, g)
+            assert np.array_equal(to_host(out[f, r0:r0 + n]), oracle.f32_to_bf16(y)), (f, r0)
+    del x, out, pay, meta
+    t.cuda.empty_cache()
+
+
 def test_block_uniform_small_config_fp32_g16():
     # 1 layer x K/V x 2 heads x 4096 tokens, fp32, g = 16, 4-bit, 32-token blocks
     L, KV, B, H, T, bits, Bt = 1, 2, 1, 2, 4096, 4, 32
