@@ -8,7 +8,13 @@ at 20x per head), gauge g = 16 from A ~ N(0, 0.1^2), zfp-style fixed rate
 4 bits/value.  One step = gauge + encode of the whole cache followed by
 decode + inverse gauge of the whole cache; inputs are resident in HBM.
 
-Prints one JSON line (see the repository's design doc for the fields).
+Prints one JSON line: the metric, value (round-trip KV GB/s), timing, the
+configuration, per-direction figures, the roofline object of the slower
+kernel (algorithmic bytes per launch over its HIP-event time, against the
+8 TB/s HBM peak, with the rocprofv3-measured HBM traffic when the kernel
+sources match the ones the counters were taken on) and the CPU oracle
+baseline on a bounded sample.  --workload selects other workloads, one JSON
+line each.
 """
 from __future__ import annotations
 
@@ -33,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 # reports null once the hash of those sources differs.
 PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "zfp_block.hpp", "zfp_kernels.hpp", "zfp_r4.hip",
                "kernels_zfp.hip")
-PMC_TRAFFIC = {"sha256": "38dbeee8c8812353e8d5acf67cce12a28b9875a7b58396dfaa442b6387b71013",
+PMC_TRAFFIC = {"sha256": "32411f5d330ef6dcb1b149ee7a8ef3cd28e881637f83613e96a2e5482fbd1364",
                "k_zfp_encode": 5402387264, "k_zfp_decode": 5402640154,
                # SQ_INSTS_VALU per launch (rocprofv3 --pmc, same sources)
                "valu_k_zfp_encode": 1511943576, "valu_k_zfp_decode": 2086540296}
@@ -474,7 +480,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path shards "
-              "by field with no exchange; see DESIGN.md)", file=sys.stderr)
+              "by field with no exchange, so run one process per GPU on its own fields)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)

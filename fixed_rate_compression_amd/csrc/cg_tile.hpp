@@ -16,7 +16,7 @@
 
 namespace cgk {
 
-constexpr int D = 128;        // head_dim this build is specialized for
+constexpr int D = 128;        // head_dim the kernels are specialized for
 constexpr int PITCH = D + 4;  // LDS row pitch in floats
 constexpr int NT = 256;       // threads per workgroup (4 waves)
 

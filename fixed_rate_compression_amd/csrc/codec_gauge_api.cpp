@@ -44,7 +44,7 @@ int check_shape(const cg_shape *s) {
   if (s->dtype != CG_DTYPE_F32 && s->dtype != CG_DTYPE_BF16)
     return fail(CG_E_INVAL, "dtype %d is not CG_DTYPE_F32 or CG_DTYPE_BF16", s->dtype);
   if (s->head_dim != 128)
-    return fail(CG_E_UNSUPPORTED, "head_dim %d: this build supports head_dim 128", s->head_dim);
+    return fail(CG_E_UNSUPPORTED, "head_dim %d: the kernels are specialized for head_dim 128", s->head_dim);
   if (s->tokens < 0 || s->token_capacity < s->tokens)
     return fail(CG_E_SHAPE, "need 0 <= tokens (%lld) <= token_capacity (%lld)",
                 (long long)s->tokens, (long long)s->token_capacity);

@@ -84,7 +84,7 @@ typedef struct cg_shape {
   int32_t heads;          /* KV heads H >= 1 */
   int64_t tokens;         /* valid rows T, 0 <= T <= token_capacity */
   int64_t token_capacity; /* allocated rows per field */
-  int32_t head_dim;       /* d_l; this build supports 128 */
+  int32_t head_dim;       /* d_l; the library supports 128 */
   int32_t dtype;          /* CG_DTYPE_* storage format of the KV tensors */
 } cg_shape;
 

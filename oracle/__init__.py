@@ -15,9 +15,9 @@ Parts:
   * ``linalg.py``: fp64 matrix exponential and its Frechet derivative.
   * ``spectral.py``: fp64 token-channel DCT statistics and their gradient.
 
-Parity status of every function is listed in the design doc; all functions here
-are pinned by the ``-m "not gpu"`` tests (closed forms, library routines that
-are independent of this code, brute force, invariants).
+Every function here is pinned by the ``-m "not gpu"`` tests (closed forms,
+library routines that are independent of this code, brute force,
+invariants); none is unpinned.
 """
 from __future__ import annotations
 

@@ -4,7 +4,8 @@
 (arXiv HTML):
  - gauge-training paragraph: the gauge parameters are optimized with AdamW
    for 25 epochs over 64 windows of 4096 tokens (hyper-parameters of the
-   optimizer are not given; the readings are listed in DESIGN.md);
+   optimizer are not given; the usual AdamW defaults are used: lr 1e-3,
+   betas (0.9, 0.999), eps 1e-8, decoupled weight decay 1e-2);
  - main-grid and coordinate-control paragraphs: identity, random orthogonal
    gauges with the learned gauge's block structure, Hadamard, DCT and PCA/KLT
    controls, the last from the uncentered second-moment eigenbasis at the same

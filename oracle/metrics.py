@@ -4,7 +4,7 @@
 (arXiv HTML), evaluation-protocol paragraphs: cache-side metrics are the
 compressed bytes, actual bits/value, KV MSE, KV NRMSE, key and value NRMSE and
 the maximum absolute error, and the evaluator writes raw sums and counts.  The
-formulas are not on the page; the readings used (listed in the design doc):
+formulas are not on the page; the readings used:
   MSE   = sum (x_hat - x)^2 / N
   NRMSE = sqrt(sum (x_hat - x)^2 / sum x^2)   (over all, key or value fields)
   max   = max |x_hat - x|

@@ -23,8 +23,9 @@
  *    pages; the reading used here (exponent header, block-floating-point
  *    quantization, the 4-point decorrelating transform with matrix
  *    F = 1/16 [[4,4,4,4],[5,1,-1,-5],[-4,4,4,-4],[-2,6,-6,2]], total-sequency
- *    ordering, negabinary, group-tested embedded bit planes) is restated in
- *    the design doc and follows that published method's steps in order.
+ *    ordering, negabinary, group-tested embedded bit planes) follows that
+ *    published method's steps in order; the choices it leaves open are
+ *    stated where they are made below.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC.
  * FMA contraction is off so every multiply and add below rounds as written;

@@ -12,7 +12,8 @@ equations themselves are missing from the page; the readings used (DCT-II,
 r_uv = sqrt((u/(T_b-1))^2 + (v/(d-1))^2)/sqrt(2), per-block centroid
 averaged over blocks, rate = mean log(1 + U^2/tau^2) -- smooth in U and
 concave in the energy E = U^2, as the page's energy-preservation argument
-needs -- and L = lambda_f L_freq + lambda_r L_rate) are listed in the design doc.
+needs -- and L = lambda_f L_freq + lambda_r L_rate) are the plainest ones
+the surrounding text supports.
 
 Everything is fp64 and written as the plain definition: U = C_Tb X'_blk C_d^T
 with explicit DCT matrices, plain sums, and the gradient by the chain rule

@@ -3,8 +3,8 @@
 "Codec-Gauge" (arXiv HTML, evaluation-protocol paragraph): block-uniform
 uses one range per T_b x d_l block; the KIVI-style path uses per-channel key
 ranges and per-token value ranges; both use the same bit settings.  Group
-size 32 and a 128-token full-precision tail come from the KIVI-style workload
-this build measures.  Pins: brute-force optimal level, exact endpoints,
+size 32 and a 128-token full-precision tail are the full-head KIVI-style
+workload's settings.  Pins: brute-force optimal level, exact endpoints,
 half-step error bound, independent min/max grouping, LSB-first packing.
 """
 from fractions import Fraction

@@ -1,7 +1,8 @@
 """The C oracle and a host build of the library's block coder, run under
 AddressSanitizer and UndefinedBehaviorSanitizer over random, special-value
 and corrupted inputs with exactly sized buffers (out-of-bounds reads or
-writes, negative or oversized shifts and signed overflow abort the driver).
+writes, negative or oversized shifts and signed overflow abort the test
+program).
 Host code only: the GPU kernels are not built with a sanitizer."""
 import os
 import shutil

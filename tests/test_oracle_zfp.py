@@ -4,7 +4,7 @@ The Codec-Gauge pages ("Codec-Gauge", arXiv HTML, evaluation-protocol and
 results paragraphs) fix: FP32 input, a 2D field with n_x = d_l and
 n_y = numel/d_l, fixed rate, measured bits/value equal to the target
 (within 6e-5; 4.000 for zfp-4 in the serial run).  The block coder itself is
-the cited zfp method (Lindstrom 2014), restated in the design doc.  Pins below:
+the cited zfp method (Lindstrom 2014), restated in the oracle.  Pins below:
 a hand-derived worked example, the published transform matrix, textbook
 negabinary values, closed-form special blocks, the embedded-prefix property,
 exact byte counts and round-trip error behaviour.
