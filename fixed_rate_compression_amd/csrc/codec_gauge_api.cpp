@@ -37,6 +37,9 @@ int64_t n_fields(const cg_shape *s) {
   return (int64_t)s->layers * s->kv * s->batch * s->heads;
 }
 
+// device buffers are read and written with 16-byte vector accesses
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
 int check_shape(const cg_shape *s) {
   if (!s) return fail(CG_E_INVAL, "shape is NULL");
   if (s->layers < 1 || s->batch < 1 || s->heads < 1 || (s->kv != 1 && s->kv != 2))
@@ -58,6 +61,7 @@ int check_gauge(const cg_gauge *g, const cg_shape *s, const cg_codec *c) {
   if (g->group < 0 || s->head_dim % g->group)
     return fail(CG_E_SHAPE, "gauge group %d must divide head_dim %d", g->group, s->head_dim);
   if (!g->G) return fail(CG_E_INVAL, "gauge matrices are NULL");
+  if ((uintptr_t)g->G & 3u) return fail(CG_E_INVAL, "gauge matrices must be 4-byte aligned");
   const bool dense_ok = !c || c->backend == CG_BACKEND_ZFP || c->backend == CG_BACKEND_BLOCK_UNIFORM ||
                         c->backend == CG_BACKEND_KIVI;
   if (g->group == 8 || g->group == 16 || g->group == 32) return CG_OK;
@@ -406,6 +410,8 @@ int cg_encode(const cg_shape *shape, const void *kv, const cg_gauge *gauge, cons
   if ((rc = check_gauge(gauge, shape, codec))) return rc;
   if ((rc = check_rows(shape, codec, t0, nt))) return rc;
   if (!kv || !payload) return fail(CG_E_INVAL, "kv or payload is NULL");
+  if (misaligned(kv) || misaligned(payload) || misaligned(meta))
+    return fail(CG_E_INVAL, "kv, payload and meta must be 16-byte aligned");
   uint64_t need_p, need_m;
   byte_counts(shape, codec, &need_p, &need_m);
   if (payload_cap < need_p) return fail(CG_E_SIZE, "payload_cap %llu < %llu",
@@ -466,6 +472,8 @@ int decode_impl(const cg_shape *shape, const void *payload, uint64_t payload_cap
   if ((rc = check_gauge(gauge, shape, codec))) return rc;
   if ((rc = check_rows(shape, codec, t0, nt))) return rc;
   if (!kv_out || !payload) return fail(CG_E_INVAL, "kv_out or payload is NULL");
+  if (misaligned(kv_out) || misaligned(payload) || misaligned(meta) || misaligned(ref))
+    return fail(CG_E_INVAL, "kv_out, payload, meta and kv_ref must be 16-byte aligned");
   uint64_t need_p, need_m;
   byte_counts(shape, codec, &need_p, &need_m);
   if (payload_cap < need_p) return fail(CG_E_SIZE, "payload_cap %llu < %llu",
@@ -567,6 +575,8 @@ int cg_decode_error(const cg_shape *shape, const void *payload, uint64_t payload
   int rc = cg_decode_error_workspace_bytes(shape, gauge, codec, t0, nt, &need);
   if (rc) return rc;
   if (!kv_ref || !err) return fail(CG_E_INVAL, "kv_ref or err is NULL");
+  if (misaligned(workspace) || misaligned(err))
+    return fail(CG_E_INVAL, "workspace and err must be 16-byte aligned");
   if (need && (!workspace || ws_bytes < need))
     return fail(CG_E_SIZE, "workspace missing or smaller than %zu bytes", need);
   if (nt == 0) {  // no rows: every field's sums are zero (written by the reduce kernel)
@@ -626,6 +636,7 @@ int cg_gauge_apply(const cg_shape *shape, const void *kv, const cg_gauge *gauge,
   if ((rc = check_shape(shape))) return rc;
   if ((rc = check_gauge(gauge, shape, nullptr))) return rc;
   if (!kv || !out) return fail(CG_E_INVAL, "kv or out is NULL");
+  if (misaligned(kv) || misaligned(out)) return fail(CG_E_INVAL, "kv and out must be 16-byte aligned");
   if (direction != 0 && direction != 1) return fail(CG_E_INVAL, "direction must be 0 or 1");
   if (shape->tokens == 0) return CG_OK;
   const int64_t tiles = (shape->tokens + cgk::TILE_T - 1) / cgk::TILE_T;
@@ -660,6 +671,8 @@ int cg_gauge_heads(const cg_shape *shape, const cg_gauge *gauge, int32_t layer, 
   if (dtype != CG_DTYPE_F32 && dtype != CG_DTYPE_BF16) return fail(CG_E_INVAL, "bad dtype %d", dtype);
   if (rows == 0) return CG_OK;
   if (!x || !y) return fail(CG_E_INVAL, "x or y is NULL");
+  if ((((uintptr_t)x | (uintptr_t)y) & (dtype == CG_DTYPE_BF16 ? 1u : 3u)) != 0)
+    return fail(CG_E_INVAL, "x and y must be aligned to their element size");
   if ((rows + 63) / 64 >= ((int64_t)1 << 31)) return fail(CG_E_SHAPE, "too many rows");
   const int64_t esz = dtype == CG_DTYPE_BF16 ? 2 : 4, bytes = rows * q_heads * shape->head_dim * esz;
   const char *xb = (const char *)x, *yb = (const char *)y;

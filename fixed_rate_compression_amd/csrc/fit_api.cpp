@@ -212,6 +212,8 @@ int cg_second_moment(const cg_shape *shape, const void *kv, int32_t g, void *wor
   int rc = cg_second_moment_workspace_bytes(shape, g, &need);
   if (rc) return rc;
   if (!kv || !M_host) return fail(CG_E_INVAL, "kv or M is NULL");
+  if (((uintptr_t)kv | (uintptr_t)workspace) & 15u)
+    return fail(CG_E_INVAL, "kv and workspace must be 16-byte aligned");
   if (!workspace || ws_bytes < need) return fail(CG_E_SIZE, "workspace missing or too small");
   const int64_t F = n_fields(shape), E = 128 * (int64_t)g, ngauge = (int64_t)shape->layers * shape->kv * shape->heads;
   memset(M_host, 0, (size_t)ngauge * E * sizeof(double));

@@ -105,6 +105,8 @@ extern "C" int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t
   int rc = validate(shape, g, T_b);
   if (rc) return rc;
   if (!kv || !workspace || !out_host) return fail(CG_E_INVAL, "kv, workspace or out is NULL");
+  if (((uintptr_t)kv | (uintptr_t)workspace) & 15u)
+    return fail(CG_E_INVAL, "kv and workspace must be 16-byte aligned");
   if (g != 0 && !A_host) return fail(CG_E_INVAL, "A is NULL");
   if (!(tau > 0.0f)) return fail(CG_E_INVAL, "tau must be positive");
   const Layout L = layout(shape, g);

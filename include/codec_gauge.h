@@ -29,6 +29,10 @@
  *    device (hipMalloc or torch); host pointers are ordinary host memory.
  *    The library never allocates or frees caller-visible memory and keeps no
  *    state between calls (except the thread-local error string).
+ *  - Device buffers of KV rows, payloads, metadata, outputs, references and
+ *    workspaces must be 16-byte aligned (the kernels use 16-byte vector
+ *    accesses; torch allocations are); gauge matrices 4-byte aligned.
+ *    Otherwise CG_E_INVAL, before anything is enqueued.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Device work is
  *    enqueued asynchronously unless stated otherwise.
  *  - Every argument is validated on the host before anything is enqueued; on
@@ -57,7 +61,7 @@ extern "C" {
 
 /* return codes */
 #define CG_OK 0
-#define CG_E_INVAL (-1)       /* NULL pointer, bad enum, negative size */
+#define CG_E_INVAL (-1)       /* NULL or misaligned pointer, bad enum, negative size */
 #define CG_E_SHAPE (-2)       /* sizes not divisible / out of range */
 #define CG_E_UNSUPPORTED (-3) /* valid but not built (dtype/backend/bits/g combination) */
 #define CG_E_SIZE (-4)        /* a caller buffer or workspace is too small */

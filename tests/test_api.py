@@ -171,3 +171,31 @@ def test_decode_gauged_and_gauge_heads_validation():
     assert "overlap" in cg.cg_last_error()
     assert heads(0, 0, 8, 4, g=64) == cg.CG_E_UNSUPPORTED
     assert heads(0, 0, 8, 0) == cg.CG_OK               # no rows: nothing launched
+
+
+def test_misaligned_device_pointers_are_refused():
+    shape = cg.make_shape(1, 2, 1, 2, 64, 64, 128, cg.CG_DTYPE_BF16)
+    L = cg.lib()
+    codec = cg.make_codec(cg.CG_BACKEND_ZFP, 4)
+    ok, odd = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8)
+
+    def enc(kv, pay):
+        return L.cg_encode(ctypes.byref(shape), kv, ctypes.byref(cg.make_gauge(0)), ctypes.byref(codec),
+                           0, 64, pay, 1 << 30, None, 0, None)
+
+    def dec(pay, out):
+        return L.cg_decode(ctypes.byref(shape), pay, 1 << 30, None, 0, ctypes.byref(cg.make_gauge(0)),
+                           ctypes.byref(codec), 0, 64, out, None)
+
+    assert enc(odd, ok) == cg.CG_E_INVAL and "aligned" in cg.cg_last_error()
+    assert enc(ok, odd) == cg.CG_E_INVAL
+    assert dec(odd, ok) == cg.CG_E_INVAL
+    assert dec(ok, odd) == cg.CG_E_INVAL
+    G = np.zeros(64, np.float32)
+    bad_gauge = cg.CgGauge(16, ctypes.c_void_p(G.ctypes.data + 2))
+    assert L.cg_encode(ctypes.byref(shape), ok, ctypes.byref(bad_gauge), ctypes.byref(codec), 0, 64,
+                       ok, 1 << 30, None, 0, None) == cg.CG_E_INVAL
+    # the consumer-side gauge needs element alignment only
+    assert L.cg_gauge_heads(ctypes.byref(shape), ctypes.byref(cg.make_gauge(0)), 0, 0, 2, 1,
+                            cg.CG_DTYPE_F32, ctypes.c_void_p(4098), ctypes.c_void_p(1 << 40),
+                            None) == cg.CG_E_INVAL
