@@ -54,7 +54,7 @@ __device__ __forceinline__ void zero_rows(float *xs, int from) {
     *(float4 *)(xs + (from + (i >> 5)) * PITCH + (i & 31) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <bool BF16, int G>
+template <bool BF16, int G, bool GRAD>
 __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
                                                   const float *__restrict__ gauges,
                                                   const float *__restrict__ C128,
@@ -62,13 +62,15 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
                                                   const float *__restrict__ rtab,
                                                   double *__restrict__ part,
                                                   float *__restrict__ gpart, StatsArgs a) {
-  __shared__ float buf[2 * TILE_T * PITCH];  // gauged tile | raw tile; Gamma scratch at the end
-  __shared__ float cm[D * D];                // C128[v][c] at v*128 + ((c + rot(v)) & 127)
-  float *xs = buf, *xr = buf + TILE_T * PITCH;
+  // gauged tile (then the adjoint Z), and with the gradient the raw tile
+  __shared__ float buf[(GRAD ? 2 : 1) * TILE_T * PITCH];
+  __shared__ float blk[4][4][2];  // per wave, per block: partial sum E, sum r E
   __shared__ double red[4][3];
-  // 16x16 Gamma tiles per field; g = 8 groups are the 8x8 diagonal blocks of
-  // the g = 16 tiles
-  constexpr int NGT = G == 32 ? 16 : (G == 16 || G == 8 ? 8 : 0);
+  float *xs = buf, *xr = buf + TILE_T * PITCH;
+  // Gamma tiles of this wave: g = 16 (and g = 8, the 8x8 diagonal blocks of
+  // the g = 16 tiles): groups 2w, 2w + 1; g = 32: group w as 2 x 2 tiles
+  constexpr int NGW = G == 32 ? 4 : (G == 16 || G == 8 ? 2 : 0);
+  constexpr int NGT = 4 * NGW;    // tiles per field
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, lg = lane >> 4, lm = lane & 15;
   const int64_t f = (int64_t)blockIdx.x / a.chunks;
@@ -77,28 +79,32 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
   TileGauge<G, false> tg;
   if constexpr (G != 0) tg.load(gauges + gauge_index(f, a.batch, a.heads) * D * G);
 
-  for (int i = threadIdx.x; i < D * D; i += NT) {
-    const int v = i >> 7, c = i & 127;
-    cm[v * D + ((c + rot(v)) & 127)] = C128[i];
-  }
-  const int rA = rot(lm);  // rotation of rows 16 nt + lm
+  // wave w owns DCT columns v (forward) and channels c (adjoint) 32w .. 32w + 31
+  const int n0 = 32 * wave + lm;                  // + 16 nt
+  float bw[2][32], ba[2][GRAD ? 32 : 1];          // B operands of C128^T and C128
+#pragma unroll
+  for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+    for (int ks = 0; ks < 32; ks++) {
+      bw[nt][ks] = C128[(n0 + 16 * nt) * D + 4 * ks + lg];
+      if constexpr (GRAD) ba[nt][ks] = C128[(4 * ks + lg) * D + n0 + 16 * nt];
+    }
   float cB[4], cBt[4];  // C16 operand fragments (permuted summation index)
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     cB[s] = C16[lm * 16 + 4 * lg + s];
     cBt[s] = C16[(4 * lg + s) * 16 + lm];
   }
-  float rr[8][4];
+  float rr[2][4];
 #pragma unroll
-  for (int nt = 0; nt < 8; nt++)
+  for (int nt = 0; nt < 2; nt++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) rr[nt][i] = rtab[(4 * lg + i) * D + 16 * nt + lm];
+    for (int i = 0; i < 4; i++) rr[nt][i] = rtab[(4 * lg + i) * D + n0 + 16 * nt];
 
   double sLb = 0.0, sLog = 0.0, sE = 0.0;
-  f4 gacc[NGT > 0 ? NGT : 1];
+  f4 gacc[NGW > 0 ? NGW : 1];
 #pragma unroll
-  for (int q = 0; q < (NGT > 0 ? NGT : 1); q++) gacc[q] = f4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
+  for (int q = 0; q < (NGW > 0 ? NGW : 1); q++) gacc[q] = f4{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t tile = chunk * a.tiles_per_chunk;
        tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
@@ -106,115 +112,135 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
     const int nrows = (int)min((int64_t)TILE_T, a.tokens - tb);
     const uint8_t *src = (const uint8_t *)kv + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
     load_tile<BF16>(src, nrows, xs);
-    if (a.grad) load_tile<BF16>(src, nrows, xr);
+    if constexpr (GRAD) load_tile<BF16>(src, nrows, xr);
     if (nrows < TILE_T) {
       zero_rows(xs, nrows);
-      if (a.grad) zero_rows(xr, nrows);
+      if constexpr (GRAD) zero_rows(xr, nrows);
     }
     __syncthreads();
     if constexpr (G != 0) {
       tg.apply(xs, nrows);
       __syncthreads();
     }
-    const bool active = 16 * wave < nrows;
-    float *X = xs + 16 * wave * PITCH;
-    // channel DCT: Y = X' C128^T
-    f4 y[8];
+    // channel DCT of the four 16-row blocks: Y = X' C128^T (this wave's columns)
+    f4 y[4][2];
 #pragma unroll
-    for (int nt = 0; nt < 8; nt++) y[nt] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 4; mt++) y[mt][0] = y[mt][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
     for (int ks = 0; ks < 32; ks++) {
-      const float av = X[lm * PITCH + 4 * ks + lg];
-      const int col = (4 * ks + lg + rA) & 127;
+      float av[4];
 #pragma unroll
-      for (int nt = 0; nt < 8; nt++) y[nt] = mma(av, cm[(16 * nt + lm) * D + col], y[nt]);
+      for (int mt = 0; mt < 4; mt++) av[mt] = xs[(16 * mt + lm) * PITCH + 4 * ks + lg];
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) y[mt][nt] = mma(av[mt], bw[nt][ks], y[mt][nt]);
     }
-    // token DCT: U = C16 Y
-    f4 U[8];
+    // token DCT: U = C16 Y per block
+    f4 U[4][2];
 #pragma unroll
-    for (int nt = 0; nt < 8; nt++) {
-      U[nt] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-      for (int s = 0; s < 4; s++) U[nt] = mma(cB[s], y[nt][s], U[nt]);
-    }
-    float se = 0.f, sre = 0.f, slog = 0.f;
+      for (int nt = 0; nt < 2; nt++) {
+        U[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < 8; nt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float u = U[nt][i];
-        const float e = u * u;
-        se += e;
-        sre += rr[nt][i] * e;
-        // log2(1 + U^2/tau^2) with the hardware log2 (~1 ulp; the argument is
-        // >= 1, so no cancellation near 0 matters for the sum); times ln 2 below
-        slog += __builtin_amdgcn_logf(1.0f + e * a.inv_tau2);
+        for (int s = 0; s < 4; s++) U[mt][nt] = mma(cB[s], y[mt][nt][s], U[mt][nt]);
       }
-    se = wave_sum(se);
-    sre = wave_sum(sre);
-    slog = wave_sum(slog) * 0.693147180559945309f;
-    const float Lb = se > 0.f ? sre / se : 0.f;
-    if (active) {
-      sLb += (double)Lb;
-      sLog += (double)slog;
-      sE += (double)se;
-    }
-    if (a.grad) {
-      const float cf = se > 0.f ? a.lam_f_nb * 2.0f / se : 0.f;
+    float slog = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 8; nt++)
+    for (int mt = 0; mt < 4; mt++) {
+      float se = 0.f, sre = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 2; nt++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const float u = U[nt][i];
-          // d/dU of (lambda_r / N_c) log(1 + U^2/tau^2), with a ~1-ulp reciprocal
-          y[nt][i] = cf * u * (rr[nt][i] - Lb) + a.lam_r_nc * 2.0f * u * __builtin_amdgcn_rcpf(a.tau2 + u * u);
+          const float u = U[mt][nt][i];
+          const float e = u * u;
+          se += e;
+          sre += rr[nt][i] * e;
+          // log2(1 + U^2/tau^2) with the hardware log2 (~1 ulp; the argument is
+          // >= 1, so no cancellation near 0 matters for the sum); times ln 2 below
+          slog += __builtin_amdgcn_logf(1.0f + e * a.inv_tau2);
         }
-      // adjoint token DCT: Z = C16^T dU
-      f4 Z[8];
-#pragma unroll
-      for (int nt = 0; nt < 8; nt++) {
-        Z[nt] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; s++) Z[nt] = mma(cBt[s], y[nt][s], Z[nt]);
-      }
-      __syncthreads();  // every wave is done reading its X' rows
-#pragma unroll
-      for (int nt = 0; nt < 8; nt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) X[(4 * lg + i) * PITCH + 16 * nt + lm] = Z[nt][i];
-      __syncthreads();
-      // adjoint channel DCT: dX' = Z C128
-      f4 dX[8];
-#pragma unroll
-      for (int nt = 0; nt < 8; nt++) dX[nt] = f4{0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < 32; ks++) {
-        const float av = X[lm * PITCH + 4 * ks + lg];
-        const int row = 4 * ks + lg, r0 = rot(row);
-#pragma unroll
-        for (int nt = 0; nt < 8; nt++) dX[nt] = mma(av, cm[row * D + ((16 * nt + lm + r0) & 127)], dX[nt]);
-      }
-      // Gamma_r[i][k] += sum_t dX'[t][gi] x[t][gk] over this block's 16 rows
-      const float *Xr = xr + 16 * wave * PITCH;
-      if constexpr (G == 8 || G == 16) {
-#pragma unroll
-        for (int r = 0; r < 8; r++)
-#pragma unroll
-          for (int s = 0; s < 4; s++)
-            gacc[r] = mma(dX[r][s], Xr[(4 * lg + s) * PITCH + 16 * r + lm], gacc[r]);
-      } else if constexpr (G == 32) {
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-#pragma unroll
-          for (int ta = 0; ta < 2; ta++)
-#pragma unroll
-            for (int tb2 = 0; tb2 < 2; tb2++)
-#pragma unroll
-              for (int s = 0; s < 4; s++)
-                gacc[r * 4 + ta * 2 + tb2] =
-                    mma(dX[2 * r + ta][s], Xr[(4 * lg + s) * PITCH + 32 * r + 16 * tb2 + lm],
-                        gacc[r * 4 + ta * 2 + tb2]);
+      se = wave_sum(se);
+      sre = wave_sum(sre);
+      if (lane == 0) {
+        blk[wave][mt][0] = se;
+        blk[wave][mt][1] = sre;
       }
     }
-    __syncthreads();
+    sLog += (double)(wave_sum(slog) * 0.693147180559945309f);
+    __syncthreads();  // block partials visible; every wave is done reading X'
+    float Lb[4], seb[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+      const float se = ((blk[0][mt][0] + blk[1][mt][0]) + blk[2][mt][0]) + blk[3][mt][0];
+      const float sre = ((blk[0][mt][1] + blk[1][mt][1]) + blk[2][mt][1]) + blk[3][mt][1];
+      seb[mt] = se;
+      Lb[mt] = se > 0.f ? sre / se : 0.f;
+      if (wave == 0 && 16 * mt < nrows) {
+        sLb += (double)Lb[mt];
+        sE += (double)se;
+      }
+    }
+    if constexpr (GRAD) {
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        const float cf = seb[mt] > 0.f ? a.lam_f_nb * 2.0f / seb[mt] : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const float u = U[mt][nt][i];
+            // d/dU of (lambda_r / N_c) log(1 + U^2/tau^2), with a ~1-ulp reciprocal
+            y[mt][nt][i] = cf * u * (rr[nt][i] - Lb[mt]) +
+                           a.lam_r_nc * 2.0f * u * __builtin_amdgcn_rcpf(a.tau2 + u * u);
+          }
+      }
+      // adjoint token DCT: Z = C16^T dU, into the tile (this wave's columns)
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) {
+          f4 z = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; s++) z = mma(cBt[s], y[mt][nt][s], z);
+#pragma unroll
+          for (int i = 0; i < 4; i++) xs[(16 * mt + 4 * lg + i) * PITCH + n0 + 16 * nt] = z[i];
+        }
+      __syncthreads();
+      // adjoint channel DCT: dX' = Z C128 (this wave's channels)
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) U[mt][0] = U[mt][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 32; ks++) {
+        float av[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) av[mt] = xs[(16 * mt + lm) * PITCH + 4 * ks + lg];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+          for (int nt = 0; nt < 2; nt++) U[mt][nt] = mma(av[mt], ba[nt][ks], U[mt][nt]);
+      }
+      // Gamma_r[i][k] += sum_t dX'_t[r][i] x_t[r][k] over the tile's rows
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+          const float *xrow = xr + (16 * mt + 4 * lg + s) * PITCH + 32 * wave + lm;
+          if constexpr (G == 8 || G == 16) {
+#pragma unroll
+            for (int q = 0; q < 2; q++) gacc[q] = mma(U[mt][q][s], xrow[16 * q], gacc[q]);
+          } else if constexpr (G == 32) {
+#pragma unroll
+            for (int ta = 0; ta < 2; ta++)
+#pragma unroll
+              for (int tb2 = 0; tb2 < 2; tb2++)
+                gacc[ta * 2 + tb2] = mma(U[mt][ta][s], xrow[16 * tb2], gacc[ta * 2 + tb2]);
+          }
+        }
+    }
+    __syncthreads();  // the tile buffers are rewritten by the next tile
   }
 
   // partial sums of this chunk, in a fixed order
@@ -222,15 +248,6 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
     red[wave][0] = sLb;
     red[wave][1] = sLog;
     red[wave][2] = sE;
-  }
-  if constexpr (NGT > 0) {
-    if (a.grad) {
-      // wave w's Gamma tiles -> xs[w][tile][16][16]
-#pragma unroll
-      for (int q = 0; q < NGT; q++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) xs[wave * NGT * 256 + q * 256 + (4 * lg + i) * 16 + lm] = gacc[q][i];
-    }
   }
   __syncthreads();
   const int64_t slot = f * a.chunks + chunk;
@@ -246,13 +263,13 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
     part[slot * 4 + 2] = s2;
     part[slot * 4 + 3] = 0.0;
   }
-  if constexpr (NGT > 0) {
-    if (a.grad) {
-      for (int e = threadIdx.x; e < NGT * 256; e += NT) {
-        const float v = ((xs[e] + xs[NGT * 256 + e]) + xs[2 * NGT * 256 + e]) + xs[3 * NGT * 256 + e];
-        gpart[slot * (NGT * 256) + e] = v;
-      }
-    }
+  if constexpr (GRAD && NGW > 0) {
+    // tile q of the field: g = 16 / 8: group 2w + q; g = 32: group w, tile q
+    float *gp = gpart + slot * (NGT * 256) + wave * NGW * 256;
+#pragma unroll
+    for (int q = 0; q < NGW; q++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) gp[q * 256 + (4 * lg + i) * 16 + lm] = gacc[q][i];
   }
 }
 
@@ -280,10 +297,15 @@ hipError_t stats_launch(bool bf16, int g, const void *kv, const float *gauges, c
                         const float *C16, const float *rtab, double *part, float *gpart,
                         double *out, const StatsArgs &a, int64_t fields, hipStream_t s) {
   const dim3 grid((unsigned)(fields * a.chunks)), block(NT);
-#define CG_S(BF, GG)                                                                          \
-  if (bf16 == BF && g == GG)                                                                  \
-    hipLaunchKernelGGL((k_dct_stats<BF, GG>), grid, block, 0, s, kv, gauges, C128, C16, rtab, \
-                       part, gpart, a);
+#define CG_S(BF, GG)                                                                           \
+  if (bf16 == BF && g == GG) {                                                                 \
+    if (a.grad)                                                                                \
+      hipLaunchKernelGGL((k_dct_stats<BF, GG, true>), grid, block, 0, s, kv, gauges, C128, C16, \
+                         rtab, part, gpart, a);                                                \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_dct_stats<BF, GG, false>), grid, block, 0, s, kv, gauges, C128,     \
+                         C16, rtab, part, gpart, a);                                           \
+  }
   CG_S(true, 0) CG_S(true, 8) CG_S(true, 16) CG_S(true, 32)
   CG_S(false, 0) CG_S(false, 8) CG_S(false, 16) CG_S(false, 32)
 #undef CG_S
