@@ -8,29 +8,37 @@
 // The chain through G = exp(A - A^T) is finished on the host (Frechet
 // derivative, fp64).
 //
-// Both 128-point transforms are dense 16 x 128 x 128 contractions per block and
-// run on the matrix cores in fp32 (v_mfma_f32_16x16x4_f32: A lane l holds
-// row l%16, k-slot l/16; B lane l holds k-slot l/16, column l%16; D lane l
-// holds column l%16, rows 4(l/16)..+3).  The 128-point matrix sits in LDS
-// with row v rotated left by rot(v) = 16 (v & 3) + 4 ((v >> 2) & 3) columns,
-// which keeps both of its access patterns (row varying across lanes in the
-// forward transform, column varying in the adjoint) free of bank conflicts.  The 16-point token transforms, the
-// adjoint and the Gamma update use the same instruction with the summation
-// index permuted so that k-slot g at k-step s is row 4g + s: the B (or A)
-// operand is then exactly element s of the previous D fragment, with no
-// cross-lane data movement.  The 128-point matrix lives in LDS; the 16-point
-// one in VGPRs.
+// The gauge and the 128-point channel transform are one linear map per head,
+// X' C128^T = X M^T with M = C128 diag(G_r) (M[v][c] = sum_i C128[v][g r + i]
+// G_r[i][c - g r], formed once per workgroup in fp64 and rounded to fp32).  It
+// runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulate)
+// in split precision: M = M_hi + M_mid + M_lo, three bf16 parts that hold all
+// 24 significand bits of the fp32 value.  A bf16 input is exact in the A
+// operand, so X M^T takes three passes with exact products; an fp32 input is
+// split the same way and takes the six passes whose parts sum to at least
+// 2^-16 of the leading product.  The adjoint channel transform Z C128 splits
+// Z and C128 into hi + lo and takes three passes (only lo x lo dropped).
+// The 16-point token transforms, their adjoint and the Gamma update stay on
+// the fp32 matrix cores (v_mfma_f32_16x16x4_f32) with the summation index
+// permuted so that k-slot j at k-step s is row 4j + s: the B (or A) operand
+// is then element s of the previous D fragment, with no cross-lane moves.
+// Operand layouts: 16x16x32 A lane l holds row l%16, k = 8(l/16)..+7; B
+// column l%16, same k; 16x16x4 A row l%16, k-slot l/16; B k-slot l/16, column
+// l%16; both D: column l%16, rows 4(l/16)..+3.
 //
 // Workgroup: 4 waves over a chunk of 64-token tiles of one field; wave w owns
-// block w (rows 16w..16w+15) of each tile.  Per-chunk partial sums (fp64
-// scalars, fp32 Gamma) go to the workspace and are reduced in a fixed order
-// by k_stats_reduce, so results are deterministic.
+// DCT columns (forward) and channels (adjoint) 32w..32w+31 of all four 16-row
+// blocks of a tile, its operand fragments in VGPRs.  Per-block sums are
+// exchanged through LDS and added in a fixed wave order; per-chunk partial
+// sums (fp64 scalars, fp32 Gamma) go to the workspace and are reduced in a
+// fixed order by k_stats_reduce, so results are deterministic.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "cg_stats.hpp"
 #include "cg_tile.hpp"
+#include "gauge128.hpp"
 
 namespace cgs {
 
@@ -41,107 +49,260 @@ __device__ __forceinline__ f4 mma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+__device__ __forceinline__ f4 mma8(bf16x8_t a, bf16x8_t b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
   return v;
 }
 
-__device__ __forceinline__ int rot(int v) { return 16 * (v & 3) + 4 * ((v >> 2) & 3); }
-
-__device__ __forceinline__ void zero_rows(float *xs, int from) {
-  for (int i = threadIdx.x; i < (TILE_T - from) * 32; i += NT)
-    *(float4 *)(xs + (from + (i >> 5)) * PITCH + (i & 31) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-template <bool BF16, int G, bool GRAD>
-__global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
+// sum over the 64 lanes, wave-uniform: each 16-lane row is summed with DPP
+// (quad swaps, then row rotations by 4 and 8), the four row sums in row order
+__device__ __forceinline__ float wave_total(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
+  const int b = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
+
+// x = hi + mid + lo exactly (each part round-to-nearest-even bf16 of what the
+// previous parts leave; both remainders are exact in fp32)
+__device__ __forceinline__ void split3(float x, uint32_t &h, uint32_t &m, uint32_t &l) {
+  h = bf16_rne(x);
+  const float r = x - bf16lo(h);
+  m = bf16_rne(r);
+  l = bf16_rne(r - bf16lo(m));
+}
+
+constexpr int PL = TILE_T * HP;  // bf16 elements per LDS tile plane
+
+// B fragments of M = C128 diag(G_r) for this wave's DCT columns v, split in
+// three: mf[part][nt][ks] holds M[cw + 16nt + (l & 15)][32ks + 8(l >> 4) + e]
+template <int G, int NTL>
+__device__ __forceinline__ void fused_frags(const float *__restrict__ C128,
+                                            const float *__restrict__ Gf, int cw, int lane,
+                                            bf16x8_t (&mf)[3][NTL][4]) {
+#pragma unroll
+  for (int nt = 0; nt < NTL; nt++)
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      const int v = cw + 16 * nt + (lane & 15);
+      const int c0 = 32 * ks + 8 * (lane >> 4);
+      double m[8];
+      if constexpr (G == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) m[e] = (double)C128[v * D + c0 + e];
+      } else {
+        // channels c0 .. c0 + 7 lie in one gauge group (g is a multiple of 8)
+        const int base = c0 / G * G;
+        const float *gr = Gf + (size_t)(c0 / G) * G * G + (c0 - base);
+#pragma unroll
+        for (int e = 0; e < 8; e++) m[e] = 0.0;
+#pragma unroll 4
+        for (int i = 0; i < G; i++) {
+          const double cv = (double)C128[v * D + base + i];
+          const float4 g0 = *(const float4 *)(gr + i * G);
+          const float4 g1 = *(const float4 *)(gr + i * G + 4);
+          m[0] = fma(cv, (double)g0.x, m[0]);
+          m[1] = fma(cv, (double)g0.y, m[1]);
+          m[2] = fma(cv, (double)g0.z, m[2]);
+          m[3] = fma(cv, (double)g0.w, m[3]);
+          m[4] = fma(cv, (double)g1.x, m[4]);
+          m[5] = fma(cv, (double)g1.y, m[5]);
+          m[6] = fma(cv, (double)g1.z, m[6]);
+          m[7] = fma(cv, (double)g1.w, m[7]);
+        }
+      }
+      uint32_t h[8], md[8], l[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) split3((float)m[e], h[e], md[e], l[e]);
+      mf[0][nt][ks] = pack8(h);
+      mf[1][nt][ks] = pack8(md);
+      mf[2][nt][ks] = pack8(l);
+    }
+}
+
+// B fragments of the adjoint channel transform, B[k = v][n = c] = C128[v][c]
+// for this wave's channels c, split in two
+template <int NTL>
+__device__ __forceinline__ void adjoint_frags(const float *__restrict__ C128, int cw, int lane,
+                                              bf16x8_t (&cf)[2][NTL][4]) {
+#pragma unroll
+  for (int nt = 0; nt < NTL; nt++)
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      const int c = cw + 16 * nt + (lane & 15);
+      const int v0 = 32 * ks + 8 * (lane >> 4);
+      uint32_t h[8], l[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) split_bf16(C128[(v0 + e) * D + c], h[e], l[e]);
+      cf[0][nt][ks] = pack8(h);
+      cf[1][nt][ks] = pack8(l);
+    }
+}
+
+// One 64 x 128 tile of a storage-format array held in registers between its
+// global load and its LDS store, so that tile i + 1 is in flight while tile i
+// is processed.  Thread i holds the 16-B pieces i, i + NTH, ... (coalesced);
+// rows past nrows read as zero.
+template <bool BF16, int NTH>
+struct StatsFetch {
+  static constexpr int N = (BF16 ? 1024 : 2048) / NTH;
+  uint4 r[N];
+  __device__ __forceinline__ void fetch(const void *__restrict__ src, int nrows) {
+    const uint4 *s = (const uint4 *)src;
+#pragma unroll
+    for (int k = 0; k < N; k++) {
+      const int i = threadIdx.x + NTH * k;
+      const int row = BF16 ? (i >> 4) : (i >> 5);
+      r[k] = row < nrows ? s[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+};
+
+// the fetched tile -> bf16 planes of the LDS tile (a bf16 input is its own
+// single plane; fp32 values are split into hi, mid, lo planes)
+template <bool BF16, int NTH>
+__device__ __forceinline__ void put_planes(const StatsFetch<BF16, NTH> &tf, uint16_t *sx) {
+#pragma unroll
+  for (int k = 0; k < StatsFetch<BF16, NTH>::N; k++) {
+    const int i = threadIdx.x + NTH * k;
+    if constexpr (BF16) {
+      *(uint4 *)(sx + (i >> 4) * HP + 8 * (i & 15)) = tf.r[k];
+    } else {
+      const uint32_t w[4] = {tf.r[k].x, tf.r[k].y, tf.r[k].z, tf.r[k].w};
+      uint32_t h[4], m[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) split3(__uint_as_float(w[e]), h[e], m[e], l[e]);
+      const int off = (i >> 5) * HP + 4 * (i & 31);
+      *(uint2 *)(sx + off) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      *(uint2 *)(sx + PL + off) = make_uint2(m[0] | (m[1] << 16), m[2] | (m[3] << 16));
+      *(uint2 *)(sx + 2 * PL + off) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+    }
+  }
+}
+
+// raw value x[t][c] from the planes (hi + mid + lo is exact)
+template <bool BF16>
+__device__ __forceinline__ float raw_at(const uint16_t *sx, int off) {
+  if constexpr (BF16) return bf16lo(sx[off]);
+  else return (bf16lo(sx[off]) + bf16lo(sx[PL + off])) + bf16lo(sx[2 * PL + off]);
+}
+
+template <bool BF16, int G, bool GRAD, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void k_dct_stats(const void *__restrict__ kv,
                                                   const float *__restrict__ gauges,
                                                   const float *__restrict__ C128,
                                                   const float *__restrict__ C16,
                                                   const float *__restrict__ rtab,
                                                   double *__restrict__ part,
                                                   float *__restrict__ gpart, StatsArgs a) {
-  // gauged tile (then the adjoint Z), and with the gradient the raw tile
-  __shared__ float buf[(GRAD ? 2 : 1) * TILE_T * PITCH];
-  __shared__ float blk[4][4][2];  // per wave, per block: partial sum E, sum r E
-  __shared__ double red[4][3];
-  float *xs = buf, *xr = buf + TILE_T * PITCH;
-  // Gamma tiles of this wave: g = 16 (and g = 8, the 8x8 diagonal blocks of
-  // the g = 16 tiles): groups 2w, 2w + 1; g = 32: group w as 2 x 2 tiles
-  constexpr int NGW = G == 32 ? 4 : (G == 16 || G == 8 ? 2 : 0);
-  constexpr int NGT = 4 * NGW;    // tiles per field
+  constexpr int NTH = 64 * NW;      // threads
+  constexpr int NTL = 8 / NW;        // 16-wide column tiles per wave
+  constexpr int NX = BF16 ? 1 : 3;   // bf16 planes of the raw tile
+  __shared__ __align__(16) uint16_t sx[NX * PL];
+  __shared__ __align__(16) uint16_t sz[GRAD ? 2 * PL : 8];  // Z hi, lo (gradient)
+  __shared__ float blk[NW][4][2];  // per wave, per block: partial sum E, sum r E
+  __shared__ double red[NW][3];
+  // 16 x 16 Gamma tiles: g = 16 (and g = 8, the 8x8 diagonal blocks of the
+  // g = 16 tiles): one per group, 8 per field, a wave has those of its
+  // channel tiles; g = 32: four per group (2 x 2), 16 per field, a wave has
+  // the two column tiles of each of its channel tiles
+  constexpr int NGW = G == 32 ? 2 * NTL : (G == 16 || G == 8 ? NTL : 0);
+  constexpr int NGT = G == 32 ? 16 : (G == 16 || G == 8 ? 8 : 0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, lg = lane >> 4, lm = lane & 15;
   const int64_t f = (int64_t)blockIdx.x / a.chunks;
   const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
   const int64_t ntiles = (a.tokens + TILE_T - 1) / TILE_T;
-  TileGauge<G, false> tg;
-  if constexpr (G != 0) tg.load(gauges + gauge_index(f, a.batch, a.heads) * D * G);
+  const int64_t tile0 = chunk * a.tiles_per_chunk;
+  const int64_t tile1 = min(ntiles, tile0 + a.tiles_per_chunk);
+  const size_t esz = BF16 ? 2 : 4;
+  const uint8_t *fbase = (const uint8_t *)kv + (size_t)f * a.tcap * D * esz;
 
-  // wave w owns DCT columns v (forward) and channels c (adjoint) 32w .. 32w + 31
-  const int n0 = 32 * wave + lm;                  // + 16 nt
-  float bw[2][32], ba[2][GRAD ? 32 : 1];          // B operands of C128^T and C128
-#pragma unroll
-  for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-    for (int ks = 0; ks < 32; ks++) {
-      bw[nt][ks] = C128[(n0 + 16 * nt) * D + 4 * ks + lg];
-      if constexpr (GRAD) ba[nt][ks] = C128[(4 * ks + lg) * D + n0 + 16 * nt];
-    }
+  StatsFetch<BF16, NTH> tf;
+  if (tile0 < tile1)
+    tf.fetch(fbase + (size_t)tile0 * TILE_T * D * esz, (int)min((int64_t)TILE_T, a.tokens - tile0 * TILE_T));
+
+  // wave w owns DCT columns v (forward) and channels c (adjoint) cw .. cw + 16 NTL - 1
+  const int cw = 16 * NTL * wave;
+  const int n0 = cw + lm;  // + 16 nt
+  bf16x8_t mf[3][NTL][4];
+  fused_frags<G, NTL>(C128, G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr,
+                      cw, lane, mf);
+  bf16x8_t cf[2][NTL][GRAD ? 4 : 1];
+  if constexpr (GRAD) adjoint_frags<NTL>(C128, cw, lane, cf);
   float cB[4], cBt[4];  // C16 operand fragments (permuted summation index)
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     cB[s] = C16[lm * 16 + 4 * lg + s];
     cBt[s] = C16[(4 * lg + s) * 16 + lm];
   }
-  float rr[2][4];
+  float rr[NTL][4];
 #pragma unroll
-  for (int nt = 0; nt < 2; nt++)
+  for (int nt = 0; nt < NTL; nt++)
 #pragma unroll
     for (int i = 0; i < 4; i++) rr[nt][i] = rtab[(4 * lg + i) * D + n0 + 16 * nt];
 
-  double sLb = 0.0, sLog = 0.0, sE = 0.0;
+  double sLb = 0.0, sE = 0.0;
+  double sLog = 0.0;  // per lane, log2 units
+  const float lam2 = a.lam_r_nc * 2.0f;
   f4 gacc[NGW > 0 ? NGW : 1];
 #pragma unroll
   for (int q = 0; q < (NGW > 0 ? NGW : 1); q++) gacc[q] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t tile = chunk * a.tiles_per_chunk;
-       tile < min(ntiles, (chunk + 1) * a.tiles_per_chunk); tile++) {
-    const int64_t tb = tile * TILE_T;
-    const int nrows = (int)min((int64_t)TILE_T, a.tokens - tb);
-    const uint8_t *src = (const uint8_t *)kv + (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
-    load_tile<BF16>(src, nrows, xs);
-    if constexpr (GRAD) load_tile<BF16>(src, nrows, xr);
-    if (nrows < TILE_T) {
-      zero_rows(xs, nrows);
-      if constexpr (GRAD) zero_rows(xr, nrows);
-    }
+  for (int64_t tile = tile0; tile < tile1; tile++) {
+    const int nrows = (int)min((int64_t)TILE_T, a.tokens - tile * TILE_T);
+    put_planes<BF16, NTH>(tf, sx);  // rows past nrows were fetched as zero
     __syncthreads();
-    if constexpr (G != 0) {
-      tg.apply(xs, nrows);
-      __syncthreads();
-    }
-    // channel DCT of the four 16-row blocks: Y = X' C128^T (this wave's columns)
-    f4 y[4][2];
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++) y[mt][0] = y[mt][1] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 32; ks++) {
-      float av[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; mt++) av[mt] = xs[(16 * mt + lm) * PITCH + 4 * ks + lg];
-#pragma unroll
-      for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++) y[mt][nt] = mma(av[mt], bw[nt][ks], y[mt][nt]);
-    }
-    // token DCT: U = C16 Y per block
-    f4 U[4][2];
+    if (tile + 1 < tile1)
+      tf.fetch(fbase + (size_t)(tile + 1) * TILE_T * D * esz,
+               (int)min((int64_t)TILE_T, a.tokens - (tile + 1) * TILE_T));
+
+    // gauge + channel DCT of the four 16-row blocks: Y = X M^T (this wave's columns)
+    f4 y[4][NTL];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++) {
+      for (int nt = 0; nt < NTL; nt++) y[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      bf16x8_t ax[4][NX];
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int p = 0; p < NX; p++)
+          ax[mt][p] = *(const bf16x8_t *)(sx + p * PL + (16 * mt + lm) * HP + 32 * ks + 8 * lg);
+      // smallest parts first: (X, M) part pairs whose order sums to at most 2
+#pragma unroll
+      for (int ord = 2; ord >= 0; ord--)
+#pragma unroll
+        for (int p = 0; p < NX; p++) {
+          if (p > ord) continue;
+#pragma unroll
+          for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+            for (int nt = 0; nt < NTL; nt++)
+              y[mt][nt] = mma8(ax[mt][p], mf[ord - p][nt][ks], y[mt][nt]);
+        }
+    }
+    // token DCT: U = C16 Y per block
+    f4 U[4][NTL];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int nt = 0; nt < NTL; nt++) {
         U[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; s++) U[mt][nt] = mma(cB[s], y[mt][nt][s], U[mt][nt]);
@@ -151,31 +312,35 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
     for (int mt = 0; mt < 4; mt++) {
       float se = 0.f, sre = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 2; nt++)
+      for (int nt = 0; nt < NTL; nt++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const float u = U[mt][nt][i];
           const float e = u * u;
           se += e;
-          sre += rr[nt][i] * e;
+          sre = fmaf(rr[nt][i], e, sre);
           // log2(1 + U^2/tau^2) with the hardware log2 (~1 ulp; the argument is
-          // >= 1, so no cancellation near 0 matters for the sum); times ln 2 below
-          slog += __builtin_amdgcn_logf(1.0f + e * a.inv_tau2);
+          // >= 1, so no cancellation near 0 matters for the sum); times ln 2 at the end
+          slog += __builtin_amdgcn_logf(fmaf(e, a.inv_tau2, 1.0f));
         }
-      se = wave_sum(se);
-      sre = wave_sum(sre);
+      se = wave_total(se);
+      sre = wave_total(sre);
       if (lane == 0) {
         blk[wave][mt][0] = se;
         blk[wave][mt][1] = sre;
       }
     }
-    sLog += (double)(wave_sum(slog) * 0.693147180559945309f);
-    __syncthreads();  // block partials visible; every wave is done reading X'
+    sLog += (double)slog;
+    __syncthreads();  // block partials visible
     float Lb[4], seb[4];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
-      const float se = ((blk[0][mt][0] + blk[1][mt][0]) + blk[2][mt][0]) + blk[3][mt][0];
-      const float sre = ((blk[0][mt][1] + blk[1][mt][1]) + blk[2][mt][1]) + blk[3][mt][1];
+      float se = blk[0][mt][0], sre = blk[0][mt][1];
+#pragma unroll
+      for (int w = 1; w < NW; w++) {
+        se += blk[w][mt][0];
+        sre += blk[w][mt][1];
+      }
       seb[mt] = se;
       Lb[mt] = se > 0.f ? sre / se : 0.f;
       if (wave == 0 && 16 * mt < nrows) {
@@ -186,64 +351,86 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
     if constexpr (GRAD) {
 #pragma unroll
       for (int mt = 0; mt < 4; mt++) {
-        const float cf = seb[mt] > 0.f ? a.lam_f_nb * 2.0f / seb[mt] : 0.f;
+        const float cf0 = seb[mt] > 0.f ? a.lam_f_nb * 2.0f / seb[mt] : 0.f;
 #pragma unroll
-        for (int nt = 0; nt < 2; nt++)
+        for (int nt = 0; nt < NTL; nt++)
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const float u = U[mt][nt][i];
-            // d/dU of (lambda_r / N_c) log(1 + U^2/tau^2), with a ~1-ulp reciprocal
-            y[mt][nt][i] = cf * u * (rr[nt][i] - Lb[mt]) +
-                           a.lam_r_nc * 2.0f * u * __builtin_amdgcn_rcpf(a.tau2 + u * u);
+            // u (centroid term + d/dU-over-U of (lambda_r / N_c) log(1 + U^2/tau^2)),
+            // with a ~1-ulp reciprocal
+            y[mt][nt][i] = u * fmaf(cf0, rr[nt][i] - Lb[mt],
+                                    lam2 * __builtin_amdgcn_rcpf(fmaf(u, u, a.tau2)));
           }
       }
-      // adjoint token DCT: Z = C16^T dU, into the tile (this wave's columns)
+      // adjoint token DCT, transposed: Z^T = dU^T C16 puts four consecutive
+      // channels of one row in each lane; split hi + lo into the Z planes
 #pragma unroll
       for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-        for (int nt = 0; nt < 2; nt++) {
+        for (int nt = 0; nt < NTL; nt++) {
           f4 z = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 4; s++) z = mma(cBt[s], y[mt][nt][s], z);
-#pragma unroll
-          for (int i = 0; i < 4; i++) xs[(16 * mt + 4 * lg + i) * PITCH + n0 + 16 * nt] = z[i];
+          for (int s = 0; s < 4; s++) z = mma(y[mt][nt][s], cBt[s], z);
+          const uint32_t h0 = pack_bf16x2(z[0], z[1]), h1 = pack_bf16x2(z[2], z[3]);
+          const uint32_t l0 = pack_bf16x2(z[0] - bf16lo(h0), z[1] - bf16hi(h0));
+          const uint32_t l1 = pack_bf16x2(z[2] - bf16lo(h1), z[3] - bf16hi(h1));
+          const int off = (16 * mt + lm) * HP + cw + 16 * nt + 4 * lg;
+          *(uint2 *)(sz + off) = make_uint2(h0, h1);
+          *(uint2 *)(sz + PL + off) = make_uint2(l0, l1);
         }
       __syncthreads();
       // adjoint channel DCT: dX' = Z C128 (this wave's channels)
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++) U[mt][0] = U[mt][1] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-      for (int ks = 0; ks < 32; ks++) {
-        float av[4];
+        for (int nt = 0; nt < NTL; nt++) U[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++) av[mt] = xs[(16 * mt + lm) * PITCH + 4 * ks + lg];
+      for (int ks = 0; ks < 4; ks++) {
+        bf16x8_t zh[4], zl[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          const int off = (16 * mt + lm) * HP + 32 * ks + 8 * lg;
+          zh[mt] = *(const bf16x8_t *)(sz + off);
+          zl[mt] = *(const bf16x8_t *)(sz + PL + off);
+        }
 #pragma unroll
         for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-          for (int nt = 0; nt < 2; nt++) U[mt][nt] = mma(av[mt], ba[nt][ks], U[mt][nt]);
+          for (int nt = 0; nt < NTL; nt++) {
+            U[mt][nt] = mma8(zl[mt], cf[0][nt][ks], U[mt][nt]);
+            U[mt][nt] = mma8(zh[mt], cf[1][nt][ks], U[mt][nt]);
+            U[mt][nt] = mma8(zh[mt], cf[0][nt][ks], U[mt][nt]);
+          }
       }
       // Gamma_r[i][k] += sum_t dX'_t[r][i] x_t[r][k] over the tile's rows
 #pragma unroll
       for (int mt = 0; mt < 4; mt++)
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-          const float *xrow = xr + (16 * mt + 4 * lg + s) * PITCH + 32 * wave + lm;
+          const int row = (16 * mt + 4 * lg + s) * HP + lm;
           if constexpr (G == 8 || G == 16) {
+            // channel tile ta is group cw / 16 + ta
 #pragma unroll
-            for (int q = 0; q < 2; q++) gacc[q] = mma(U[mt][q][s], xrow[16 * q], gacc[q]);
+            for (int ta = 0; ta < NTL; ta++)
+              gacc[ta] = mma(U[mt][ta][s], raw_at<BF16>(sx, row + cw + 16 * ta), gacc[ta]);
           } else if constexpr (G == 32) {
+            // channel tiles of group cw / 32 (all of it when NTL = 2, half otherwise)
+            const int gb = cw / 32 * 32;
+            const float x0 = raw_at<BF16>(sx, row + gb), x1 = raw_at<BF16>(sx, row + gb + 16);
 #pragma unroll
-            for (int ta = 0; ta < 2; ta++)
-#pragma unroll
-              for (int tb2 = 0; tb2 < 2; tb2++)
-                gacc[ta * 2 + tb2] = mma(U[mt][ta][s], xrow[16 * tb2], gacc[ta * 2 + tb2]);
+            for (int ta = 0; ta < NTL; ta++) {
+              gacc[ta * 2 + 0] = mma(U[mt][ta][s], x0, gacc[ta * 2 + 0]);
+              gacc[ta * 2 + 1] = mma(U[mt][ta][s], x1, gacc[ta * 2 + 1]);
+            }
           }
         }
     }
-    __syncthreads();  // the tile buffers are rewritten by the next tile
+    __syncthreads();  // the tile planes are rewritten by the next tile
   }
 
   // partial sums of this chunk, in a fixed order
+  sLog = wave_sum(sLog) * 0.693147180559945309;
   if (lane == 0) {
     red[wave][0] = sLb;
     red[wave][1] = sLog;
@@ -253,7 +440,7 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
   const int64_t slot = f * a.chunks + chunk;
   if (threadIdx.x == 0) {
     double s0 = 0, s1 = 0, s2 = 0;
-    for (int w = 0; w < 4; w++) {
+    for (int w = 0; w < NW; w++) {
       s0 += red[w][0];
       s1 += red[w][1];
       s2 += red[w][2];
@@ -264,8 +451,10 @@ __global__ __launch_bounds__(NT) void k_dct_stats(const void *__restrict__ kv,
     part[slot * 4 + 3] = 0.0;
   }
   if constexpr (GRAD && NGW > 0) {
-    // tile q of the field: g = 16 / 8: group 2w + q; g = 32: group w, tile q
-    float *gp = gpart + slot * (NGT * 256) + wave * NGW * 256;
+    // the wave's tiles are contiguous in the field's list: g = 16 / 8 from
+    // group cw / 16; g = 32 from tile 2 (cw / 16) (group cw / 32, row tile
+    // (cw / 16) % 2, column tiles 0 and 1)
+    float *gp = gpart + slot * (NGT * 256) + (G == 32 ? 2 : 1) * (cw / 16) * 256;
 #pragma unroll
     for (int q = 0; q < NGW; q++)
 #pragma unroll
@@ -293,18 +482,26 @@ __global__ __launch_bounds__(NT) void k_stats_reduce(const double *__restrict__ 
     }
 }
 
+// waves per workgroup: with the gradient 8 (a wave owns 16 columns, which
+// halves its operand fragments to fit two waves per SIMD; the 8 waves share
+// one LDS tile); without it 4 (already two waves per SIMD at 4 per group,
+// and half as many per-block cross-lane sums per tile)
+constexpr int kWavesGrad = 8;
+constexpr int kWavesStats = 4;
+
 hipError_t stats_launch(bool bf16, int g, const void *kv, const float *gauges, const float *C128,
                         const float *C16, const float *rtab, double *part, float *gpart,
                         double *out, const StatsArgs &a, int64_t fields, hipStream_t s) {
   const dim3 grid((unsigned)(fields * a.chunks)), block(NT);
-#define CG_S(BF, GG)                                                                           \
-  if (bf16 == BF && g == GG) {                                                                 \
-    if (a.grad)                                                                                \
-      hipLaunchKernelGGL((k_dct_stats<BF, GG, true>), grid, block, 0, s, kv, gauges, C128, C16, \
-                         rtab, part, gpart, a);                                                \
-    else                                                                                       \
-      hipLaunchKernelGGL((k_dct_stats<BF, GG, false>), grid, block, 0, s, kv, gauges, C128,     \
-                         C16, rtab, part, gpart, a);                                           \
+#define CG_S(BF, GG)                                                                         \
+  if (bf16 == BF && g == GG) {                                                               \
+    if (a.grad)                                                                              \
+      hipLaunchKernelGGL((k_dct_stats<BF, GG, true, kWavesGrad>), grid, dim3(64 * kWavesGrad), \
+                         0, s, kv, gauges, C128, C16, rtab, part, gpart, a);                 \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_dct_stats<BF, GG, false, kWavesStats>), grid,                    \
+                         dim3(64 * kWavesStats), 0, s, kv, gauges, C128, C16, rtab, part,    \
+                         gpart, a);                                                          \
   }
   CG_S(true, 0) CG_S(true, 8) CG_S(true, 16) CG_S(true, 32)
   CG_S(false, 0) CG_S(false, 8) CG_S(false, 16) CG_S(false, 32)
