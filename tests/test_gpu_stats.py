@@ -83,3 +83,18 @@ def test_stats_27b_class_windows_sampled():
     for f in (0, F - 1):
         h, ls = f % H, f // (B * H)
         compare(stats, dA, to_host(x[f]), A[ls // KV, ls % KV, h], 16, f)
+
+
+@pytest.mark.parametrize("g", [8, 32])
+def test_stats_fp32_multi_chunk(g):
+    """fp32 input (every value split into three bf16 parts for the matrix
+    cores) over two workgroup chunks per field (64 tiles of 64 tokens each)
+    with a ragged last tile, statistics and dL/dA."""
+    L, KV, B, H, T = 1, 2, 1, 1, 64 * 64 + 64 * 2 + 48
+    x = kv_cpu(95 + g, L, KV, B, H, T, T, 0.95, 4, bf16=False)
+    A = synth.gauge_params(96 + g, L * KV * H * (D // g), g).reshape(L, KV, H, D // g, g, g)
+    shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_F32)
+    stats, dA = run_stats(to_dev(x), shape, A, g)
+    for f in range(n_fields(L, KV, B, H)):
+        h, ls = f % H, f // (B * H)
+        compare(stats, dA, x[f], A[ls // KV, ls % KV, h], g, f)
