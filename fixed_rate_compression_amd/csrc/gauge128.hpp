@@ -97,18 +97,18 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint3
 
 // One tile of a storage-format [rows][128] array held in registers between
 // its global load and its LDS store, so that a workgroup can fetch tile i+1
-// while the matrix cores work on tile i.  Thread i holds the 16-B pieces
-// i, i + NT, ... (coalesced); rows past nrows read as zero.
-template <bool BF16>
+// while the matrix cores work on tile i.  Thread i of the NTH threads holds
+// the 16-B pieces i, i + NTH, ... (coalesced); rows past nrows read as zero.
+template <bool BF16, int NTH = NT>
 struct TileFetch {
-  static constexpr int N = BF16 ? 4 : 8;   // 16-B pieces per thread
+  static constexpr int N = (BF16 ? TILE_T * D * 2 : TILE_T * D * 4) / 16 / NTH;  // pieces per thread
   uint4 r[N];
 
   __device__ __forceinline__ void fetch(const void *__restrict__ src, int nrows) {
     const uint4 *s = (const uint4 *)src;
 #pragma unroll
     for (int k = 0; k < N; k++) {
-      const int i = threadIdx.x + NT * k;
+      const int i = threadIdx.x + NTH * k;
       const int row = BF16 ? (i >> 4) : (i >> 5);
       r[k] = row < nrows ? s[i] : make_uint4(0u, 0u, 0u, 0u);
     }
@@ -118,7 +118,7 @@ struct TileFetch {
   __device__ __forceinline__ void put_f32(float *xs) const {
 #pragma unroll
     for (int k = 0; k < N; k++) {
-      const int i = threadIdx.x + NT * k;
+      const int i = threadIdx.x + NTH * k;
       if (BF16) {
         float *d = xs + (i >> 4) * PITCH + 8 * (i & 15);
         *(float4 *)d = make_float4(bf16lo(r[k].x), bf16hi(r[k].x), bf16lo(r[k].y), bf16hi(r[k].y));
@@ -133,7 +133,7 @@ struct TileFetch {
   __device__ __forceinline__ void put(uint16_t *sh, uint16_t *sl) const {
 #pragma unroll
     for (int k = 0; k < N; k++) {
-      const int i = threadIdx.x + NT * k;
+      const int i = threadIdx.x + NTH * k;
       if (BF16) {
         *(uint4 *)(sh + (i >> 4) * HP + 8 * (i & 15)) = r[k];
       } else {

@@ -152,31 +152,12 @@ __device__ __forceinline__ void adjoint_frags(const float *__restrict__ C128, in
     }
 }
 
-// One 64 x 128 tile of a storage-format array held in registers between its
-// global load and its LDS store, so that tile i + 1 is in flight while tile i
-// is processed.  Thread i holds the 16-B pieces i, i + NTH, ... (coalesced);
-// rows past nrows read as zero.
-template <bool BF16, int NTH>
-struct StatsFetch {
-  static constexpr int N = (BF16 ? 1024 : 2048) / NTH;
-  uint4 r[N];
-  __device__ __forceinline__ void fetch(const void *__restrict__ src, int nrows) {
-    const uint4 *s = (const uint4 *)src;
-#pragma unroll
-    for (int k = 0; k < N; k++) {
-      const int i = threadIdx.x + NTH * k;
-      const int row = BF16 ? (i >> 4) : (i >> 5);
-      r[k] = row < nrows ? s[i] : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-};
-
 // the fetched tile -> bf16 planes of the LDS tile (a bf16 input is its own
 // single plane; fp32 values are split into hi, mid, lo planes)
 template <bool BF16, int NTH>
-__device__ __forceinline__ void put_planes(const StatsFetch<BF16, NTH> &tf, uint16_t *sx) {
+__device__ __forceinline__ void put_planes(const TileFetch<BF16, NTH> &tf, uint16_t *sx) {
 #pragma unroll
-  for (int k = 0; k < StatsFetch<BF16, NTH>::N; k++) {
+  for (int k = 0; k < TileFetch<BF16, NTH>::N; k++) {
     const int i = threadIdx.x + NTH * k;
     if constexpr (BF16) {
       *(uint4 *)(sx + (i >> 4) * HP + 8 * (i & 15)) = tf.r[k];
@@ -231,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_dct_stats(const void *__restrict
   const size_t esz = BF16 ? 2 : 4;
   const uint8_t *fbase = (const uint8_t *)kv + (size_t)f * a.tcap * D * esz;
 
-  StatsFetch<BF16, NTH> tf;
+  TileFetch<BF16, NTH> tf;
   if (tile0 < tile1)
     tf.fetch(fbase + (size_t)tile0 * TILE_T * D * esz, (int)min((int64_t)TILE_T, a.tokens - tile0 * TILE_T));
 
