@@ -129,6 +129,15 @@ __host__ __device__ __forceinline__ int clz32(uint32_t x) {  // x != 0
   return __builtin_clz(x);
 }
 
+// number of significant bits of x (0 for x = 0)
+__host__ __device__ __forceinline__ int bitlen32(uint32_t x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return 32 - __clz((int)x);  // __clz(0) = 32
+#else
+  return x ? 32 - __builtin_clz(x) : 0;
+#endif
+}
+
 // Append `len` (<= 32) bits of `code` at bit `pos`; bits at or past 16R are
 // dropped.
 template <int R>
@@ -307,7 +316,7 @@ __host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Ra
   // a plane's group part never spans more than 2m+1 bits
   uint32_t E = ef < room ? ef : room;
   E = E < 2u * m + 2u ? E : 2u * m + 2u;                      // <= 32
-  const uint32_t below = E >= 32u ? ~0u : (1u << E) - 1u;
+  const uint32_t below = (uint32_t)~(~0ull << E);            // E <= 32
   uint32_t term = W & ~P & below;
   uint32_t y = 0u, bias = 1u;
   while (term) {                        // two newly significant coefficients per step
@@ -332,7 +341,7 @@ __host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Ra
   y = cap ? ycap : (fail ? y : ybud);
   const uint32_t used = cap ? m + (uint32_t)__builtin_popcount(ycap) : (fail ? ef + 1u : room);
   pos += (int)used;
-  n += y ? 32 - clz32(y) : 0;           // every index up to the last new one is now verbatim
+  n += bitlen32(y);                     // every index up to the last new one is now verbatim
   return y;
 }
 
