@@ -262,17 +262,16 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
     if (pos < LIMIT) {                  // (no early exit: keeps the loop unrollable)
       const uint32_t w = j < 16 ? (u[15 - j] >> 16) : (u[31 - j] & 0xFFFFu);
       const uint32_t rest = w >> n;
-      const int hb = 31 - clz32(w | 1u);
-      const int e14 = hb < 14 ? hb : 14;
-      // scanned positions n..e14; when rest == 0 the count can be negative,
-      // but then the code below is replaced by the failed test
-      const int L = max(e14 - n + 1, 0);
+      const int hb1 = 32 - clz32(w | 1u);   // highest set bit + 1 (1 when w <= 1)
+      // scanned positions n .. min(hb, 14); when rest == 0 the code below is
+      // replaced by the failed test
+      const int L = max(min(hb1, 15), n) - n;
       const uint32_t S = rest & ((1u << L) - 1u);
       const uint32_t lo = S & 0xFFu, hi = S >> 8;
       const int pclo = __builtin_popcount(lo), pc = pclo + __builtin_popcount(hi);
       const uint32_t D = (uint32_t)dbl[lo] | ((uint32_t)dbl[hi] << (8 + pclo));
       uint32_t code = 1u | (D << 1);
-      if (hb <= 14) code &= ~(1u << (L + pc));
+      if (hb1 <= 15) code &= ~(1u << (L + pc));
       int len = 1 + L + pc;
       if (rest == 0) {
         code = 0u;
@@ -281,7 +280,7 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
       const uint64_t full = (uint64_t)(w & ((1u << n) - 1u)) | ((uint64_t)code << n);
       put64<R>(acc, pos, full);
       pos += n + len;
-      n = rest ? hb + 1 : n;
+      n = rest ? hb1 : n;
     }
   }
   if (LIMIT % 64) acc[NA - 1] &= (~0ull) >> (64 - LIMIT % 64);
