@@ -37,12 +37,12 @@ HBM_PEAK_GBS = 8000.0
 # counters read for a plain device copy of the KV tensor (fetch x 2.0, write
 # x 1.0).  They hold only for the kernel sources they were taken on: bench.py
 # reports null once the hash of those sources differs.
-PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "zfp_block.hpp", "zfp_kernels.hpp", "zfp_r4.hip",
-               "kernels_zfp.hip")
-PMC_TRAFFIC = {"sha256": "32411f5d330ef6dcb1b149ee7a8ef3cd28e881637f83613e96a2e5482fbd1364",
-               "k_zfp_encode": 5402387264, "k_zfp_decode": 5402640154,
+PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "gauge128.hpp", "zfp_block.hpp", "zfp_kernels.hpp",
+               "zfp_r4.hip", "kernels_zfp.hip")
+PMC_TRAFFIC = {"sha256": "81431a66b5930a3559dc8e0606d68b5f8f7873e991117b0b8a35c90fbdd41288",
+               "k_zfp_encode": 5402502349, "k_zfp_decode": 5402640077,
                # SQ_INSTS_VALU per launch (rocprofv3 --pmc, same sources)
-               "valu_k_zfp_encode": 1511943576, "valu_k_zfp_decode": 2086540296}
+               "valu_k_zfp_encode": 1474195984, "valu_k_zfp_decode": 2036478252}
 
 CFG = dict(layers=32, kv=2, batch=1, heads=8, tokens=32768, head_dim=128, g=16, rate=4,
            rho=0.95, outliers=4, seed=2)
