@@ -326,7 +326,7 @@ __host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Ra
     term = rest ^ low2;
     bias += 2u;
   }
-  const uint32_t cnt = E - (uint32_t)__builtin_popcount(tests & below);  // bits scanned before E
+  const uint32_t cnt = (uint32_t)__builtin_popcount(below & ~tests);     // bits scanned before E
   // three ways the part ends, selected without branches (lanes diverge here):
   //  cap    the scan reaches coefficient 15, whose 1 is implicit;
   //  fail   a failed group test at ef;
@@ -367,7 +367,9 @@ __host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate
 #pragma unroll
   for (int j = 0; j < 32; j++) {
     uint32_t x = 0u;                    // plane word 31-j of the shifted words
-    if (j <= 31 - s && pos < LIMIT) {   // (no early exit: keeps the loop unrollable)
+    // planes past the last one (j > 31 - s) lie below bit s of the shifted
+    // words, which the final shift drops; the encoder codes them as zeros
+    if (pos < LIMIT) {                  // (no early exit: keeps the loop unrollable)
       x = window<R>(acc, pos) & ((1u << n) - 1u);   // verbatim bits (n <= 16)
       pos += n;
       const int n0 = n;
