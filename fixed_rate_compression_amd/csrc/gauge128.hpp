@@ -167,9 +167,14 @@ __device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j
 // takes its products in the order ks = 0..3, and within a ks hi*G_hi,
 // hi*G_lo, lo*G_hi, so results depend on the tile only.  Contains two
 // workgroup barriers; the caller has synchronized after writing sh/sl.
-template <bool EXACT>
+// AFFINE: the tile holds integer codes q and the result is written as
+// scale_r (q G)[r][n] + min_r cs[n], with (min_r, scale_r) = rowp[r] and
+// cs[n] the column sums of the matrix (the dequantized tile min + q scale
+// times the matrix, with the range applied after the product).
+template <bool EXACT, bool AFFINE = false>
 __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t *sl, float *xs,
-                                              const G128Frags &f) {
+                                              const G128Frags &f, const float2 *rowp = nullptr,
+                                              const float *cs = nullptr) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   f32x4_t acc[4][2];
@@ -208,17 +213,34 @@ __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t
     }
   }
   __syncthreads();  // every wave has read its operands: xs may overwrite them
+  if constexpr (AFFINE) {
+    const float c0 = cs[32 * wave + (lane & 15)], c1 = cs[32 * wave + 16 + (lane & 15)];
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-    for (int ntl = 0; ntl < 2; ntl++) {
-      const int n = 32 * wave + 16 * ntl + (lane & 15);
+    for (int mt = 0; mt < 4; mt++) {
       const int m0 = 16 * mt + 4 * (lane >> 4);
-      xs[(m0 + 0) * PITCH + n] = acc[mt][ntl].x;
-      xs[(m0 + 1) * PITCH + n] = acc[mt][ntl].y;
-      xs[(m0 + 2) * PITCH + n] = acc[mt][ntl].z;
-      xs[(m0 + 3) * PITCH + n] = acc[mt][ntl].w;
+      const float4 pa = *(const float4 *)(rowp + m0), pb = *(const float4 *)(rowp + m0 + 2);
+      const float mn[4] = {pa.x, pa.z, pb.x, pb.z}, sc[4] = {pa.y, pa.w, pb.y, pb.w};
+#pragma unroll
+      for (int ntl = 0; ntl < 2; ntl++) {
+        const int n = 32 * wave + 16 * ntl + (lane & 15);
+        const float c = ntl ? c1 : c0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) xs[(m0 + i) * PITCH + n] = fmaf(sc[i], acc[mt][ntl][i], mn[i] * c);
+      }
     }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int ntl = 0; ntl < 2; ntl++) {
+        const int n = 32 * wave + 16 * ntl + (lane & 15);
+        const int m0 = 16 * mt + 4 * (lane >> 4);
+        xs[(m0 + 0) * PITCH + n] = acc[mt][ntl].x;
+        xs[(m0 + 1) * PITCH + n] = acc[mt][ntl].y;
+        xs[(m0 + 2) * PITCH + n] = acc[mt][ntl].z;
+        xs[(m0 + 3) * PITCH + n] = acc[mt][ntl].w;
+      }
+  }
   __syncthreads();
 }
 

@@ -344,13 +344,25 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
                                                   const float *__restrict__ gauges,
                                                   void *__restrict__ out, QK a) {
   __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  // dense gauge: (min, step) of each tile row and the column sums of the
+  // inverse matrix, for the range applied after the product
+  __shared__ __align__(16) float2 rowp[G == 128 ? TILE_T : 1];
+  __shared__ float csum[G == 128 ? D : 1];
   float *xs = (float *)lds;
   const int64_t f = launch_field((int64_t)blockIdx.x / a.chunks, a.fsel, a.fstep, a.fbase);
   const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
-  if constexpr (G == 128) load_g128<true>(Gf, fr);
+  if constexpr (G == 128) {
+    load_g128<true>(Gf, fr);
+    // inverse matrix B[k][n] = G[k][n]: column sums in a fixed order
+    if (threadIdx.x < D) {
+      float c = 0.0f;
+      for (int k = 0; k < D; k++) c += Gf[k * D + threadIdx.x];
+      csum[threadIdx.x] = c;
+    }
+  }
   TileGauge<G, true> tg;
   if constexpr (G != 0 && G != 128) tg.load(Gf);
   const int BT = a.block;
@@ -375,18 +387,44 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
   for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
     const int nrows = tile_rows(a, tile);
-    float v[32];
-    if (t < nrows) {
+    if constexpr (G == 128) {
+      // block-uniform ranges are one per block: (min + q step) G = step (q G) + min colsum(G),
+      // and the codes (at most 8 bits) are exact bf16 values: two passes, no split
       uint32_t q[32];
-      unpack32<BITS>(wd, q);
+      if (t < nrows) {
+        unpack32<BITS>(wd, q);
+      } else {
 #pragma unroll
-      for (int k = 0; k < 32; k++) v[k] = dequant1(q[k], mn, sc);
+        for (int k = 0; k < 32; k++) q[k] = 0u;
+      }
+      uint16_t *sh = (uint16_t *)lds;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; k4++) {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          h[e] = (__float_as_uint((float)q[8 * k4 + 2 * e]) >> 16) |
+                 (__float_as_uint((float)q[8 * k4 + 2 * e + 1]) & 0xFFFF0000u);
+        *(uint4 *)(sh + t * HP + 32 * j + 8 * k4) = make_uint4(h[0], h[1], h[2], h[3]);
+      }
+      if (j == 0) rowp[t] = t < nrows ? make_float2(mn, sc) : make_float2(0.0f, 0.0f);
+      if (tile + 1 < tend) fetch(tile + 1);
+      __syncthreads();
+      gauge128_tile<true, true>(sh, sh, xs, fr, rowp, csum);
     } else {
+      float v[32];
+      if (t < nrows) {
+        uint32_t q[32];
+        unpack32<BITS>(wd, q);
 #pragma unroll
-      for (int k = 0; k < 32; k++) v[k] = 0.0f;
+        for (int k = 0; k < 32; k++) v[k] = dequant1(q[k], mn, sc);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 32; k++) v[k] = 0.0f;
+      }
+      if (tile + 1 < tend) fetch(tile + 1);
+      inverse_gauged_tile<G>(lds, t, j, v, nrows, tg, fr);
     }
-    if (tile + 1 < tend) fetch(tile + 1);
-    inverse_gauged_tile<G>(lds, t, j, v, nrows, tg, fr);
     const size_t off = (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
     if (a.ref)
       store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
