@@ -11,9 +11,11 @@ decode + inverse gauge of the whole cache; inputs are resident in HBM.
 Prints one JSON line: the metric, value (round-trip KV GB/s), timing, the
 configuration, per-direction figures, the roofline object of the slower
 kernel (algorithmic bytes per launch over its HIP-event time, against the
-8 TB/s HBM peak, with the rocprofv3-measured HBM traffic when the kernel
-sources match the ones the counters were taken on) and the CPU oracle
-baseline on a bounded sample.  --workload selects other workloads, one JSON
+8 TB/s HBM peak, with the rocprofv3-measured HBM traffic and VALU
+instruction count when the kernel sources match the ones the counters were
+taken on; the instruction rate is also given as a fraction of the chip's
+single-issue VALU rate, the resource these coders are bound by) and the CPU
+oracle baseline on a bounded sample.  --workload selects other workloads, one JSON
 line each.
 """
 from __future__ import annotations
@@ -31,6 +33,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV GB/s for gauge+encode and decode+inverse at 4 bits/value; % of HBM peak"
 HBM_PEAK_GBS = 8000.0
+# single-issue VALU rate of the chip: 256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles
+# per wave64 instruction = 614.4 G wave-instructions/s (gfx950 can pair two
+# VALU instructions in one quad-cycle, so a kernel can exceed it)
+VALU_ISSUE_PEAK_GPS = 256 * 4 * 2.4 / 4
 
 # HBM bytes per launch of the fused zfp kernels on this workload, from two
 # rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by what the same
@@ -39,8 +45,8 @@ HBM_PEAK_GBS = 8000.0
 # reports null once the hash of those sources differs.
 PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "gauge128.hpp", "zfp_block.hpp", "zfp_kernels.hpp",
                "zfp_r4.hip", "kernels_zfp.hip")
-PMC_TRAFFIC = {"sha256": "b55337698b2e53cd607bc3b3ecbde46b05affc884977cd43b680bdb34a9ad2ef",
-               "k_zfp_encode": 5402492314, "k_zfp_decode": 5402647040,
+PMC_TRAFFIC = {"sha256": "a2d7008c60ff0d14b4f6b501d0e5fc7e0f6a0e286e92a80ec5416b6badc70fde",
+               "k_zfp_encode": 5402493440, "k_zfp_decode": 5402647936,
                # SQ_INSTS_VALU per launch (rocprofv3 --pmc, same sources)
                "valu_k_zfp_encode": 1474195984, "valu_k_zfp_decode": 1958951029}
 
@@ -538,6 +544,8 @@ def main():
                      "traffic": measured_traffic(f"k_zfp_{dom}"),
                      "valu_instr_per_launch": valu_rate(f"k_zfp_{dom}", t_dom)[0],
                      "valu_ginstr_per_s": valu_rate(f"k_zfp_{dom}", t_dom)[1],
+                     "valu_issue_frac": (round(valu_rate(f"k_zfp_{dom}", t_dom)[1] / VALU_ISSUE_PEAK_GPS, 4)
+                                         if valu_rate(f"k_zfp_{dom}", t_dom)[1] else None),
                      "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu_baseline:
