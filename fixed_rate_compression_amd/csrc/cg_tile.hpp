@@ -1,6 +1,6 @@
 // Device building blocks shared by the Codec-Gauge kernels: the LDS token
-// tile, storage-format conversion, and the gauge for g <= 32 (matrix cores
-// for g = 16 and 32, VALU for g = 8; fmaf chains either way).
+// tile, storage-format conversion, and the fmaf-chain gauge (matrix cores for
+// g = 16, 32 and, with fp32 storage, 128; VALU for g = 8).
 //
 // Tile: TILE_T tokens x 128 channels of one field, held in LDS as fp32 with a
 // row pitch of 132 floats (the 4-float pad spreads the per-token rows of the
@@ -167,17 +167,18 @@ __device__ __forceinline__ void write_err(ErrAcc e, double *__restrict__ epart) 
 
 typedef float cg_f32x4_t __attribute__((ext_vector_type(4)));
 
-// Matrix-core form of the gauge for g = 16 and 32, in place on the tile.
-// v_mfma_f32_16x16x4f32 adds its four products to the accumulator as a
-// chain of fused multiply-adds in k order (checked bit for bit on gfx950
+// Matrix-core form of the gauge for g = 16, 32 and 128, in place on the
+// tile.  v_mfma_f32_16x16x4f32 adds its four products to the accumulator as
+// a chain of fused multiply-adds in k order (checked bit for bit on gfx950
 // against fmaf chains, over normal, wide-exponent, cancelling and subnormal
 // operands), so g/4 of them in k order give exactly the fmaf chain over the
 // group's inputs in index order from +0 that the VALU form computes.
 // Operand layout: A[m][k] in lane m + 16k, B[k][n] in lane n + 16k, D[m][n]
 // in lane n + 16 (m / 4), element m % 4.  Wave w owns channels
-// [32w, 32w + 32) (two groups of 16, or one of 32) for all rows; one 16-row
-// x 16-channel output block takes g/4 instructions.  The B operands of a
-// wave depend only on the field, so they are loaded once per workgroup.
+// [32w, 32w + 32) (two groups of 16, one of 32, or a quarter of the full-head
+// group) for all rows; one 16-row x 16-channel output block takes g/4
+// instructions.  The B operands of a wave depend only on the field, so they
+// are loaded once per workgroup (g = 128: 64 floats per lane).
 template <int G>
 struct MfmaGaugeFrags {
   static constexpr int KS = G / 4;  // instructions per output block
@@ -204,24 +205,28 @@ __device__ __forceinline__ void load_mfma_gauge(const float *__restrict__ Gf, Mf
 
 // Rows past nrows (up to the next 32-row boundary) are computed from
 // whatever the tile holds there and are never stored by the callers.
+// g = 128: every wave reads all 128 channels of the rows it updates, so the
+// waves meet at a workgroup barrier between reading a row pair's operands and
+// writing its results (the trip count depends on nrows only: uniform).
 template <int G>
 __device__ __forceinline__ void gauge_tile_mfma(float *xs, int nrows, const MfmaGaugeFrags<G> &f) {
-  static_assert(G == 16 || G == 32, "matrix-core gauge handles g = 16 and 32");
+  static_assert(G == 16 || G == 32 || G == 128, "matrix-core gauge handles g = 16, 32 and 128");
   constexpr int KS = G / 4;
   constexpr int TP = 2;  // 16-row blocks per pass: independent accumulation chains interleave
+  constexpr int NA = G == 16 ? 2 : 1;  // A operand sets per row block (g >= 32: shared by both blocks)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, kr = lane >> 4, n = lane & 15;
   for (int tb0 = 0; tb0 < TILE_T / 16 && 16 * tb0 < nrows; tb0 += TP) {
-    float a[TP][2][KS];   // A[m = n][k = 4s + kr] of row block tb0 + p, output block nb
+    float a[TP][NA][KS];  // A[m = n][k = 4s + kr] of row block tb0 + p (g = 16: output block nb)
 #pragma unroll
     for (int p = 0; p < TP; p++) {
-      const float *arow = xs + (16 * (tb0 + p) + n) * PITCH + 32 * wave + kr;
+      const float *arow = xs + (16 * (tb0 + p) + n) * PITCH + (G == 128 ? 0 : 32 * wave) + kr;
 #pragma unroll
-      for (int nb = 0; nb < 2; nb++)
+      for (int nb = 0; nb < NA; nb++)
 #pragma unroll
-        for (int s = 0; s < KS; s++)
-          a[p][nb][s] = G == 16 ? arow[16 * nb + 4 * s] : arow[4 * s];  // g = 32: both blocks read the group
+        for (int s = 0; s < KS; s++) a[p][nb][s] = arow[16 * nb + 4 * s];
     }
+    if constexpr (G == 128) __syncthreads();  // all waves hold the rows' operands
     cg_f32x4_t acc[TP][2];
 #pragma unroll
     for (int p = 0; p < TP; p++)
@@ -233,7 +238,8 @@ __device__ __forceinline__ void gauge_tile_mfma(float *xs, int nrows, const Mfma
       for (int p = 0; p < TP; p++)
 #pragma unroll
         for (int nb = 0; nb < 2; nb++)
-          acc[p][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[p][nb][s], f.b[nb][s], acc[p][nb], 0, 0, 0);
+          acc[p][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[p][NA == 2 ? nb : 0][s], f.b[nb][s],
+                                                             acc[p][nb], 0, 0, 0);
 #pragma unroll
     for (int p = 0; p < TP; p++)
 #pragma unroll
@@ -282,13 +288,13 @@ __device__ __forceinline__ void gauge_tile(float *xs, int nrows, const float *__
   }
 }
 
-// The gauge of one field for every tile a workgroup processes: g = 16 and
-// 32 on the matrix cores (operands loaded once), g = 8 on the VALU, g = 0
-// (identity) nothing.  Same results in every case: fmaf chains in index
+// The gauge of one field for every tile a workgroup processes: g = 16, 32
+// and 128 on the matrix cores (operands loaded once), g = 8 on the VALU,
+// g = 0 (identity) nothing.  Same results in every case: fmaf chains in index
 // order from +0.
 template <int G, bool INV>
 struct TileGauge {
-  static constexpr bool kMfma = G == 16 || G == 32;
+  static constexpr bool kMfma = G == 16 || G == 32 || G == 128;
   MfmaGaugeFrags<kMfma ? G : 16> f;
   const float *Gf;
   __device__ __forceinline__ void load(const float *__restrict__ gf) {

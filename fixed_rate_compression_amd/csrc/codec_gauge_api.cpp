@@ -449,7 +449,10 @@ namespace {
 // error partials per field of a decode launch (one per workgroup)
 int64_t err_per_field(const cg_shape *s, const cg_codec *c, int g, int64_t nt) {
   const int64_t tiles = (nt + cgk::TILE_T - 1) / cgk::TILE_T;
-  if (g == 128) return (tiles + cgk::ZFP128_CHUNK - 1) / cgk::ZFP128_CHUNK;
+  // zfp with the full-head gauge: bf16 storage takes the split bf16 kernels
+  // (16-tile chunks), fp32 storage the fmaf-chain kernels (chunked like g <= 32)
+  if (c->backend == CG_BACKEND_ZFP && g == 128 && s->dtype == CG_DTYPE_BF16)
+    return (tiles + cgk::ZFP128_CHUNK - 1) / cgk::ZFP128_CHUNK;
   if (c->backend == CG_BACKEND_ZFP) {
     const int ct = cgk::zfp_chunk_tiles(n_fields(s), tiles);
     return (tiles + ct - 1) / ct;
@@ -644,7 +647,7 @@ int cg_gauge_apply(const cg_shape *shape, const void *kv, const cg_gauge *gauge,
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = shape->dtype == CG_DTYPE_BF16;
   hipError_t e;
-  if (gauge->group == 128)
+  if (gauge->group == 128 && bf16)
     e = cgq::gauge128_rows_launch(bf16, direction == 1, kv, gauge->G, out,
                                   shape->token_capacity, shape->tokens, n_fields(shape),
                                   shape->batch, shape->heads, s);

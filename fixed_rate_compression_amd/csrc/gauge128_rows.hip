@@ -1,5 +1,6 @@
-// cg_gauge_apply for the dense (g = 128) gauge: the quantizers' MFMA routine
-// on the same 64-token tiles and 16-tile workgroup chunks.
+// cg_gauge_apply for the dense (g = 128) gauge with bf16 storage: the
+// quantizers' split bf16 MFMA routine on the same 64-token tiles and 16-tile
+// workgroup chunks.
 #include "quant_launch.hpp"
 
 namespace cgq {
@@ -10,13 +11,9 @@ hipError_t gauge128_rows_launch(bool bf16, bool inverse, const void *kv, const f
   QuantArgs q = make_args(tcap, tokens, 0, tokens, fields, batch, heads, 0, 0, 0, 0, 1);
   const QK a = make_qk(q, quant_chunk_tiles(128, fields, (tokens + TILE_T - 1) / TILE_T));
   const dim3 grid((unsigned)(fields * a.chunks)), block(NT);
-  if (bf16) {
-    if (inverse) hipLaunchKernelGGL((k_gauge128_rows<true, true>), grid, block, 0, s, kv, gauges, out, a);
-    else hipLaunchKernelGGL((k_gauge128_rows<true, false>), grid, block, 0, s, kv, gauges, out, a);
-  } else {
-    if (inverse) hipLaunchKernelGGL((k_gauge128_rows<false, true>), grid, block, 0, s, kv, gauges, out, a);
-    else hipLaunchKernelGGL((k_gauge128_rows<false, false>), grid, block, 0, s, kv, gauges, out, a);
-  }
+  if (!bf16) return hipErrorInvalidValue;  // fp32 storage: the fmaf-chain rows kernel
+  if (inverse) hipLaunchKernelGGL((k_gauge128_rows<true, true>), grid, block, 0, s, kv, gauges, out, a);
+  else hipLaunchKernelGGL((k_gauge128_rows<true, false>), grid, block, 0, s, kv, gauges, out, a);
   return hipGetLastError();
 }
 

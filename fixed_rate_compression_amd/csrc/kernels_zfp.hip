@@ -92,6 +92,12 @@ static hipError_t gauge_rows_g(int g, const void *src, const float *gauges, void
     case 32:
       hipLaunchKernelGGL((k_gauge_rows<SB, DB, 32, INV>), grid, block, 0, s, src, gauges, dst, a);
       return hipGetLastError();
+    case 128:  // fp32 storage only (bf16 takes the split bf16 rows kernel)
+      if constexpr (!SB) {
+        hipLaunchKernelGGL((k_gauge_rows<SB, DB, 128, INV>), grid, block, 0, s, src, gauges, dst, a);
+        return hipGetLastError();
+      }
+      break;
   }
   return hipErrorInvalidValue;
 }

@@ -13,8 +13,11 @@
 // field at bit (t * 128 + c) * bits of its code region).
 //
 // Work layout: a workgroup (256 threads) processes 64-token tiles of one
-// field (a chunk of consecutive tiles when the dense MFMA gauge is used, so
-// its 64 KB matrix is loaded once).  After the gauge, thread i owns the 32
+// field (a chunk of consecutive tiles when the full-head gauge is used, so
+// its 64 KB matrix is loaded once).  The full-head gauge runs on the bf16
+// matrix cores in split precision with bf16 storage (kDense), and as fp32
+// matrix-core fmaf chains (TileGauge, the reading order of the smaller
+// groups) with fp32 storage.  After the gauge, thread i owns the 32
 // values (row i/4, channels 32 (i%4) .. +31): exactly `bits` 32-bit words of
 // codes, stored with one vector store, so a wave writes a contiguous span.
 #pragma once
@@ -30,6 +33,10 @@
 namespace cgq {
 
 using namespace cgk;
+
+// full-head gauge with bf16 storage: split-precision bf16 matrix-core path
+template <int G, bool BF16>
+constexpr bool kDense = G == 128 && BF16;
 
 struct QK {
   int64_t tcap, tokens, t0, nt;
@@ -181,7 +188,7 @@ struct GaugedTiles {
                                        unsigned char *lds, const TileGauge<G, false> &tg,
                                        const G128Frags &fr) {
     float *xs = (float *)lds;
-    if constexpr (G == 128) {
+    if constexpr (kDense<G, BF16>) {
       uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
       pre.put(sh, sl);
       __syncthreads();
@@ -202,13 +209,13 @@ struct GaugedTiles {
 
 // Every thread hands over its 32 decoded values (row t, channels 32 j ..);
 // apply the inverse gauge to the whole tile, result in the tile view of lds.
-template <int G>
+template <int G, bool BF16>
 __device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, int j,
                                                     const float (&v)[32], int nrows,
                                                     const TileGauge<G, true> &tg,
                                                     const G128Frags &fr) {
   float *xs = (float *)lds;
-  if constexpr (G == 128) {
+  if constexpr (kDense<G, BF16>) {
     uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
     split32(sh, sl, t, j, v);
     __syncthreads();
@@ -279,9 +286,9 @@ __global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
-  if constexpr (G == 128) load_g128<false>(Gf, fr);
+  if constexpr (kDense<G, BF16>) load_g128<false>(Gf, fr);
   TileGauge<G, false> tg;
-  if constexpr (G != 0 && G != 128) tg.load(Gf);
+  if constexpr (G != 0 && !kDense<G, BF16>) tg.load(Gf);
   const int BT = a.block;
   const int64_t nblk_f = a.tcap / BT;
   const int t = threadIdx.x >> 2, j = threadIdx.x & 3, w = threadIdx.x >> 6;
@@ -346,15 +353,15 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
   __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
   // dense gauge: (min, step) of each tile row and the column sums of the
   // inverse matrix, for the range applied after the product
-  __shared__ __align__(16) float2 rowp[G == 128 ? TILE_T : 1];
-  __shared__ float csum[G == 128 ? D : 1];
+  __shared__ __align__(16) float2 rowp[kDense<G, BF16> ? TILE_T : 1];
+  __shared__ float csum[kDense<G, BF16> ? D : 1];
   float *xs = (float *)lds;
   const int64_t f = launch_field((int64_t)blockIdx.x / a.chunks, a.fsel, a.fstep, a.fbase);
   const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
-  if constexpr (G == 128) {
+  if constexpr (kDense<G, BF16>) {
     load_g128<true>(Gf, fr);
     // inverse matrix B[k][n] = G[k][n]: column sums in a fixed order
     if (threadIdx.x < D) {
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
     }
   }
   TileGauge<G, true> tg;
-  if constexpr (G != 0 && G != 128) tg.load(Gf);
+  if constexpr (G != 0 && !kDense<G, BF16>) tg.load(Gf);
   const int BT = a.block;
   const int64_t nblk_f = a.tcap / BT;
   const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
   for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
     const int nrows = tile_rows(a, tile);
-    if constexpr (G == 128) {
+    if constexpr (kDense<G, BF16>) {
       // block-uniform ranges are one per block: (min + q step) G = step (q G) + min colsum(G),
       // and the codes (at most 8 bits) are exact bf16 values: two passes, no split
       uint32_t q[32];
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
         for (int k = 0; k < 32; k++) v[k] = 0.0f;
       }
       if (tile + 1 < tend) fetch(tile + 1);
-      inverse_gauged_tile<G>(lds, t, j, v, nrows, tg, fr);
+      inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, fr);
     }
     const size_t off = (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
     if (a.ref)
@@ -459,9 +466,9 @@ __global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
-  if constexpr (G == 128) load_g128<false>(Gf, fr);
+  if constexpr (kDense<G, BF16>) load_g128<false>(Gf, fr);
   TileGauge<G, false> tg;
-  if constexpr (G != 0 && G != 128) tg.load(Gf);
+  if constexpr (G != 0 && !kDense<G, BF16>) tg.load(Gf);
   const int64_t Tq = a.tokens - a.residual, Tcq = a.tcap - a.residual;
   const size_t Pf = (size_t)Tcq * 16 * BITS + (size_t)a.residual * D * ESZ;
   uint8_t *pf = payload + (size_t)f * Pf;
@@ -552,9 +559,9 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
-  if constexpr (G == 128) load_g128<true>(Gf, fr);
+  if constexpr (kDense<G, BF16>) load_g128<true>(Gf, fr);
   TileGauge<G, true> tg;
-  if constexpr (G != 0 && G != 128) tg.load(Gf);
+  if constexpr (G != 0 && !kDense<G, BF16>) tg.load(Gf);
   const int64_t Tq = a.tokens - a.residual, Tcq = a.tcap - a.residual;
   const size_t Pf = (size_t)Tcq * 16 * BITS + (size_t)a.residual * D * ESZ;
   const uint8_t *pf = payload + (size_t)f * Pf;
@@ -620,7 +627,7 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
     if (tile + 1 < tend) fetch(tile + 1);
-    inverse_gauged_tile<G>(lds, t, j, v, nrows, tg, fr);
+    inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, fr);
     const size_t off = (size_t)(f * a.tcap + tb) * D * ESZ;
     if (a.ref)
       store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
@@ -631,8 +638,9 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
   if (a.ref) write_err(err, a.epart);
 }
 
-// dense-gauge rows kernel behind cg_gauge_apply(g = 128): same tiles, same
-// fragments, same MFMA sequence as the fused quantizer kernels
+// dense-gauge rows kernel behind cg_gauge_apply(g = 128) with bf16 storage:
+// same tiles, same fragments, same MFMA sequence as the fused quantizer
+// kernels (fp32 storage uses the fmaf-chain rows kernel of the smaller groups)
 template <bool BF16, bool INV>
 __global__ __launch_bounds__(NT) void k_gauge128_rows(const void *__restrict__ src,
                                                       const float *__restrict__ gauges,

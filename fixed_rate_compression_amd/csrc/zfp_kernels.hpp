@@ -8,8 +8,9 @@
 // stream.  A workgroup (256 threads) walks a chunk of consecutive tiles of one
 // field, loading tile i+1 into registers while it works on tile i:
 //   encode: coalesced tile load -> LDS (fp32) -> gauge in place (TileGauge:
-//           matrix-core fmaf chains for g = 16/32, VALU for g = 8; the
-//           split-precision MFMA routine for g = 128)
+//           matrix-core fmaf chains for g = 16/32 and, with fp32 storage,
+//           g = 128; VALU for g = 8; the split-precision bf16 MFMA routine
+//           for g = 128 with bf16 storage)
 //           -> one block per thread-iteration (zfp_block.hpp, all in VGPRs)
 //           -> codes staged in LDS -> coalesced 16-byte stores of the span.
 //   decode: the mirror image; with a reference pointer the store also
@@ -199,10 +200,12 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
   if (a.ref) write_err(err, a.epart);
 }
 
-// Dense (g = 128) gauge on the matrix cores (gauge128.hpp): a workgroup walks
-// ZFP128_CHUNK consecutive tiles of one field so the 64 KB gauge is turned
-// into VGPR fragments once, and loads tile i+1 (KV rows, or code words) while
-// it works on tile i.
+// Dense (g = 128) gauge with bf16 storage on the bf16 matrix cores
+// (gauge128.hpp, split precision): a workgroup walks ZFP128_CHUNK
+// consecutive tiles of one field so the 64 KB gauge is turned into VGPR
+// fragments once, and loads tile i+1 (KV rows, or code words) while it works
+// on tile i.  (fp32 storage takes the fp32 fmaf-chain gauge of k_zfp_encode /
+// k_zfp_decode instead.)
 template <int R, bool BF16>
 __global__ __launch_bounds__(NT) void k_zfp_encode128(const void *__restrict__ kv,
                                                       const float *__restrict__ gauges,
@@ -349,8 +352,11 @@ hipError_t zfp_launch_rate(bool encode, bool bf16, int g, const void *src, const
   }
   CG_L(true, 0) CG_L(true, 8) CG_L(true, 16) CG_L(true, 32)
   CG_L(false, 0) CG_L(false, 8) CG_L(false, 16) CG_L(false, 32)
+  // fp32 storage, full-head gauge: fp32 matrix-core fmaf chains (exact
+  // reading order), in the same kernels as the grouped gauges
+  CG_L(false, 128)
 #undef CG_L
-  if (g == 128) {
+  if (g == 128 && bf16) {
     TileArgs c = a;
     c.chunks = (a.tiles + ZFP128_CHUNK - 1) / ZFP128_CHUNK;
     c.chunk_tiles = ZFP128_CHUNK;
@@ -365,7 +371,7 @@ hipError_t zfp_launch_rate(bool encode, bool bf16, int g, const void *src, const
                          gauges, dst, c);                                                        \
     return hipGetLastError();                                                                    \
   }
-    CG_L128(true) CG_L128(false)
+    CG_L128(true)
 #undef CG_L128
   }
   return hipErrorInvalidValue;

@@ -130,7 +130,7 @@ def _attention(q, K, V, Wo, H, q_heads):
     return Wo @ o
 
 
-@pytest.mark.parametrize("g,bf16,tol", [(16, False, 1e-5), (128, False, 1e-4), (32, True, 2e-2)])
+@pytest.mark.parametrize("g,bf16,tol", [(16, False, 1e-5), (128, False, 1e-5), (32, True, 2e-2)])
 def test_folded_attention_step(g, bf16, tol):
     """Decode-attention step of layer 1 on the decoded cache: explicit recovery
     (cg_decode) against the gauged cache with the query and W_o gauged by

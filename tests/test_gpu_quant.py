@@ -1,12 +1,13 @@
 """GPU parity of the fused gauge + block-uniform / KIVI-style quantizers and
 their decoders against the oracle ("Codec-Gauge", arXiv HTML,
 evaluation-protocol paragraph).  Bar: bit-exact codes and metadata; for
-g <= 32 the decoded cache is bit-exact too.  For the dense g = 128 gauge
-(MFMA, accumulation order not reproducible on the CPU) parity is staged: the
-oracle quantizes the library's own gauged field (cg_gauge_apply, the same
-device routine as the fused kernel) and must produce the fused kernel's codes
-exactly; the gauge itself and the decoded cache are checked against fp64
-within a tolerance."""
+g <= 32, and for the full-head gauge with fp32 storage (fp32 matrix-core
+fmaf chains), the decoded cache is bit-exact too.  For the full-head gauge
+with bf16 storage (split-precision bf16 matrix cores, an accumulation order
+the CPU does not reproduce) parity is staged: the oracle quantizes the
+library's own gauged field (cg_gauge_apply, the same device routine as the
+fused kernel) and must produce the fused kernel's codes exactly; the gauge
+itself and the decoded cache are checked against fp64 within the bf16 bar."""
 import numpy as np
 import pytest
 
@@ -220,30 +221,53 @@ def test_dense_gauge_staged(backend, bits, blk, res):
     assert worst_o <= 1e-2
 
 
-@pytest.mark.parametrize("bits,blk", [(3, 64), (8, 32)])
-def test_dense_gauge_block_uniform_fp32_decode(bits, blk):
-    """Block-uniform decode with the dense gauge applies the block's range after
-    the product, (min + q step) G = step (q G) + min colsum(G): fp32 I/O,
-    staged codes exact, the decoded cache within 5e-5 of the fp64 oracle."""
-    L, KV, B, H, T = 1, 2, 1, 2, 1344
+@pytest.mark.parametrize("backend,bits,blk,res", [
+    (cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64, 0),
+    (cg.CG_BACKEND_BLOCK_UNIFORM, 8, 32, 0),
+    (cg.CG_BACKEND_KIVI, 2, 32, 128),
+    (cg.CG_BACKEND_KIVI, 4, 32, 128),
+])
+def test_full_head_gauge_quantizers_fp32_bit_exact(backend, bits, blk, res):
+    """Full-head gauge (g = 128) with fp32 storage: fp32 matrix-core fmaf
+    chains over k = 0..127, so codes, metadata, the KIVI tail and the decoded
+    cache are bit-exact against the oracle end to end; the gauge and the
+    decoded cache are also held to the 1e-5 fp32 bar against fp64."""
+    L, KV, B, H, T = 1, 2, 1, 2, 1344             # 21 tiles: a full 16-tile chunk and a ragged one
     x = kv_cpu(64 + bits, L, KV, B, H, T, T, 0.95, 4, bf16=False)
     G = gauges_for(71, L, KV, H, 128)
-    codec = cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, bits, blk, 0)
-    pay, meta, out, xg = run(x, G, 128, codec, L, KV, B, H, T, False)
-    per = T * D * bits // 8
-    worst = 0.0
+    codec = cg.make_codec(backend, bits, blk, res)
+    pay, meta, out, xg_lib = run(x, G, 128, codec, L, KV, B, H, T, False)
+    worst_g, worst_o = 0.0, 0.0
     for f in range(n_fields(L, KV, B, H)):
-        Gf = gauge_of_field(G, f, KV, B, H).astype(np.float64)
-        p_ref, m_ref = oracle.bu_encode_field(xg[f], blk, bits)
-        assert np.array_equal(pay[f * per:(f + 1) * per], p_ref)
-        assert np.array_equal(meta.reshape(-1, T // blk, 2)[f].view(np.uint32), m_ref.view(np.uint32))
-        ref = oracle.gauge_inverse_f64(oracle.bu_decode_field(p_ref, m_ref, T, D, blk, bits), Gf, 128)
-        worst = max(worst, rel_err(out[f], ref))
-    print(f"dense block-uniform fp32 decode max rel err {worst:.3e}")
-    assert worst <= 5e-5
+        Gf = gauge_of_field(G, f, KV, B, H)
+        xg = oracle.gauge_forward(x[f], Gf, 128)
+        assert np.array_equal(xg_lib[f].view(np.uint32), xg.view(np.uint32)), f
+        if backend == cg.CG_BACKEND_BLOCK_UNIFORM:
+            per = T * D * bits // 8
+            p_ref, m_ref = oracle.bu_encode_field(xg, blk, bits)
+            assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f
+            assert np.array_equal(meta.reshape(-1, T // blk, 2)[f].view(np.uint32), m_ref.view(np.uint32)), f
+            deq = oracle.bu_decode_field(p_ref, m_ref, T, D, blk, bits)
+        else:
+            kind = (f // (B * H)) % KV
+            p_ref, m_ref, tail = oracle.kivi_encode_field(xg, kind, 32, bits, res)
+            pq, pt, mf = kivi_split(pay, meta, f, T, res, bits, 4)
+            assert np.array_equal(pq, p_ref), f
+            assert np.array_equal(mf.view(np.uint32), m_ref.view(np.uint32)), f
+            assert np.array_equal(pt, tail.view(np.uint8).reshape(-1)), f
+            deq = oracle.kivi_decode_field(p_ref, m_ref, tail, T, D, kind, 32, bits, res)
+        y = oracle.gauge_inverse(deq, Gf, 128)
+        assert np.array_equal(out[f].view(np.uint32), y.view(np.uint32)), f
+        G64 = Gf.astype(np.float64)
+        worst_g = max(worst_g, rel_err(xg, oracle.gauge_forward_f64(x[f], G64, 128)))
+        worst_o = max(worst_o, rel_err(out[f], oracle.gauge_inverse_f64(deq, G64, 128)))
+    print(f"fp32 full-head gauge rel err {worst_g:.3e}; inverse gauge rel err {worst_o:.3e}")
+    assert worst_g <= 1e-5 and worst_o <= 1e-5
 
 
 def test_dense_gauge_apply_fp32_and_inverse():
+    """cg_gauge_apply with the full-head gauge and fp32 storage: bit-exact
+    fmaf chains in both directions, and within the 1e-5 fp32 bar of fp64."""
     t = torch()
     L, KV, B, H, T = 1, 1, 1, 2, 200
     x = kv_cpu(80, L, KV, B, H, T, T, 0.95, 4, bf16=False)
@@ -259,43 +283,84 @@ def test_dense_gauge_apply_fp32_and_inverse():
     t.cuda.synchronize()
     yh, zh = to_host(y), to_host(z)
     for f in range(2):
-        Gf = gauge_of_field(G, f, KV, B, H).astype(np.float64)
-        ref = oracle.gauge_forward_f64(x[f], Gf, 128)
-        e1 = rel_err(yh[f], ref)
-        e2 = rel_err(zh[f], x[f].astype(np.float64))
-        print(f"fp32 dense gauge rel err {e1:.3e}, round trip {e2:.3e}")
-        assert e1 <= 3e-5 and e2 <= 6e-5
+        Gf = gauge_of_field(G, f, KV, B, H)
+        fwd = oracle.gauge_forward(x[f], Gf, 128)
+        assert np.array_equal(yh[f].view(np.uint32), fwd.view(np.uint32)), f
+        inv = oracle.gauge_inverse(fwd, Gf, 128)
+        assert np.array_equal(zh[f].view(np.uint32), inv.view(np.uint32)), f
+        G64 = Gf.astype(np.float64)
+        e1 = rel_err(yh[f], oracle.gauge_forward_f64(x[f], G64, 128))
+        e2 = rel_err(zh[f], oracle.gauge_inverse_f64(yh[f], G64, 128))
+        e3 = rel_err(zh[f], x[f].astype(np.float64))
+        print(f"fp32 dense gauge rel err {e1:.3e}, inverse {e2:.3e}, round trip {e3:.3e}")
+        assert e1 <= 1e-5 and e2 <= 1e-5 and e3 <= 1e-5
 
 
-def test_full_head_config_sampled_fields():
-    """Full-head gauge workload: 32 layers x K/V x 8 KV heads x 131072 tokens,
-    bf16, dense 128 x 128 gauges; KIVI-style 4-bit (group 32, 128-token tail).
-    Sampled fields of layers 0 and 31 are checked staged (bit-exact codes and
-    metadata on the library's gauged field)."""
+FULL_HEAD_FIELDS = [(0, 0, 0), (0, 1, 7), (15, 0, 3), (15, 1, 4), (31, 0, 5), (31, 1, 7)]
+
+
+@pytest.mark.parametrize("backend,bits,blk,res", [
+    (cg.CG_BACKEND_KIVI, 2, 32, 128),
+    (cg.CG_BACKEND_KIVI, 4, 32, 128),
+    (cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64, 0),
+])
+def test_full_head_config_sampled_fields(backend, bits, blk, res):
+    """Full-head gauge workload at its real size: 32 layers x K/V x 8 KV heads
+    x 131072 tokens, bf16, dense 128 x 128 gauges; KIVI-style 2- and 4-bit
+    (group 32, 128-token tail) and block-uniform 3-bit (64-token blocks),
+    encoded and decoded by the same launches the bench times.  Fields of
+    layers 0, 15 and 31 (the last field among them) are checked staged:
+    codes, metadata and tail bit-exact against the oracle applied to the
+    library's gauged field; the gauge within 1e-4 of fp64; the decoded bf16
+    cache within the 1e-2 bf16 bar of the fp64 inverse gauge of the oracle's
+    dequantized codes."""
     t = torch()
-    L, KV, B, H, T, res, bits = 32, 2, 1, 8, 131072, 128, 4
+    L, KV, B, H, T = 32, 2, 1, 8, 131072
+    print(f"full-head config: backend {backend}, {bits} bits", flush=True)
     x = kv_gpu(3, L, KV, B, H, T, T, 0.95, 4, bf16=True)
     G = gauges_for(103, L, KV, H, 128)
     shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16)
-    codec = cg.make_codec(cg.CG_BACKEND_KIVI, bits, 32, res)
+    codec = cg.make_codec(backend, bits, blk, res)
     pb, mb, _ = cg.cg_encoded_bytes(shape, codec)
     pay = empty_u8(pb)
     meta = t.zeros(mb // 4, dtype=t.float32, device="cuda")
     gauge = cg.make_gauge(128, to_dev(np.ascontiguousarray(G)))
+    out = t.zeros_like(x)
     cg.cg_encode(shape, x, gauge, codec, 0, T, pay, meta)
+    cg.cg_decode(shape, pay, meta, gauge, codec, 0, T, out)
     t.cuda.synchronize()
-    Tq = T - res
-    per = Tq * D * bits // 8 + res * D * 2
     sub = cg.make_shape(1, 1, 1, 1, T, T, D, cg.CG_DTYPE_BF16)
-    for (l, s, h) in [(0, 0, 0), (0, 1, 7), (31, 0, 3), (31, 1, 5)]:
+    kivi = backend == cg.CG_BACKEND_KIVI
+    Tq = T - res
+    per = Tq * D * bits // 8 + res * D * 2 if kivi else T * D * bits // 8
+    mper = 8 * Tq if kivi else 2 * (T // blk)
+    worst_g, worst_o = 0.0, 0.0
+    for (l, s, h) in FULL_HEAD_FIELDS:
         f = (l * KV + s) * H + h
-        xg = t.zeros((1, T, D), dtype=t.float32, device="cuda")
-        cg.cg_gauge_apply(sub, x[f:f + 1].contiguous(), cg.make_gauge(128, gauge._keep[l, s, h].contiguous()), 0, xg)
+        Gf = G[l, s, h]
+        xg_d = t.zeros((1, T, D), dtype=t.float32, device="cuda")
+        cg.cg_gauge_apply(sub, x[f:f + 1].contiguous(), cg.make_gauge(128, gauge._keep[l, s, h].contiguous()), 0, xg_d)
         t.cuda.synchronize()
-        xg = to_host(xg)[0]
-        p_ref, m_ref, tail = oracle.kivi_encode_field(xg, s, 32, bits, res)
+        xg = to_host(xg_d)[0]
+        xf = oracle.to_f32(to_host(x[f]))
+        worst_g = max(worst_g, rel_err(xg, oracle.gauge_forward_f64(xf, Gf.astype(np.float64), 128)))
         pf = to_host(pay[f * per:(f + 1) * per])
-        assert np.array_equal(pf[:Tq * D * bits // 8], p_ref), (l, s, h)
-        mf = to_host(meta[f * 8 * Tq:(f + 1) * 8 * Tq]).reshape(-1, 2)
-        assert np.array_equal(mf.view(np.uint32), m_ref.view(np.uint32)), (l, s, h)
-        assert np.array_equal(pf[Tq * D * bits // 8:], oracle.f32_to_bf16(tail).view(np.uint8).reshape(-1))
+        mf = to_host(meta[f * mper:(f + 1) * mper]).reshape(-1, 2)
+        if kivi:
+            p_ref, m_ref, tail = oracle.kivi_encode_field(xg, s, 32, bits, res)
+            assert np.array_equal(pf[:Tq * D * bits // 8], p_ref), (l, s, h)
+            tail_st = oracle.f32_to_bf16(tail)
+            assert np.array_equal(pf[Tq * D * bits // 8:], tail_st.view(np.uint8).reshape(-1)), (l, s, h)
+            deq = oracle.kivi_decode_field(p_ref, m_ref, oracle.to_f32(tail_st), T, D, s, 32, bits, res)
+        else:
+            p_ref, m_ref = oracle.bu_encode_field(xg, blk, bits)
+            assert np.array_equal(pf, p_ref), (l, s, h)
+            deq = oracle.bu_decode_field(p_ref, m_ref, T, D, blk, bits)
+        assert np.array_equal(mf.view(np.uint32), m_ref.reshape(-1, 2).view(np.uint32)), (l, s, h)
+        ref = oracle.gauge_inverse_f64(deq, Gf.astype(np.float64), 128)
+        worst_o = max(worst_o, rel_err(oracle.to_f32(to_host(out[f])), ref))
+        print(f"  field (layer {l}, kv {s}, head {h}) ok", flush=True)
+    print(f"gauge rel err {worst_g:.3e}; decoded cache vs fp64 inverse {worst_o:.3e}")
+    assert worst_g <= 1e-4 and worst_o <= 1e-2
+    del x, out, pay, meta
+    t.cuda.empty_cache()

@@ -1,9 +1,11 @@
 """GPU parity of the fused gauge + zfp-style encode and decode + inverse gauge
 against the oracle ("Codec-Gauge", arXiv HTML, evaluation-protocol
 paragraph: gauge -> fixed-rate zfp on the FP32-transformed field -> decode ->
-inverse gauge).  Bar: bit-exact codec streams; for g <= 32 the decoded cache
-is bit-exact too, because both sides evaluate the gauge as the same fmaf
-chains, decode the same integers and round to bf16 the same way."""
+inverse gauge).  Bar: bit-exact codec streams; for g <= 32, and for the
+full-head gauge with fp32 storage, the decoded cache is bit-exact too,
+because both sides evaluate the gauge as the same fmaf chains, decode the
+same integers and round to bf16 the same way.  The full-head gauge with bf16
+storage (split-precision bf16 matrix cores) is checked staged."""
 import numpy as np
 import pytest
 
@@ -13,6 +15,10 @@ from gpu_util import (D, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu, n
                       to_dev, to_host, zfp_oracle_field)
 
 pytestmark = pytest.mark.gpu
+
+
+def rel_err(got, ref):
+    return float(np.max(np.abs(got.astype(np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
 def run_zfp(x_host, G, g, R, L, KV, B, H, T, Tcap, bf16, chunks=None):
@@ -303,23 +309,51 @@ def test_27b_class_full_size_sampled_fields():
 
 
 @pytest.mark.parametrize("R", [3, 4, 8])
-@pytest.mark.parametrize("bf16", [True, False])
-def test_dense_gauge_zfp_staged(R, bf16):
-    """Full-head gauge (g = 128, matrix cores) with the zfp-style coder.  The
-    dense gauge is not an fmaf chain, so parity is staged: (1) the gauge,
-    through cg_gauge_apply (the routine the fused kernels run), against the
-    fp64 oracle; (2) the codes bit-exact against the oracle's coder applied to
-    those gauged values; (3) the decoded cache bit-exact against the oracle's
-    decode of the same codes taken through the same inverse routine."""
+def test_full_head_gauge_zfp_fp32_bit_exact(R):
+    """Full-head gauge (g = 128) with fp32 storage: the gauge runs as fp32
+    matrix-core fmaf chains over k = 0..127 (the reading order of every
+    group size), so payload and decoded cache are bit-exact against the
+    oracle end to end.  The fp64 gauge is the tolerance reference for the
+    1e-5 fp32 bar on the gauge and the inverse gauge."""
     t = __import__("torch")
-    # 22 tiles: one full 16-tile workgroup chunk, a ragged chunk, an 8-row last tile
+    # 22 tiles: several 4-tile workgroup chunks, a ragged chunk, an 8-row last tile
     L, KV, B, H, T = 1, 2, 1, 2, 64 * 21 + 8
-    x = kv_cpu(400 + R, L, KV, B, H, T, T, 0.95, 4, bf16=bf16)
+    x = kv_cpu(400 + R, L, KV, B, H, T, T, 0.95, 4, bf16=False)
     G = gauges_for(410, L, KV, H, 128)
-    pay, out = run_zfp(x, G, 128, R, L, KV, B, H, T, T, bf16)
+    pay, out = run_zfp(x, G, 128, R, L, KV, B, H, T, T, False)
+    per = T * D * R // 8
+    worst_f, worst_i = 0.0, 0.0
+    for f in range(n_fields(L, KV, B, H)):
+        Gf = gauge_of_field(G, f, KV, B, H)
+        xg = oracle.gauge_forward(x[f], Gf, 128)
+        p_ref = oracle.zfp_encode_field(xg, R)
+        assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f"payload mismatch in field {f}"
+        dec = oracle.zfp_decode_field(p_ref, T, D, R)
+        y = oracle.gauge_inverse(dec, Gf, 128)
+        assert np.array_equal(out[f].view(np.uint32), y.view(np.uint32)), f"decoded mismatch in field {f}"
+        G64 = Gf.astype(np.float64)
+        worst_f = max(worst_f, rel_err(xg, oracle.gauge_forward_f64(x[f], G64, 128)))
+        worst_i = max(worst_i, rel_err(out[f], oracle.gauge_inverse_f64(dec, G64, 128)))
+    print(f"fp32 full-head gauge rel err {worst_f:.3e}, inverse gauge rel err {worst_i:.3e}")
+    assert worst_f <= 1e-5 and worst_i <= 1e-5
+
+
+@pytest.mark.parametrize("R", [3, 4, 8])
+def test_dense_gauge_zfp_bf16_staged(R):
+    """Full-head gauge (g = 128) with bf16 storage: the split-precision bf16
+    matrix-core gauge is not an fmaf chain, so parity is staged.  (1) The
+    gauge, through cg_gauge_apply (the routine the fused kernels run),
+    against the fp64 oracle; (2) the codes bit-exact against the oracle's
+    coder applied to those gauged values; (3) the decoded cache within the
+    bf16 bar (1e-2) of the oracle's fp64 inverse gauge of the oracle's decode
+    of the same codes."""
+    t = __import__("torch")
+    L, KV, B, H, T = 1, 2, 1, 2, 64 * 21 + 8
+    x = kv_cpu(400 + R, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    G = gauges_for(410, L, KV, H, 128)
+    pay, out = run_zfp(x, G, 128, R, L, KV, B, H, T, T, True)
     F = n_fields(L, KV, B, H)
-    shape_in = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16 if bf16 else cg.CG_DTYPE_F32)
-    shape32 = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_F32)
+    shape_in = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16)
     gauge = cg.make_gauge(128, to_dev(np.ascontiguousarray(G)))
     xg_d = t.zeros((F, T, D), dtype=t.float32, device="cuda")
     cg.cg_gauge_apply(shape_in, to_dev(x), gauge, 0, xg_d)
@@ -327,20 +361,15 @@ def test_dense_gauge_zfp_staged(R, bf16):
     xg = to_host(xg_d)
     per = T * D * R // 8
     dec = np.zeros((F, T, D), np.float32)
-    worst = 0.0
+    worst_g, worst_o = 0.0, 0.0
     for f in range(F):
         Gf = gauge_of_field(G, f, KV, B, H).astype(np.float64)
-        ref = oracle.gauge_forward_f64(oracle.to_f32(x[f]), Gf, 128)
-        worst = max(worst, float(np.max(np.abs(xg[f] - ref)) / np.max(np.abs(ref))))
+        worst_g = max(worst_g, rel_err(xg[f], oracle.gauge_forward_f64(oracle.to_f32(x[f]), Gf, 128)))
         p_ref = oracle.zfp_encode_field(xg[f], R)
         assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f"payload mismatch in field {f}"
         dec[f] = oracle.zfp_decode_field(p_ref, T, D, R)
-    assert worst <= 1e-4, worst
-    y_d = t.zeros((F, T, D), dtype=t.float32, device="cuda")
-    cg.cg_gauge_apply(shape32, to_dev(dec), gauge, 1, y_d)
-    t.cuda.synchronize()
-    y = to_host(y_d)
-    if bf16:
-        assert np.array_equal(out, oracle.f32_to_bf16(y))
-    else:
-        assert np.array_equal(out.view(np.uint32), y.view(np.uint32))
+        ref = oracle.gauge_inverse_f64(dec[f], Gf, 128)
+        worst_o = max(worst_o, rel_err(oracle.to_f32(out[f]), ref))
+    print(f"bf16 dense gauge rel err {worst_g:.3e}; decoded cache vs fp64 inverse {worst_o:.3e}")
+    assert worst_g <= 1e-4          # the bf16 I/O bar is 1e-2
+    assert worst_o <= 1e-2
