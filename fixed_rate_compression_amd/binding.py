@@ -24,11 +24,12 @@ CG_HEADER_BYTES = 64
 EXPORTED = ["cg_encoded_bytes", "cg_encode", "cg_decode", "cg_decode_gauged", "cg_roundtrip",
             "cg_gauge_fit_stats", "cg_stats_workspace_bytes", "cg_gauge_from_skew",
             "cg_gauge_apply", "cg_write_header", "cg_decode_error_workspace_bytes",
-            "cg_decode_error", "cg_cache_error_summary", "cg_adamw_update", "cg_gauge_control",
+            "cg_decode_error", "cg_decode_error_noalloc", "cg_cache_error_summary", "cg_adamw_update", "cg_gauge_control",
             "cg_second_moment_workspace_bytes", "cg_second_moment", "cg_gauge_grad", "cg_gauge_heads",
             "cg_last_error"]
 
 CG_KEEP_KEYS, CG_KEEP_VALUES = 1, 2
+CG_NOALLOC_SCRATCH_BYTES = 16 << 20
 CG_CONTROL_IDENTITY, CG_CONTROL_HADAMARD, CG_CONTROL_DCT, CG_CONTROL_ORTHONORMALIZE, CG_CONTROL_KLT = range(5)
 
 
@@ -103,6 +104,7 @@ def lib():
             "cg_write_header": [SP, CP, I32, I32, P, U64],
             "cg_decode_error_workspace_bytes": [SP, GP, CP, I64, I64, ctypes.POINTER(ctypes.c_size_t)],
             "cg_decode_error": [SP, P, U64, P, U64, GP, CP, I64, I64, P, P, P, ctypes.c_size_t, P, P],
+            "cg_decode_error_noalloc": [SP, P, U64, P, U64, GP, CP, I64, I64, P, P, P, P],
             "cg_cache_error_summary": [SP, P, ctypes.POINTER(CgCacheError)],
             "cg_adamw_update": [I64, P, P, P, P, I64, ctypes.c_double, ctypes.c_double,
                                 ctypes.c_double, ctypes.c_double, ctypes.c_double],
@@ -219,6 +221,15 @@ def cg_decode_error(shape, payload, meta, gauge, codec, t0, nt, kv_out, kv_ref, 
         ctypes.byref(shape), _ptr(payload), _nbytes(payload), _ptr(meta), _nbytes(meta),
         ctypes.byref(gauge), ctypes.byref(codec), t0, nt, _ptr(kv_out), _ptr(kv_ref),
         _ptr(workspace), _nbytes(workspace), _ptr(err), _stream(stream)))
+
+
+def cg_decode_error_noalloc(shape, payload, meta, gauge, codec, t0, nt, kv_out, kv_ref, err,
+                            stream=None):
+    """cg_decode_error with the library's built-in device scratch (no workspace)."""
+    _check("cg_decode_error_noalloc", lib().cg_decode_error_noalloc(
+        ctypes.byref(shape), _ptr(payload), _nbytes(payload), _ptr(meta), _nbytes(meta),
+        ctypes.byref(gauge), ctypes.byref(codec), t0, nt, _ptr(kv_out), _ptr(kv_ref),
+        _ptr(err), _stream(stream)))
 
 
 def cg_cache_error_summary(shape, err_host: np.ndarray) -> dict:

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -595,6 +596,60 @@ int cg_decode_error(const cg_shape *shape, const void *payload, uint64_t payload
                                           (double)nt * shape->head_dim, (double *)err, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "cg_decode_error reduce");
   return CG_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of cg_decode_error_noalloc: the per-workgroup error partials live
+// in this file-scope device array instead of a caller workspace.  Host code
+// never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol); it passes the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and cached here.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) double scratch[CG_NOALLOC_SCRATCH_BYTES / sizeof(double)];
+std::mutex g_scratch_mu;
+double *g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(double **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CG_E_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(CG_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = (double *)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cg_decode_error_noalloc(const cg_shape *shape, const void *payload, uint64_t payload_cap,
+                            const void *meta, uint64_t meta_cap, const cg_gauge *gauge,
+                            const cg_codec *codec, int64_t t0, int64_t nt, void *kv_out,
+                            const void *kv_ref, cg_field_error *err, void *stream) {
+  g_err.clear();
+  size_t need = 0;
+  int rc = cg_decode_error_workspace_bytes(shape, gauge, codec, t0, nt, &need);
+  if (rc) return rc;
+  if (need > CG_NOALLOC_SCRATCH_BYTES)
+    return fail(CG_E_SIZE, "this call needs %zu bytes of error partials; the built-in scratch "
+                           "holds %zu (use cg_decode_error with a workspace)",
+                need, (size_t)CG_NOALLOC_SCRATCH_BYTES);
+  double *ws = nullptr;
+  if ((rc = noalloc_scratch(&ws))) return rc;
+  return cg_decode_error(shape, payload, payload_cap, meta, meta_cap, gauge, codec, t0, nt, kv_out,
+                         kv_ref, ws, CG_NOALLOC_SCRATCH_BYTES, err, stream);
 }
 
 int cg_cache_error_summary(const cg_shape *shape, const cg_field_error *err, cg_cache_error *out) {

@@ -227,6 +227,28 @@ int cg_decode_error(const cg_shape *shape, const void *payload, uint64_t payload
                     const void *kv_ref, void *workspace, size_t ws_bytes, cg_field_error *err,
                     void *stream);
 
+/*
+ * cg_decode_error for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, validation, results and errors as cg_decode_error, minus
+ * the workspace: the per-workgroup error partials go to a device array of
+ * CG_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  Its device address is looked up on the first
+ * call on a device (that device must be current, and `stream` must belong
+ * to it).  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  Calls whose partials need more than
+ * CG_NOALLOC_SCRATCH_BYTES (see cg_decode_error_workspace_bytes) return
+ * CG_E_SIZE before anything is enqueued.  Every call on a GPU shares that
+ * GPU's array and nothing in it needs to start at zero (each launch
+ * overwrites the partials it reads), but calls that overlap on one GPU
+ * (concurrent streams or threads) race on it: serialize them.
+ */
+#define CG_NOALLOC_SCRATCH_BYTES (16u << 20)
+int cg_decode_error_noalloc(const cg_shape *shape, const void *payload, uint64_t payload_cap,
+                            const void *meta, uint64_t meta_cap, const cg_gauge *gauge,
+                            const cg_codec *codec, int64_t t0, int64_t nt, void *kv_out,
+                            const void *kv_ref, cg_field_error *err, void *stream);
+
 /* Host: per-field sums (host array of n_fields) -> whole-cache figures. */
 int cg_cache_error_summary(const cg_shape *shape, const cg_field_error *err, cg_cache_error *out);
 

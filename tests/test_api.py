@@ -199,3 +199,20 @@ def test_misaligned_device_pointers_are_refused():
     assert L.cg_gauge_heads(ctypes.byref(shape), ctypes.byref(cg.make_gauge(0)), 0, 0, 2, 1,
                             cg.CG_DTYPE_F32, ctypes.c_void_p(4098), ctypes.c_void_p(1 << 40),
                             None) == cg.CG_E_INVAL
+
+
+def test_noalloc_decode_error_refuses_more_partials_than_its_scratch():
+    """The allocation-free cg_decode_error_noalloc checks, on the host and
+    before any device call, that the call's error partials fit the library's
+    built-in scratch (2^20 fields of 64 tokens need 24 MiB > 16 MiB)."""
+    shape = cg.make_shape(1024, 2, 1, 512, 64, 64, 128, cg.CG_DTYPE_BF16)
+    codec = cg.make_codec(cg.CG_BACKEND_ZFP, 4)
+    gauge = cg.make_gauge(0)
+    need = cg.cg_decode_error_workspace_bytes(shape, gauge, codec, 0, 64)
+    assert need > cg.CG_NOALLOC_SCRATCH_BYTES
+    fake = 1 << 20   # never dereferenced: the size check comes first
+    rc = cg.lib().cg_decode_error_noalloc(ctypes.byref(shape), fake, 1 << 40, None, 0,
+                                          ctypes.byref(gauge), ctypes.byref(codec), 0, 64, fake,
+                                          fake, fake, None)
+    assert rc == cg.CG_E_SIZE
+    assert "scratch" in cg.lib().cg_last_error().decode()
