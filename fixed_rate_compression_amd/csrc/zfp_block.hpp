@@ -24,7 +24,15 @@
 //    significant (each coefficient does so at most once per block);
 //  * the block's bits live in ceil(16R/64) 64-bit accumulators; bits past
 //    16R are dropped, which equals stopping at the budget because the code
-//    of a block is a prefix code emitted strictly left to right.
+//    of a block is a prefix code emitted strictly left to right;
+//  * decoder: a plane's verbatim bits and group part come from one 32-bit
+//    window; the group part's flag positions come from the runs of ones (a
+//    found coefficient's 1 is always followed by a flag, so within a run of
+//    ones counted from a data position, data and flag positions alternate);
+//    when no lane of the wave has budget left after 8 planes (the common case
+//    at 2-4 bits per value) the planes are turned into integers with two 8x8
+//    bit transposes and a byte-wise negabinary conversion instead of the full
+//    32-plane transpose.
 // The functions are __host__ __device__ so the same code can be checked on
 // the CPU; they use only portable integer operations.
 #pragma once
@@ -67,19 +75,30 @@ __host__ __device__ __forceinline__ void fwd_xform4(int32_t &a, int32_t &b, int3
   b = (int32_t)((uint32_t)b - (uint32_t)(d >> 1));
 }
 
-// exact inverse of every lifting step, in reverse order (mod 2^32)
+// exact inverse of every lifting step, in reverse order (mod 2^32).  Each
+// undone rotation pair (u += v; v = 2v - u) is written as u' = u + v,
+// v' = v - u (old u), which is the same value mod 2^32 in two operations.
 __host__ __device__ __forceinline__ void inv_xform4(int32_t &a, int32_t &b, int32_t &c,
                                                     int32_t &d) {
-  b = (int32_t)((uint32_t)b + (uint32_t)(d >> 1));
-  d = (int32_t)((uint32_t)d - (uint32_t)(b >> 1));
-  b = (int32_t)((uint32_t)b + (uint32_t)d);
-  d = (int32_t)(((uint32_t)d << 1) - (uint32_t)b);
-  c = (int32_t)((uint32_t)c + (uint32_t)a);
-  a = (int32_t)(((uint32_t)a << 1) - (uint32_t)c);
-  b = (int32_t)((uint32_t)b + (uint32_t)c);
-  c = (int32_t)(((uint32_t)c << 1) - (uint32_t)b);
-  d = (int32_t)((uint32_t)d + (uint32_t)a);
-  a = (int32_t)(((uint32_t)a << 1) - (uint32_t)d);
+  uint32_t A = (uint32_t)a, B = (uint32_t)b, C = (uint32_t)c, Dd = (uint32_t)d;
+  B = B + (uint32_t)(d >> 1);
+  Dd = Dd - (uint32_t)((int32_t)B >> 1);
+  uint32_t t = B;
+  B = B + Dd;
+  Dd = Dd - t;
+  t = C;
+  C = C + A;
+  A = A - t;
+  t = B;
+  B = B + C;
+  C = C - t;
+  t = Dd;
+  Dd = Dd + A;
+  A = A - t;
+  a = (int32_t)A;
+  b = (int32_t)B;
+  c = (int32_t)C;
+  d = (int32_t)Dd;
 }
 
 // Transpose the two 16x16 bit matrices held in the low and high halves of
@@ -119,6 +138,21 @@ __host__ __device__ __forceinline__ void transpose16x2(uint32_t (&w)[16]) {
     if (!(i & 2)) swap_stage(w[i], w[i + 2], 2, 0x33333333u);
 #pragma unroll
   for (int i = 0; i < 16; i += 2) swap_stage(w[i], w[i + 1], 1, 0x55555555u);
+}
+
+// 8x8 bit-matrix transpose of the 64-bit word hi:lo (row r = byte r, column
+// c = bit c of the byte): afterwards byte c holds column c, bit r = row r
+// (three delta swaps of 7, 14 and 28 bit positions; the first two stay
+// within each 32-bit half).
+__host__ __device__ __forceinline__ void transpose8x8(uint32_t &lo, uint32_t &hi) {
+  uint32_t t;
+  t = (lo ^ (lo >> 7)) & 0x00AA00AAu; lo ^= t ^ (t << 7);
+  t = (hi ^ (hi >> 7)) & 0x00AA00AAu; hi ^= t ^ (t << 7);
+  t = (lo ^ (lo >> 14)) & 0x0000CCCCu; lo ^= t ^ (t << 14);
+  t = (hi ^ (hi >> 14)) & 0x0000CCCCu; hi ^= t ^ (t << 14);
+  t = (lo ^ ((hi << 4) | (lo >> 28))) & 0xF0F0F0F0u;
+  lo ^= t;
+  hi ^= t >> 4;
 }
 
 __host__ __device__ __forceinline__ int ctz32(uint32_t x) {  // x != 0
@@ -286,29 +320,50 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
   if (LIMIT % 64) acc[NA - 1] &= (~0ull) >> (64 - LIMIT % 64);
 }
 
-// Group-test/scan part of one bit plane, read bit-parallel.  On entry `pos`
-// is at the plane's first group test and `n` (< 16) coefficients are
-// significant.  The code there is a run of pairs "1 0^gap 1" (a positive
-// group test, zeros scanned over, the newly significant coefficient's 1) and
-// ends with a 0 (failed test), or with the budget, or with the implicit 1 of
-// coefficient 15 (a scan reaching index 15 reads no bit).  With P the
-// inclusive prefix parity of the window, a 1 at odd parity is a test, a 1 at
-// even parity ends a scan and a 0 at even parity is the failed test; the k-th
-// scan-ending 1 (k from 0) at window bit t is coefficient n + t - (k + 1).
-// Returns the new coefficients' bits relative to n; advances pos and n.
+// true when the predicate holds for any lane of the wave executing this call
+// (the host build decides per block)
+__host__ __device__ __forceinline__ bool wave_any(bool p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ballot_w64(p) != 0ull;
+#else
+  return p;
+#endif
+}
+
+__host__ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_perm(hi, lo, sel);
+#else
+  const uint64_t x = ((uint64_t)hi << 32) | lo;
+  uint32_t r = 0;
+  for (int i = 0; i < 4; i++) r |= (uint32_t)((x >> (8 * ((sel >> (8 * i)) & 7))) & 0xFFu) << (8 * i);
+  return r;
+#endif
+}
+
+// Group-test/scan part of one bit plane, read bit-parallel from the window W
+// (bit 0 = the plane's first group test, bits past the budget zero).  On
+// entry `pos` is at that bit and `n` (< 16) coefficients are significant.
+// The part is a run of "test 1, zeros scanned over, the newly significant
+// coefficient's 1" pieces ending with a failed test (0), the budget, or the
+// implicit 1 of coefficient 15 (a scan reaching index 15 reads no bit).
+// Flag positions (the tests) are position 0 and the position right after
+// every found 1.  With a virtual data 1 prepended (G1 = W << 1 | 1), data and
+// flag positions alternate inside every run of ones that starts at a data
+// position, so the data 1s are the even offsets of runs starting at even
+// positions and the odd offsets of runs starting at odd positions; the runs
+// that start at odd positions are picked out by adding their start bits
+// (the carry clears exactly the run).  D (bit t = flag at window bit t) marks
+// the tests; the k-th found 1 (k from 0) at window bit t is coefficient
+// n + t - (k + 1).  Returns the new coefficients' bits relative to n;
+// advances pos and n.
 template <int R>
-__host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Rate<R>::kAcc],
-                                                        int &pos, int &n) {
+__host__ __device__ __forceinline__ uint32_t group_part(uint32_t W, int &pos, int &n) {
   constexpr int LIMIT = Rate<R>::kBits;
-  const uint32_t W = window<R>(acc, pos);
-  uint32_t P = W;
-  P ^= P << 1;
-  P ^= P << 2;
-  P ^= P << 4;
-  P ^= P << 8;
-  P ^= P << 16;
-  const uint32_t tests = W & P;
-  const uint32_t fails = ~(W | P);
+  const uint32_t G1 = (W << 1) | 1u;
+  const uint32_t odd_starts = G1 & ~(G1 << 1) & 0xAAAAAAAAu;
+  const uint32_t D = G1 & (0x55555555u ^ (G1 & ~(G1 + odd_starts)));
+  const uint32_t fails = D & ~W;                              // tests that read 0
   const uint32_t ef = fails ? (uint32_t)ctz32(fails) : 32u;  // first failed test
   const uint32_t room = (uint32_t)(LIMIT - pos);              // >= 1
   const uint32_t m = 15u - (uint32_t)n;                       // index of coefficient 15
@@ -316,7 +371,7 @@ __host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Ra
   uint32_t E = ef < room ? ef : room;
   E = E < 2u * m + 2u ? E : 2u * m + 2u;                      // <= 32
   const uint32_t below = (uint32_t)~(~0ull << E);            // E <= 32
-  uint32_t term = W & ~P & below;
+  uint32_t term = (D >> 1) & below;     // found 1s before E
   uint32_t y = 0u, bias = 1u;
   while (term) {                        // two newly significant coefficients per step
     const uint32_t low1 = term & (0u - term);
@@ -326,7 +381,7 @@ __host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Ra
     term = rest ^ low2;
     bias += 2u;
   }
-  const uint32_t cnt = (uint32_t)__builtin_popcount(below & ~tests);     // bits scanned before E
+  const uint32_t cnt = (uint32_t)__builtin_popcount(below & ~D);        // bits scanned before E
   // three ways the part ends, selected without branches (lanes diverge here):
   //  cap    the scan reaches coefficient 15, whose 1 is implicit;
   //  fail   a failed group test at ef;
@@ -335,7 +390,7 @@ __host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Ra
   const bool cap = cnt > m;
   const bool fail = ef < room;
   const uint32_t ycap = (y & ((1u << m) - 1u)) | (1u << m);
-  const uint32_t inscan = (P >> ((room - 1u) & 31u)) & 1u;
+  const uint32_t inscan = ((D >> (room & 31u)) & 1u) ^ 1u;   // room is not a flag position
   const uint32_t ybud = y | (inscan << (cnt & 31u));
   y = cap ? ycap : (fail ? y : ybud);
   const uint32_t used = cap ? m + (uint32_t)__builtin_popcount(ycap) : (fail ? ef + 1u : room);
@@ -344,48 +399,87 @@ __host__ __device__ __forceinline__ uint32_t group_part(const uint64_t (&acc)[Ra
   return y;
 }
 
-// Decode one block of 16R bits into 16 fp32 values v[4j + i].
+// One bit plane: the n verbatim bits, then (n < 16) the group part, both from
+// one 32-bit window (a plane never spans more than 32 - n bits).
 template <int R>
+__host__ __device__ __forceinline__ uint32_t decode_plane(const uint64_t (&acc)[Rate<R>::kAcc],
+                                                          int &pos, int &n) {
+  constexpr int LIMIT = Rate<R>::kBits;
+  const uint32_t W0 = window<R>(acc, pos);
+  uint32_t x = W0 & ((1u << n) - 1u);   // verbatim bits (n <= 16)
+  const int n0 = n;
+  pos += n0;
+  if (n0 < 16 && pos < LIMIT) x |= group_part<R>(W0 >> n0, pos, n) << n0;
+  return x;
+}
+
+// Decode one block of 16R bits into 16 fp32 values v[4j + i].  Plane j (from
+// the top) is bit 31 - s - j of the negabinary coefficient words, held as
+// 16-bit plane words, two per register: Z[i] = plane 2i | plane 2i+1 << 16.
+// GENERAL = true forces the 32-plane reconstruction (both give the same
+// values whenever the 8-plane one applies).
+template <int R, bool GENERAL = false>
 __host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate<R>::kAcc],
                                                       float (&v)[16]) {
   constexpr int LIMIT = Rate<R>::kBits;
-#pragma unroll
-  for (int k = 0; k < 16; k++) v[k] = 0.0f;
-  if (!(acc[0] & 1u)) return;
   const int emax = (int)((acc[0] >> 1) & 0xFFu) - 127;
-
-  int pos = 9;
-  uint32_t win = window<R>(acc, pos);
-  const int s = win ? ctz32(win) : 32;  // leading failed group tests
-  if (s >= 32 || pos + s >= LIMIT) return;  // no plane reached: all integers 0
-  pos += s;
-
-  uint32_t w[16];
-#pragma unroll
-  for (int k = 0; k < 16; k++) w[k] = 0;
+  const uint32_t win = window<R>(acc, 9);
+  int s = win ? ctz32(win) : 32;        // leading failed group tests
+  int pos = 9 + s;
+  if (!(acc[0] & 1u) || s >= 32 || pos >= LIMIT) {  // empty block, or no plane reached:
+    pos = LIMIT;                                     // every integer is 0
+    s = 0;
+  }
+  uint32_t Z[16];
   int n = 0;
 #pragma unroll
-  for (int j = 0; j < 32; j++) {
-    uint32_t x = 0u;                    // plane word 31-j of the shifted words
-    // planes past the last one (j > 31 - s) lie below bit s of the shifted
-    // words, which the final shift drops; the encoder codes them as zeros
-    if (pos < LIMIT) {                  // (no early exit: keeps the loop unrollable)
-      x = window<R>(acc, pos) & ((1u << n) - 1u);   // verbatim bits (n <= 16)
-      pos += n;
-      const int n0 = n;
-      if (n < 16 && pos < LIMIT) x |= group_part<R>(acc, pos, n) << n0;
-    }
-    if (j < 16)
-      w[15 - j] |= x << 16;
-    else
-      w[31 - j] |= x;
+  for (int j = 0; j < 8; j++) {
+    uint32_t x = 0u;
+    if (pos < LIMIT) x = decode_plane<R>(acc, pos, n);
+    if (j & 1) Z[j >> 1] |= x << 16; else Z[j >> 1] = x;
   }
-  transpose16x2(w);
-
   int32_t q[16];
+  if (!GENERAL && !wave_any(pos < LIMIT || s > 24)) {
+    // Planes 0..7 only, s <= 24.  Rows r = 0..7 of two 8x8 bit matrices are
+    // the low (coefficients 0..7) and high (8..15) bytes of plane 7 - r;
+    // transposed, byte c of a matrix holds coefficient c's planes with plane
+    // 0 in bit 7, i.e. the top byte of its shifted word.
+    uint32_t a0 = byte_perm(Z[3], Z[2], 0x00020406u), a1 = byte_perm(Z[1], Z[0], 0x00020406u);
+    uint32_t b0 = byte_perm(Z[3], Z[2], 0x01030507u), b1 = byte_perm(Z[1], Z[0], 0x01030507u);
+    transpose8x8(a0, a1);
+    transpose8x8(b0, b1);
+    // negabinary digits of a byte at bit 24 - s + r weigh +-2^(24 - s + r),
+    // negative where 24 - s + r is odd: value = ((byte ^ m) - m) << (24 - s)
+    // with m the bits r of that parity (0xAA for even s, 0x55 for odd s)
+    const uint32_t m4 = 0xAAAAAAAAu >> (s & 1);
+    const uint32_t sh = (uint32_t)(24 - s);
+    const uint32_t negm = 0u - ((m4 & 0xFFu) << sh);
+    const uint32_t T[4] = {a0 ^ m4, a1 ^ m4, b0 ^ m4, b1 ^ m4};
 #pragma unroll
-  for (int k = 0; k < 16; k++)
-    q[seq_index(k)] = (int32_t)(((w[k] >> s) ^ kNegaMask) - kNegaMask);
+    for (int k = 0; k < 16; k++)
+      q[seq_index(k)] = (int32_t)((((T[k >> 2] >> (8 * (k & 3))) & 0xFFu) << sh) + negm);
+  } else {
+    // the remaining planes, then all 32 planes: w[15 - j] high half = plane j,
+    // w[31 - j] low half = plane j, and the 16x16 transposes
+#pragma unroll
+    for (int j = 8; j < 32; j++) {
+      uint32_t x = 0u;
+      if (pos < LIMIT) x = decode_plane<R>(acc, pos, n);
+      if (j & 1) Z[j >> 1] |= x << 16; else Z[j >> 1] = x;
+    }
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      w[15 - 2 * i] = byte_perm(Z[i], Z[8 + i], 0x05040100u);
+      w[14 - 2 * i] = byte_perm(Z[i], Z[8 + i], 0x07060302u);
+    }
+    transpose16x2(w);
+    // planes past the last one (j > 31 - s) lie below bit s of the shifted
+    // words and are dropped by the shift; the encoder codes them as zeros
+#pragma unroll
+    for (int k = 0; k < 16; k++)
+      q[seq_index(k)] = (int32_t)(((w[k] >> s) ^ kNegaMask) - kNegaMask);
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++) inv_xform4(q[i], q[4 + i], q[8 + i], q[12 + i]);
 #pragma unroll

@@ -21,13 +21,13 @@ static void enc(const float *v, unsigned char *out) {
   for (int i = 0; i < 2 * R; i++) out[i] = (unsigned char)(acc[i / 8] >> (8 * (i % 8)));
 }
 
-template <int R>
+template <int R, bool GENERAL>
 static void dec(const unsigned char *in, float *v) {
   uint64_t acc[cgz::Rate<R>::kAcc];
   for (int a = 0; a < cgz::Rate<R>::kAcc; a++) acc[a] = 0;
   for (int i = 0; i < 2 * R; i++) acc[i / 8] |= (uint64_t)in[i] << (8 * (i % 8));
   float b[16];
-  cgz::decode_block<R>(acc, b);
+  cgz::decode_block<R, GENERAL>(acc, b);
   memcpy(v, b, sizeof b);
 }
 
@@ -42,9 +42,20 @@ extern "C" int hc_encode_block(const float *v, int R, unsigned char *out) {
   return -1;
 }
 
+// the decoder as the kernels run it (8-plane reconstruction whenever it
+// applies to the block), and with the 32-plane reconstruction forced
 extern "C" int hc_decode_block(const unsigned char *in, int R, float *v) {
   switch (R) {
-#define C(r) case r: dec<r>(in, v); return 0;
+#define C(r) case r: dec<r, false>(in, v); return 0;
+    RATES(C)
+#undef C
+  }
+  return -1;
+}
+
+extern "C" int hc_decode_block_general(const unsigned char *in, int R, float *v) {
+  switch (R) {
+#define C(r) case r: dec<r, true>(in, v); return 0;
     RATES(C)
 #undef C
   }

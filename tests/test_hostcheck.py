@@ -24,6 +24,7 @@ def hc():
     L = ctypes.CDLL(LIB)
     L.hc_encode_block.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.hc_decode_block.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.hc_decode_block_general.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     return L
 
 
@@ -34,10 +35,11 @@ def enc(L, v, R):
     return o
 
 
-def dec(L, b, R):
+def dec(L, b, R, general=False):
     b = np.ascontiguousarray(b, np.uint8)
     o = np.zeros(16, np.float32)
-    assert L.hc_decode_block(b.ctypes.data, R, o.ctypes.data) == 0
+    fn = L.hc_decode_block_general if general else L.hc_decode_block
+    assert fn(b.ctypes.data, R, o.ctypes.data) == 0
     return o
 
 
@@ -49,7 +51,9 @@ def test_kv_blocks_bit_exact(hc, R):
             v = x[t:t + 4, c:c + 4].reshape(16)
             b = oracle.zfp_encode_block(v, R)
             assert np.array_equal(enc(hc, v, R), b)
-            assert np.array_equal(dec(hc, b, R).view(np.uint32), oracle.zfp_decode_block(b, R).view(np.uint32))
+            ref = oracle.zfp_decode_block(b, R).view(np.uint32)
+            assert np.array_equal(dec(hc, b, R).view(np.uint32), ref)
+            assert np.array_equal(dec(hc, b, R, general=True).view(np.uint32), ref)
 
 
 @pytest.mark.parametrize("R", RATES)
@@ -62,7 +66,9 @@ def test_wide_range_and_special_blocks(hc, R):
     for v in blocks:
         b = oracle.zfp_encode_block(v, R)
         assert np.array_equal(enc(hc, v, R), b)
-        assert np.array_equal(dec(hc, b, R).view(np.uint32), oracle.zfp_decode_block(b, R).view(np.uint32))
+        ref = oracle.zfp_decode_block(b, R).view(np.uint32)
+        assert np.array_equal(dec(hc, b, R).view(np.uint32), ref)
+        assert np.array_equal(dec(hc, b, R, general=True).view(np.uint32), ref)
 
 
 @pytest.mark.parametrize("R", RATES)
@@ -70,4 +76,6 @@ def test_random_streams(hc, R):
     rng = np.random.default_rng(100 + R)
     for _ in range(1500):
         b = rng.integers(0, 256, 2 * R).astype(np.uint8)
-        assert np.array_equal(dec(hc, b, R).view(np.uint32), oracle.zfp_decode_block(b, R).view(np.uint32))
+        ref = oracle.zfp_decode_block(b, R).view(np.uint32)
+        assert np.array_equal(dec(hc, b, R).view(np.uint32), ref)
+        assert np.array_equal(dec(hc, b, R, general=True).view(np.uint32), ref)
