@@ -240,8 +240,68 @@ __host__ __device__ __forceinline__ uint32_t window(const uint64_t (&acc)[Rate<R
   return r;
 }
 
-// Encode 16 fp32 values v[4j + i] (j = token row, i = channel) at rate R.
+// true when the predicate holds for any lane of the wave executing this call
+// (the host build decides per block)
+__host__ __device__ __forceinline__ bool wave_any(bool p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ballot_w64(p) != 0ull;
+#else
+  return p;
+#endif
+}
+
+__host__ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_perm(hi, lo, sel);
+#else
+  const uint64_t x = ((uint64_t)hi << 32) | lo;
+  uint32_t r = 0;
+  for (int i = 0; i < 4; i++) r |= (uint32_t)((x >> (8 * ((sel >> (8 * i)) & 7))) & 0xFFu) << (8 * i);
+  return r;
+#endif
+}
+
+// One coded bit plane.  For plane word w with n coefficients already
+// significant the code is: the n verbatim bits, then (if n < 16) either a
+// failed group test (0) or a 1 followed by the bits w[n..min(hb,14)] with
+// every 1 among them followed by one more bit -- 1 if another one follows in
+// the plane, 0 after the last one (hb = highest set bit; a one at position 15
+// is implied and not sent).  The "1 after every 1" expansion comes from the
+// 256-entry table `dbl`.  Fixed cost whatever the plane's content.
 template <int R>
+__host__ __device__ __forceinline__ void encode_plane(uint64_t (&acc)[Rate<R>::kAcc], uint32_t w,
+                                                      int &pos, int &n,
+                                                      const uint16_t *__restrict__ dbl) {
+  const uint32_t rest = w >> n;
+  const int hb1 = 32 - clz32(w | 1u);   // highest set bit + 1 (1 when w <= 1)
+  // scanned positions n .. min(hb, 14); when rest == 0 the code below is
+  // replaced by the failed test
+  const int L = max(min(hb1, 15), n) - n;
+  const uint32_t S = rest & ((1u << L) - 1u);
+  const uint32_t lo = S & 0xFFu, hi = S >> 8;
+  const int pclo = __builtin_popcount(lo), pc = pclo + __builtin_popcount(hi);
+  const uint32_t D = (uint32_t)dbl[lo] | ((uint32_t)dbl[hi] << (8 + pclo));
+  uint32_t code = 1u | (D << 1);
+  if (hb1 <= 15) code &= ~(1u << (L + pc));
+  int len = 1 + L + pc;
+  if (rest == 0) {
+    code = 0u;
+    len = n < 16 ? 1 : 0;
+  }
+  const uint64_t full = (uint64_t)(w & ((1u << n) - 1u)) | ((uint64_t)code << n);
+  put64<R>(acc, pos, full);
+  pos += n + len;
+  n = rest ? hb1 : n;
+}
+
+// Encode 16 fp32 values v[4j + i] (j = token row, i = channel) at rate R.
+// The planes are coded from the top, plane j = bit 31 - s - j of the
+// negabinary words (s = leading all-zero planes).  When no lane of the wave
+// has s > 24, planes 0..7 come from two 8x8 bit transposes of the words'
+// bytes at bits 31 - s .. 24 - s; the full 16x16 transposes are formed only
+// when some lane of the wave still has budget after 8 planes.  GENERAL = true
+// forces the full transposes (same stream).
+template <int R, bool GENERAL = false>
 __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
                                                       uint64_t (&acc)[Rate<R>::kAcc],
                                                       const uint16_t *__restrict__ dbl) {
@@ -279,66 +339,48 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
   if (any == 0) return;
   const int s = clz32(any);            // planes 31..32-s are all zero
   int pos = 9 + s;                      // one failed group test per zero plane
-#pragma unroll
-  for (int k = 0; k < 16; k++) u[k] <<= s;
-  transpose16x2(u);                     // u[m]: plane m (low), plane m+16 (high)
-
-  // Planes from the top, one fixed-cost step each.  For plane word w with n
-  // coefficients already significant the code is: the n verbatim bits, then
-  // (if n < 16) either a failed group test (0) or a 1 followed by the bits
-  // w[n..min(hb,14)] with every 1 among them followed by one more bit -- 1 if
-  // another one follows in the plane, 0 after the last one (hb = highest set
-  // bit; a one at position 15 is implied and not sent).  The "1 after every
-  // 1" expansion comes from the 256-entry table `dbl`.
   int n = 0;                            // coefficients already significant
+  uint32_t X[4];                        // planes 2i (low half) and 2i + 1 (high half)
+  bool transposed = false;
+  if (!GENERAL && !wave_any(s > 24)) {
+    // rows of two 8x8 bit matrices: the byte of coefficient k (plane 0 in
+    // bit 7), coefficients 0..7 and 8..15; transposed, byte c of a matrix is
+    // plane 7 - c of its eight coefficients
+    const int sh = 24 - s;
+    uint32_t r[4];
 #pragma unroll
-  for (int j = 0; j < 32; j++) {        // plane 31-j of the shifted words
-    if (pos < LIMIT) {                  // (no early exit: keeps the loop unrollable)
-      const uint32_t w = j < 16 ? (u[15 - j] >> 16) : (u[31 - j] & 0xFFFFu);
-      const uint32_t rest = w >> n;
-      const int hb1 = 32 - clz32(w | 1u);   // highest set bit + 1 (1 when w <= 1)
-      // scanned positions n .. min(hb, 14); when rest == 0 the code below is
-      // replaced by the failed test
-      const int L = max(min(hb1, 15), n) - n;
-      const uint32_t S = rest & ((1u << L) - 1u);
-      const uint32_t lo = S & 0xFFu, hi = S >> 8;
-      const int pclo = __builtin_popcount(lo), pc = pclo + __builtin_popcount(hi);
-      const uint32_t D = (uint32_t)dbl[lo] | ((uint32_t)dbl[hi] << (8 + pclo));
-      uint32_t code = 1u | (D << 1);
-      if (hb1 <= 15) code &= ~(1u << (L + pc));
-      int len = 1 + L + pc;
-      if (rest == 0) {
-        code = 0u;
-        len = n < 16 ? 1 : 0;
-      }
-      const uint64_t full = (uint64_t)(w & ((1u << n) - 1u)) | ((uint64_t)code << n);
-      put64<R>(acc, pos, full);
-      pos += n + len;
-      n = rest ? hb1 : n;
+    for (int i = 0; i < 4; i++)
+      r[i] = ((u[4 * i] >> sh) & 0xFFu) | (((u[4 * i + 1] >> sh) & 0xFFu) << 8) |
+             (((u[4 * i + 2] >> sh) & 0xFFu) << 16) | (((u[4 * i + 3] >> sh) & 0xFFu) << 24);
+    transpose8x8(r[0], r[1]);
+    transpose8x8(r[2], r[3]);
+    X[0] = byte_perm(r[3], r[1], 0x06020703u);
+    X[1] = byte_perm(r[3], r[1], 0x04000501u);
+    X[2] = byte_perm(r[2], r[0], 0x06020703u);
+    X[3] = byte_perm(r[2], r[0], 0x04000501u);
+  } else {
+    transposed = true;
+#pragma unroll
+    for (int k = 0; k < 16; k++) u[k] <<= s;
+    transpose16x2(u);                   // u[m]: plane m (low), plane m+16 (high)
+#pragma unroll
+    for (int i = 0; i < 4; i++) X[i] = byte_perm(u[14 - 2 * i], u[15 - 2 * i], 0x07060302u);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++)           // planes 0..7 (no early exit: keeps the loop unrollable)
+    if (pos < LIMIT) encode_plane<R>(acc, (X[j >> 1] >> (16 * (j & 1))) & 0xFFFFu, pos, n, dbl);
+  if (wave_any(pos < LIMIT)) {
+    if (!transposed) {
+#pragma unroll
+      for (int k = 0; k < 16; k++) u[k] <<= s;
+      transpose16x2(u);
     }
+#pragma unroll
+    for (int j = 8; j < 32; j++)        // plane 31-j of the shifted words
+      if (pos < LIMIT)
+        encode_plane<R>(acc, j < 16 ? (u[15 - j] >> 16) : (u[31 - j] & 0xFFFFu), pos, n, dbl);
   }
   if (LIMIT % 64) acc[NA - 1] &= (~0ull) >> (64 - LIMIT % 64);
-}
-
-// true when the predicate holds for any lane of the wave executing this call
-// (the host build decides per block)
-__host__ __device__ __forceinline__ bool wave_any(bool p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_amdgcn_ballot_w64(p) != 0ull;
-#else
-  return p;
-#endif
-}
-
-__host__ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_amdgcn_perm(hi, lo, sel);
-#else
-  const uint64_t x = ((uint64_t)hi << 32) | lo;
-  uint32_t r = 0;
-  for (int i = 0; i < 4; i++) r |= (uint32_t)((x >> (8 * ((sel >> (8 * i)) & 7))) & 0xFFu) << (8 * i);
-  return r;
-#endif
 }
 
 // Group-test/scan part of one bit plane, read bit-parallel from the window W

@@ -8,7 +8,7 @@
 static uint16_t g_dbl[256];
 static bool g_dbl_ready = false;
 
-template <int R>
+template <int R, bool GENERAL>
 static void enc(const float *v, unsigned char *out) {
   if (!g_dbl_ready) {
     for (int i = 0; i < 256; i++) g_dbl[i] = cgz::dbl8_entry((uint32_t)i);
@@ -17,7 +17,7 @@ static void enc(const float *v, unsigned char *out) {
   float b[16];
   memcpy(b, v, sizeof b);
   uint64_t acc[cgz::Rate<R>::kAcc];
-  cgz::encode_block<R>(b, acc, g_dbl);
+  cgz::encode_block<R, GENERAL>(b, acc, g_dbl);
   for (int i = 0; i < 2 * R; i++) out[i] = (unsigned char)(acc[i / 8] >> (8 * (i % 8)));
 }
 
@@ -33,9 +33,20 @@ static void dec(const unsigned char *in, float *v) {
 
 #define RATES(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(12) X(16)
 
+// the encoder as the kernels run it (planes 0..7 from the 8x8 transposes
+// whenever they apply to the block), and with the 16x16 transposes forced
 extern "C" int hc_encode_block(const float *v, int R, unsigned char *out) {
   switch (R) {
-#define C(r) case r: enc<r>(v, out); return 0;
+#define C(r) case r: enc<r, false>(v, out); return 0;
+    RATES(C)
+#undef C
+  }
+  return -1;
+}
+
+extern "C" int hc_encode_block_general(const float *v, int R, unsigned char *out) {
+  switch (R) {
+#define C(r) case r: enc<r, true>(v, out); return 0;
     RATES(C)
 #undef C
   }

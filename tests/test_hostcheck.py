@@ -23,15 +23,17 @@ def hc():
         __graft_entry__._build_hostcheck()
     L = ctypes.CDLL(LIB)
     L.hc_encode_block.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.hc_encode_block_general.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.hc_decode_block.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.hc_decode_block_general.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     return L
 
 
-def enc(L, v, R):
+def enc(L, v, R, general=False):
     v = np.ascontiguousarray(v, np.float32)
     o = np.zeros(2 * R, np.uint8)
-    assert L.hc_encode_block(v.ctypes.data, R, o.ctypes.data) == 0
+    fn = L.hc_encode_block_general if general else L.hc_encode_block
+    assert fn(v.ctypes.data, R, o.ctypes.data) == 0
     return o
 
 
@@ -51,6 +53,7 @@ def test_kv_blocks_bit_exact(hc, R):
             v = x[t:t + 4, c:c + 4].reshape(16)
             b = oracle.zfp_encode_block(v, R)
             assert np.array_equal(enc(hc, v, R), b)
+            assert np.array_equal(enc(hc, v, R, general=True), b)
             ref = oracle.zfp_decode_block(b, R).view(np.uint32)
             assert np.array_equal(dec(hc, b, R).view(np.uint32), ref)
             assert np.array_equal(dec(hc, b, R, general=True).view(np.uint32), ref)
@@ -66,6 +69,7 @@ def test_wide_range_and_special_blocks(hc, R):
     for v in blocks:
         b = oracle.zfp_encode_block(v, R)
         assert np.array_equal(enc(hc, v, R), b)
+        assert np.array_equal(enc(hc, v, R, general=True), b)
         ref = oracle.zfp_decode_block(b, R).view(np.uint32)
         assert np.array_equal(dec(hc, b, R).view(np.uint32), ref)
         assert np.array_equal(dec(hc, b, R, general=True).view(np.uint32), ref)
