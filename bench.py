@@ -8,15 +8,19 @@ at 20x per head), gauge g = 16 from A ~ N(0, 0.1^2), zfp-style fixed rate
 4 bits/value.  One step = gauge + encode of the whole cache followed by
 decode + inverse gauge of the whole cache; inputs are resident in HBM.
 
-Prints one JSON line: the metric, value (round-trip KV GB/s), timing, the
-configuration, per-direction figures, the roofline object of the slower
-kernel (algorithmic bytes per launch over its HIP-event time, against the
-8 TB/s HBM peak, with the rocprofv3-measured HBM traffic and VALU
-instruction count when the kernel sources match the ones the counters were
-taken on; the instruction rate is also given as a fraction of the chip's
-single-issue VALU rate, the resource these coders are bound by) and the CPU
-oracle baseline on a bounded sample.  --workload selects other workloads, one JSON
-line each.
+Prints one JSON line: the metric, value (round-trip KV GB/s), timing
+(medians of HIP-event times), the configuration, per-direction figures, the
+roofline object of the slower kernel (algorithmic bytes per launch over its
+HIP-event time, against the 8 TB/s HBM peak and against the streaming-kernel
+ceiling measured in the same run; the rocprofv3-measured HBM traffic and
+VALU instruction count when the kernel sources match the ones the counters
+were taken on, with the instruction rate against the chip's single-issue
+VALU rate; `bound` names the resource with the larger measured fraction),
+the CPU oracle baseline on a bounded sample, and `configs`: the encode and
+decode figures of every other workload (small fp32 cache, the other zfp
+rates, the full-head gauge quantizers, the rolling history, the 27B-class
+cache and its gauge-fit statistics), measured in the same run.
+--workload selects the detailed lines of one workload, one JSON line each.
 """
 from __future__ import annotations
 
@@ -45,10 +49,11 @@ VALU_ISSUE_PEAK_GPS = 256 * 4 * 2.4 / 4
 # reports null once the hash of those sources differs.
 PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "gauge128.hpp", "zfp_block.hpp", "zfp_kernels.hpp",
                "zfp_r4.hip", "kernels_zfp.hip")
-PMC_TRAFFIC = {"sha256": "a2d7008c60ff0d14b4f6b501d0e5fc7e0f6a0e286e92a80ec5416b6badc70fde",
-               "k_zfp_encode": 5402493440, "k_zfp_decode": 5402647936,
+PMC_TRAFFIC = {"sha256": "cf13f7ba6a96b3fa4d24bcb046e6016ec97057f7422c1a181e9808f62e77a502",
+               # FETCH_SIZE x 2 + WRITE_SIZE x 1 (KiB -> B), per launch
+               "k_zfp_encode": 5402861568, "k_zfp_decode": 5404357427,
                # SQ_INSTS_VALU per launch (rocprofv3 --pmc, same sources)
-               "valu_k_zfp_encode": 1474195984, "valu_k_zfp_decode": 1958951029}
+               "valu_k_zfp_encode": 1348859585, "valu_k_zfp_decode": 1598336909}
 
 CFG = dict(layers=32, kv=2, batch=1, heads=8, tokens=32768, head_dim=128, g=16, rate=4,
            rho=0.95, outliers=4, seed=2)
@@ -132,10 +137,22 @@ def time_steps(s, steps, warmup):
     return wall, enc, dec
 
 
-def cpu_baseline(s, n_fields=64):
+def host_threads() -> int:
+    """Worker threads for the CPU baseline: the cores this process may run on,
+    at most 16 (a one-GPU machine's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(s):
     """The oracle (plain C + numpy, untuned) on a bounded sample of the same
-    workload: n_fields fields (layers 0..1 of the cache), full round trip,
-    one field per worker thread."""
+    workload: every field of layers 0, L/2 and L-1 (K and V, all heads), a
+    full round trip (gauge, encode, decode, inverse gauge) per field, one
+    field per worker thread; the rate and a labelled extrapolation of the
+    whole cache's time at that rate."""
     import concurrent.futures as cf
 
     import torch
@@ -145,9 +162,10 @@ def cpu_baseline(s, n_fields=64):
     D, T, R, g = s["D"], s["T"], s["R"], s["g"]
     L, KV, H = CFG["layers"], CFG["kv"], CFG["heads"]
     Gh = s["G"].cpu().numpy().reshape(L, KV, H, D // g, g, g)
-    fields = list(range(min(n_fields, s["F"])))
+    layers = sorted({0, L // 2, L - 1})
+    fields = [(l * KV + kv) * H + h for l in layers for kv in range(KV) for h in range(H)]
     host = [x[f].view(torch.int16).cpu().numpy().view(np.uint16) for f in fields]
-    threads = max(1, min(16, os.cpu_count() or 1, len(fields)))
+    threads = min(host_threads(), len(fields))
 
     def one(i):
         f = fields[i]
@@ -160,9 +178,14 @@ def cpu_baseline(s, n_fields=64):
         list(ex.map(one, range(len(fields))))
     wall = time.perf_counter() - t0
     nvals = len(fields) * T * D
-    return dict(value=round(nvals * 2 / wall / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
-                sample=f"{len(fields)} of {s['F']} fields ({nvals} values), gauge+encode+decode+"
-                       f"inverse round trip, {wall:.2f} s wall on {threads} threads")
+    rate = nvals * 2 / wall / 1e9
+    return dict(value=round(rate, 4), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"all {len(fields)} fields of layers {layers} ({nvals} values, "
+                       f"{len(fields)} of {s['F']} fields), gauge+encode+decode+inverse round trip, "
+                       f"{wall:.2f} s wall on {threads} threads",
+                extrapolated_full_cache_s=round(s["N"] * 2 / 1e9 / rate, 2),
+                extrapolation="labelled estimate: the whole cache's round trip at the sampled rate "
+                              "(fields are independent and equal in size)")
 
 
 # ---------------------------------------------------------------------------
@@ -210,10 +233,10 @@ def _time(fn, steps, warmup):
         b.record()
         ts.append((a, b))
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e-3
+    return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e-3
 
 
-def _codec_line(name, shape, x, G, g, codec, steps, warmup, esz, desc):
+def _codec_line(name, shape, x, G, g, codec, steps, warmup, esz, desc, folded=True):
     import torch
 
     from fixed_rate_compression_amd import binding as cg
@@ -236,11 +259,11 @@ def _codec_line(name, shape, x, G, g, codec, steps, warmup, esz, desc):
     tde = _time(dece, steps, warmup)
     summ = cg.cg_cache_error_summary(shape, err.cpu().numpy())
     # recovery folded into the consumer: values (or keys and values) left gauged
-    folded = {}
-    if g:
+    fold = {}
+    if g and folded:
         for nm, keep in (("values", cg.CG_KEEP_VALUES), ("both", cg.CG_KEEP_KEYS | cg.CG_KEEP_VALUES)):
             fn = lambda keep=keep: cg.cg_decode_gauged(shape, pay, meta, gauge, codec, 0, T, keep, out)
-            folded[f"decode_folded_{nm}_ms"] = round(_time(fn, steps, warmup) * 1e3, 4)
+            fold[f"decode_folded_{nm}_ms"] = round(_time(fn, steps, warmup) * 1e3, 4)
     N = x.numel()
     alg = N * esz + pb + mb
     del pay, meta, out, ws
@@ -252,7 +275,7 @@ def _codec_line(name, shape, x, G, g, codec, steps, warmup, esz, desc):
             "encode_ms": round(te * 1e3, 4), "decode_ms": round(td * 1e3, 4),
             "encode_kv_GBs": round(N * esz / te / 1e9, 2), "decode_kv_GBs": round(N * esz / td / 1e9, 2),
             "encode_hbm_frac": round(alg / te / 1e9 / HBM_PEAK_GBS, 4),
-            "decode_hbm_frac": round(alg / td / 1e9 / HBM_PEAK_GBS, 4), **folded}
+            "decode_hbm_frac": round(alg / td / 1e9 / HBM_PEAK_GBS, 4), **fold}
 
 
 def small_lines(steps, warmup):
@@ -301,7 +324,24 @@ def llama8b_lines(steps, warmup):
     return lines
 
 
-def fullhead_lines(steps, warmup):
+def llama8b_rate_lines(steps, warmup, rates=(3, 6)):
+    """the other zfp rates of the Llama-3-8B-class cache (g = 16)"""
+    import torch
+
+    from fixed_rate_compression_amd import binding as cg
+    L, KV, B, H, T = 32, 2, 1, 8, 32768
+    x = _gen(L * KV * B * H, T, T, 0.95, 2, 4, True)
+    G, _ = _gauge(L, KV, H, 16, 102)
+    sh = cg.make_shape(L, KV, B, H, T, T, 128, cg.CG_DTYPE_BF16)
+    lines = [_codec_line(f"llama8b_zfp{R}", sh, x, G, 16, cg.make_codec(cg.CG_BACKEND_ZFP, R), steps,
+                         warmup, 2, "32 layers x K/V x 8 heads x 32768 tokens bf16, g=16", folded=False)
+             for R in rates]
+    del x
+    torch.cuda.empty_cache()
+    return lines
+
+
+def fullhead_lines(steps, warmup, folded=True):
     """full-head gauge (g = 128, MFMA): KIVI-2/4 (group 32, 128-token tail), block-uniform 3-bit"""
     import torch
 
@@ -315,21 +355,23 @@ def fullhead_lines(steps, warmup):
                       (cg.make_codec(cg.CG_BACKEND_KIVI, 4, 32, 128), "kivi4"),
                       (cg.make_codec(cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64), "bu3")):
         lines.append(_codec_line(f"fullhead_{nm}", sh, x, G, 128, codec, steps, warmup, 2,
-                                 "32 layers x K/V x 8 heads x 131072 tokens bf16, dense g=128"))
+                                 "32 layers x K/V x 8 heads x 131072 tokens bf16, dense g=128",
+                                 folded=folded))
     del x
     torch.cuda.empty_cache()
     return lines
 
 
-def rolling_line():
-    """rolling history: 64 seq x 28 layers x 4 heads, 8192 -> 8192 + 256 tokens, g = 32, 4 b/v"""
+def rolling_line(modes=True, appends=256):
+    """rolling history: 64 seq x 28 layers x 4 heads, 8192 -> 8192 + 256 tokens, g = 32, 4 b/v
+    (modes=False: the workload's own mode only; appends < 256 times the first appends only)"""
     import torch
 
     from fixed_rate_compression_amd import binding as cg
     from fixed_rate_compression_amd.rolling import RollingHistory
-    L, KV, B, H, T0, nsteps = 28, 2, 64, 4, 8192, 256
-    cap = T0 + nsteps
-    raw = _gen(L * KV * B * H, T0 + nsteps, cap, 0.95, 4, 4, True)
+    L, KV, B, H, T0, nsteps = 28, 2, 64, 4, 8192, appends
+    cap = T0 + 256
+    raw = _gen(L * KV * B * H, cap, cap, 0.95, 4, 4, True)
     G, _ = _gauge(L, KV, H, 32, 104)
 
     def run(every_token, keep):
@@ -347,22 +389,21 @@ def rolling_line():
         return a.elapsed_time(b) / nsteps
 
     ms = run(False, 0)                      # the workload: encode each completed 4-token block
-    ms_every = run(True, 0)                 # every token through the codec
-    ms_folded = run(True, cg.CG_KEEP_KEYS | cg.CG_KEEP_VALUES)
     Nmean = L * KV * B * H * 128 * (T0 + nsteps / 2)
     line = {"workload": "rolling_g32_zfp4", "desc": "64 seq x 28 layers x 4 heads, history 8192+, "
             f"{nsteps} appends (encode each completed 4-token block, decode + inverse-gauge the whole history)",
             "ms_per_step": round(ms, 4), "history_values_mean": int(Nmean),
             "decode_kv_GBs": round(Nmean * 2 / (ms * 1e-3) / 1e9, 2),
-            "decode_hbm_frac": round(Nmean * 2.5 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "ms_per_step_every_token": round(ms_every, 4),
-            "ms_per_step_every_token_folded": round(ms_folded, 4)}
+            "decode_hbm_frac": round(Nmean * 2.5 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if modes:
+        line["ms_per_step_every_token"] = round(run(True, 0), 4)   # every token through the codec
+        line["ms_per_step_every_token_folded"] = round(run(True, cg.CG_KEEP_KEYS | cg.CG_KEEP_VALUES), 4)
     del raw
     torch.cuda.empty_cache()
     return line
 
 
-def b27_codec_line(steps, warmup):
+def b27_codec_line(steps, warmup, folded=True):
     """27B-class cache, zfp-3, g = 16"""
     import torch
 
@@ -372,7 +413,7 @@ def b27_codec_line(steps, warmup):
     G, _ = _gauge(L, KV, H, 16, 105)
     sh = cg.make_shape(L, KV, B, H, T, T, 128, cg.CG_DTYPE_BF16)
     line = _codec_line("27b_zfp3", sh, x, G, 16, cg.make_codec(cg.CG_BACKEND_ZFP, 3), steps, warmup, 2,
-                       "46 layers x K/V x 16 heads x 65536 tokens bf16, g=16")
+                       "46 layers x K/V x 16 heads x 65536 tokens bf16, g=16", folded=folded)
     del x
     torch.cuda.empty_cache()
     return line
@@ -413,7 +454,7 @@ def stats_line():
 WORKLOADS = ("small", "llama8b-rates", "fullhead", "rolling", "27b", "stats", "fit")
 
 
-def workload_lines(names, steps, warmup):
+def workload_lines(names, steps, warmup, appends=256):
     lines = []
     for nm in names:
         if nm == "small":
@@ -423,7 +464,7 @@ def workload_lines(names, steps, warmup):
         elif nm == "fullhead":
             lines += fullhead_lines(max(3, steps // 4), 1)
         elif nm == "rolling":
-            lines.append(rolling_line())
+            lines.append(rolling_line(appends=appends))
         elif nm == "27b":
             lines.append(b27_codec_line(steps, warmup))
         elif nm == "stats":
@@ -472,15 +513,51 @@ def fit_line(epochs=25):
     return out
 
 
+def config_summaries(steps, warmup):
+    """Encode/decode figures of every other workload, measured in this run
+    (medians of HIP-event times): the compact form of the --workload lines."""
+    import torch
+
+    keep = ("values", "bits_per_value", "encode_ms", "decode_ms", "encode_hbm_frac", "decode_hbm_frac",
+            "kv_nrmse")
+
+    def compact(line):
+        return {k: line[k] for k in keep if k in line}
+
+    out = {}
+    log("configs: small fp32 cache")
+    out["small_fp32_g16"] = {ln["workload"]: compact(ln) for ln in small_lines(steps, warmup)}
+    log("configs: Llama-3-8B-class cache at 3 and 6 b/v")
+    out["llama8b_g16_other_rates"] = {ln["workload"]: compact(ln)
+                                      for ln in llama8b_rate_lines(steps, warmup)}
+    log("configs: full-head gauge quantizers")
+    out["fullhead_g128"] = {ln["workload"]: compact(ln)
+                            for ln in fullhead_lines(max(3, steps // 2), 1, folded=False)}
+    log("configs: rolling history")
+    rl = rolling_line(modes=False)
+    out["rolling_g32_zfp4"] = {k: rl[k] for k in ("ms_per_step", "history_values_mean", "decode_hbm_frac")}
+    log("configs: 27B-class cache and its gauge-fit statistics")
+    out["27b_g16"] = {"zfp3": compact(b27_codec_line(steps, warmup, folded=False))}
+    st = stats_line()
+    out["27b_g16"]["stats"] = {k: st[k] for k in ("values", "wall_s_with_grad", "wall_s_stats_only",
+                                                   "kv_GBs_with_grad", "kv_GBs_stats_only")}
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads' figures (the `configs` key)")
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "all"] + list(WORKLOADS),
                     help="llama8b: the headline line only; all: the headline line, then one JSON "
                          "line per other workload; any other name: only that workload's lines")
+    ap.add_argument("--appends", type=int, default=256,
+                    help="rolling workload: appends timed (256 = the whole workload)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain device copy of the KV tensor (counter calibration)")
     args = ap.parse_args()
@@ -492,9 +569,11 @@ def main():
     import torch
     torch.cuda.set_device(0)
     if args.workload in WORKLOADS:
-        for line in workload_lines([args.workload], max(3, args.steps // 2), 1):
+        for line in workload_lines([args.workload], max(3, args.steps // 2), 1, args.appends):
             print(json.dumps(line), flush=True)
         return
+    from fixed_rate_compression_amd import probe
+
     log("setup: generating the synthetic cache on the device")
     s = setup()
     if args.copy_probe:
@@ -505,12 +584,20 @@ def main():
     N, R = s["N"], s["R"]
     kv_bytes = N * 2
     alg = N * 2 + N * R // 8            # read bf16 + write payload (and the reverse)
-    t_enc, t_dec = float(enc.mean()), float(dec.mean())
+    t_enc, t_dec = float(np.median(enc)), float(np.median(dec))
     ms_step = (t_enc + t_dec) * 1e3
     value = kv_bytes / (t_enc + t_dec) / 1e9
     dom = "encode" if t_enc >= t_dec else "decode"
     t_dom = max(t_enc, t_dec)
     achieved = alg / t_dom / 1e9
+    log("streaming-kernel memory ceiling")
+    ceil = probe.ceilings(s["x"])
+    ceil_dom = ceil["enc" if dom == "encode" else "dec"]["GBs"]
+    n_valu, valu_gps = valu_rate(f"k_zfp_{dom}", t_dom)
+    issue_frac = round(valu_gps / VALU_ISSUE_PEAK_GPS, 4) if valu_gps else None
+    hbm_frac = round(achieved / HBM_PEAK_GBS, 4)
+    # the resource the kernel is bound by: the one with the larger measured fraction
+    bound = "alu" if issue_frac is not None and issue_frac > achieved / ceil_dom else "hbm"
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -522,39 +609,46 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32+i32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": "Llama-3-8B-class GQA KV cache round trip: 32 layers x K/V x 8 KV heads x "
                         "head_dim 128 x 32768 tokens, bf16 storage, gauge g=16, zfp-style 4 b/v",
             "values": N, "storage": "bf16", "gauge_group": s["g"], "zfp_rate": R,
+            "compute": "fp32 gauge (matrix-core fmaf chains), int32 block coder",
             "global_batch": 1, "seq_len": s["T"], "parallelism": "none (1 GPU)",
+            "timing": "median of HIP-event times per direction",
         },
         "encode": {"ms": round(t_enc * 1e3, 4), "kv_GBs": round(kv_bytes / t_enc / 1e9, 2),
                    "hbm_GBs": round(alg / t_enc / 1e9, 2),
-                   "hbm_frac": round(alg / t_enc / 1e9 / HBM_PEAK_GBS, 4)},
+                   "hbm_frac": round(alg / t_enc / 1e9 / HBM_PEAK_GBS, 4),
+                   "frac_of_stream_ceiling": round(alg / t_enc / 1e9 / ceil["enc"]["GBs"], 4)},
         "decode": {"ms": round(t_dec * 1e3, 4), "kv_GBs": round(kv_bytes / t_dec / 1e9, 2),
                    "hbm_GBs": round(alg / t_dec / 1e9, 2),
-                   "hbm_frac": round(alg / t_dec / 1e9 / HBM_PEAK_GBS, 4)},
+                   "hbm_frac": round(alg / t_dec / 1e9 / HBM_PEAK_GBS, 4),
+                   "frac_of_stream_ceiling": round(alg / t_dec / 1e9 / ceil["dec"]["GBs"], 4)},
         "bits_per_value": round(8.0 * (s["pbytes"] + s["hbytes"]) / N, 6),
         "wall_s": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": f"k_zfp_{dom}", "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": bound, "kernel": f"k_zfp_{dom}", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hbm_frac,
                      "traffic": measured_traffic(f"k_zfp_{dom}"),
-                     "valu_instr_per_launch": valu_rate(f"k_zfp_{dom}", t_dom)[0],
-                     "valu_ginstr_per_s": valu_rate(f"k_zfp_{dom}", t_dom)[1],
-                     "valu_issue_frac": (round(valu_rate(f"k_zfp_{dom}", t_dom)[1] / VALU_ISSUE_PEAK_GPS, 4)
-                                         if valu_rate(f"k_zfp_{dom}", t_dom)[1] else None),
-                     "alg_bytes_per_launch": alg},
+                     "alg_bytes_per_launch": alg,
+                     "stream_ceiling_GBs": ceil_dom,
+                     "frac_of_stream_ceiling": round(achieved / ceil_dom, 4),
+                     "alu": {"valu_instr_per_launch": n_valu, "achieved": valu_gps,
+                             "peak": VALU_ISSUE_PEAK_GPS, "unit": "G wave64 VALU instructions/s",
+                             "frac": issue_frac}},
+        "stream_ceilings": ceil,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(s)
+    del s
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        res["configs"] = config_summaries(max(3, args.steps // 4), 1)
     print(json.dumps(res), flush=True)
     if args.workload == "all":
-        del s
-        torch.cuda.empty_cache()
         for line in workload_lines(WORKLOADS, max(3, args.steps // 2), 1):
             print(json.dumps(line), flush=True)
 

@@ -1,0 +1,93 @@
+"""Streaming HBM kernels (libcgprobe.so) that move bytes in the codec
+kernels' read : write proportions with no other work: the practical memory
+ceiling the zfp kernels are quoted against next to the 8 TB/s peak.
+Measurement only; nothing on the codec path uses them."""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "stream.hip")
+_LIB = os.path.join(_HERE, "libcgprobe.so")
+
+MODES = {"copy": (0, 1, 1), "enc": (1, 4, 1), "dec": (2, 1, 4)}   # name: (mode, read, write)
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call([
+            "hipcc", "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (bind to torch's HIP runtime first)
+        if not os.path.exists(_LIB):
+            raise RuntimeError("libcgprobe.so is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(_LIB)
+        L.cgprobe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                     ctypes.c_uint64, ctypes.c_void_p]
+        L.cgprobe_stream.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def stream(name: str, src, dst, stream=None) -> None:
+    """Launch the `name` kernel ('copy', 'enc', 'dec') over all of src (torch
+    device tensors; dst sized for the mode's write share)."""
+    import torch
+    mode, rin, rout = MODES[name]
+    nb = src.numel() * src.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    rc = lib().cgprobe_stream(mode, src.data_ptr(), nb, dst.data_ptr(),
+                              dst.numel() * dst.element_size(), s)
+    if rc != 0:
+        raise RuntimeError(f"cgprobe_stream({name}) failed with {rc}")
+
+
+def ceilings(kv, steps: int = 10, warmup: int = 2) -> dict:
+    """HBM GB/s (bytes read + written per second, median over `steps` timed
+    launches) of the three kernels on the tensor `kv` (the copy and the
+    encode-shaped kernel read it; the decode-shaped kernel reads a quarter
+    of its size and writes its full size)."""
+    import numpy as np
+    import torch
+    nb = kv.numel() * kv.element_size()
+    flat = kv.view(torch.uint8).view(-1)
+    out = {}
+    for name in ("copy", "enc", "dec"):
+        _, rin, rout = MODES[name]
+        if name == "dec":
+            src = flat[: nb // 4]
+            dst = torch.empty(nb, dtype=torch.uint8, device=kv.device)
+        else:
+            src = flat
+            dst = torch.empty(nb * rout // rin, dtype=torch.uint8, device=kv.device)
+        moved = src.numel() + dst.numel()
+        for _ in range(warmup):
+            stream(name, src, dst)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            stream(name, src, dst)
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e-3
+        out[name] = {"GBs": round(moved / t / 1e9, 1), "ms": round(t * 1e3, 4), "bytes": moved}
+        del dst
+        torch.cuda.empty_cache()
+    return out
