@@ -22,7 +22,7 @@ CG_BACKEND_NONE, CG_BACKEND_ZFP, CG_BACKEND_BLOCK_UNIFORM, CG_BACKEND_KIVI = 0, 
 CG_HEADER_BYTES = 64
 
 EXPORTED = ["cg_encoded_bytes", "cg_encode", "cg_decode", "cg_decode_gauged", "cg_roundtrip",
-            "cg_gauge_fit_stats", "cg_stats_workspace_bytes", "cg_gauge_from_skew",
+            "cg_gauge_fit_stats", "cg_gauge_fit_grad", "cg_stats_workspace_bytes", "cg_gauge_from_skew",
             "cg_gauge_apply", "cg_write_header", "cg_decode_error_workspace_bytes",
             "cg_decode_error", "cg_decode_error_noalloc", "cg_cache_error_summary", "cg_adamw_update", "cg_gauge_control",
             "cg_second_moment_workspace_bytes", "cg_second_moment", "cg_gauge_grad", "cg_gauge_heads",
@@ -97,6 +97,8 @@ def lib():
             "cg_gauge_heads": [SP, GP, I32, I32, I32, I64, I32, P, P, P],
             "cg_roundtrip": [SP, P, GP, CP, P, U64, P, U64, P, P],
             "cg_gauge_fit_stats": [SP, P, I32, P, I32, ctypes.c_float, ctypes.c_float,
+                                   ctypes.c_float, P, ctypes.c_size_t, P, P, P],
+            "cg_gauge_fit_grad": [SP, P, I32, P, I32, ctypes.c_float, ctypes.c_float,
                                    ctypes.c_float, P, ctypes.c_size_t, P, P, P],
             "cg_stats_workspace_bytes": [SP, I32, I32, ctypes.POINTER(ctypes.c_size_t)],
             "cg_gauge_from_skew": [I64, I32, P, P],
@@ -331,6 +333,24 @@ def cg_gauge_fit_stats(shape, kv, g, A_host: np.ndarray, T_b, tau, lambda_f, lam
         lambda_f, lambda_r,
         _ptr(workspace), _nbytes(workspace), ctypes.cast(out, ctypes.c_void_p),
         dA.ctypes.data if grad else None, _stream(stream)))
+    stats = np.array([(o.L_freq, o.L_rate, o.L, o.sum_E) for o in out],
+                     dtype=[("L_freq", "f8"), ("L_rate", "f8"), ("L", "f8"), ("sum_E", "f8")])
+    return stats, dA
+
+
+def cg_gauge_fit_grad(shape, kv, g, A_host: np.ndarray, T_b, tau, lambda_f, lambda_r, workspace,
+                      stream=None):
+    """Returns (stats structured array [n_fields], dA fp64 [L, KV, H, D/g, g, g]
+    summed over the batch, or None for g = 0)."""
+    nf = shape.layers * shape.kv * shape.batch * shape.heads
+    out = (CgStats * nf)()
+    A = np.ascontiguousarray(A_host, np.float64) if A_host is not None else None
+    dA = (np.zeros((shape.layers, shape.kv, shape.heads, shape.head_dim // g, g, g), np.float64)
+          if g else None)
+    _check("cg_gauge_fit_grad", lib().cg_gauge_fit_grad(
+        ctypes.byref(shape), _ptr(kv), g, A.ctypes.data if A is not None else None, T_b, tau,
+        lambda_f, lambda_r, _ptr(workspace), _nbytes(workspace), ctypes.cast(out, ctypes.c_void_p),
+        dA.ctypes.data if g else None, _stream(stream)))
     stats = np.array([(o.L_freq, o.L_rate, o.L, o.sum_E) for o in out],
                      dtype=[("L_freq", "f8"), ("L_rate", "f8"), ("L", "f8"), ("sum_E", "f8")])
     return stats, dA

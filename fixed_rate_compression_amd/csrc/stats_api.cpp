@@ -1,4 +1,4 @@
-// cg_gauge_fit_stats / cg_stats_workspace_bytes: host side of the gauge-fit
+// cg_gauge_fit_stats / cg_gauge_fit_grad / cg_stats_workspace_bytes: host side of the gauge-fit
 // statistics ("Codec-Gauge", arXiv HTML, frequency-objective and
 // gauge-training paragraphs).  The host builds G = exp(A - A^T) and the DCT
 // tables in fp64 (rounded to fp32 for the device), launches the statistics
@@ -98,10 +98,13 @@ extern "C" int cg_stats_workspace_bytes(const cg_shape *shape, int32_t g, int32_
   return CG_OK;
 }
 
-extern "C" int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t g,
-                                  const double *A_host, int32_t T_b, float tau, float lambda_f,
-                                  float lambda_r, void *workspace, size_t ws_bytes,
-                                  cg_stats *out_host, double *dA_host, void *stream) {
+namespace {
+
+// per_gauge: dA_host holds one gradient per gauge (layer, kind, head), the sum
+// over the batch of its fields' gradients, else one per field
+int fit_stats(const cg_shape *shape, const void *kv, int32_t g, const double *A_host, int32_t T_b,
+              float tau, float lambda_f, float lambda_r, void *workspace, size_t ws_bytes,
+              cg_stats *out_host, double *dA_host, bool per_gauge, void *stream) {
   int rc = validate(shape, g, T_b);
   if (rc) return rc;
   if (!kv || !workspace || !out_host) return fail(CG_E_INVAL, "kv, workspace or out is NULL");
@@ -199,14 +202,21 @@ extern "C" int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t
   }
   if (!a.grad) return CG_OK;
 
-  // dA per field and group: Psi = L_exp(S^T, Gamma), dA = Psi - Psi^T
+  // dA per field (or per gauge) and group: Psi = L_exp(S^T, Gamma),
+  // dA = Psi - Psi^T.  Per gauge, Gamma is the sum over the batch (b = 0, 1,
+  // ... in order) of its fields' Gamma: the Frechet derivative is linear in
+  // its direction, so this is the sum of the fields' gradients.
   const int gg = g * g;
-  auto work = [&](int64_t f0, int64_t f1, int *bad) {
+  const int64_t B = shape->batch, H = shape->heads;
+  const int64_t items = per_gauge ? ngauge : F;
+  auto work = [&](int64_t i0, int64_t i1, int *bad) {
     std::vector<double> St(gg), Gam(gg), Psi(gg);
-    for (int64_t f = f0; f < f1; f++) {
-      const int64_t ls = f / ((int64_t)shape->batch * shape->heads), h = f % shape->heads;
-      const int64_t gidx = ls * shape->heads + h;
-      const double *r = res.data() + (size_t)f * width + 4;
+    for (int64_t it = i0; it < i1; it++) {
+      // item -> its gauge and the fields whose Gamma it takes
+      const int64_t gidx = per_gauge ? it : (it / (B * H)) * H + it % H;
+      const int64_t ls = gidx / H, h = gidx % H;
+      const int64_t fb0 = per_gauge ? ls * B * H + h : it;   // first field
+      const int64_t nfb = per_gauge ? B : 1;                 // fields, H apart
       for (int q = 0; q < R; q++) {
         const double *A = A_host + ((size_t)gidx * R + q) * gg;
         for (int i = 0; i < g; i++)
@@ -215,30 +225,52 @@ extern "C" int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t
         // g = 8 -> diagonal block q % 2 of tile q / 2
         for (int i = 0; i < g; i++)
           for (int j = 0; j < g; j++) {
-            double v;
-            if (g == 16) v = r[q * 256 + i * 16 + j];
-            else if (g == 8) v = r[(q / 2) * 256 + (8 * (q % 2) + i) * 16 + 8 * (q % 2) + j];
-            else v = r[(q * 4 + (i / 16) * 2 + (j / 16)) * 256 + (i % 16) * 16 + (j % 16)];
+            double v = 0.0;
+            for (int64_t b = 0; b < nfb; b++) {
+              const double *r = res.data() + (size_t)(fb0 + b * H) * width + 4;
+              if (g == 16) v += r[q * 256 + i * 16 + j];
+              else if (g == 8) v += r[(q / 2) * 256 + (8 * (q % 2) + i) * 16 + 8 * (q % 2) + j];
+              else v += r[(q * 4 + (i / 16) * 2 + (j / 16)) * 256 + (i % 16) * 16 + (j % 16)];
+            }
             Gam[i * g + j] = v;
           }
         if (!frechet(g, St.data(), Gam.data(), Psi.data())) { *bad = 1; return; }
-        double *out = dA_host + ((size_t)f * R + q) * gg;
+        double *out = dA_host + ((size_t)it * R + q) * gg;
         for (int i = 0; i < g; i++)
           for (int j = 0; j < g; j++) out[i * g + j] = Psi[i * g + j] - Psi[j * g + i];
       }
     }
   };
-  const unsigned nth = host_threads(F);
+  const unsigned nth = host_threads(items);
   std::vector<std::thread> pool;
   std::vector<int> bad(nth, 0);
   for (unsigned t = 0; t < nth; t++) {
-    const int64_t f0 = F * t / nth, f1 = F * (t + 1) / nth;
-    pool.emplace_back(work, f0, f1, &bad[t]);
+    const int64_t i0 = items * t / nth, i1 = items * (t + 1) / nth;
+    pool.emplace_back(work, i0, i1, &bad[t]);
   }
   for (auto &th : pool) th.join();
   for (int b : bad)
     if (b) return fail(CG_E_INTERNAL, "Frechet derivative failed");
   return CG_OK;
+}
+
+}  // namespace
+
+extern "C" int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t g,
+                                  const double *A_host, int32_t T_b, float tau, float lambda_f,
+                                  float lambda_r, void *workspace, size_t ws_bytes,
+                                  cg_stats *out_host, double *dA_host, void *stream) {
+  return fit_stats(shape, kv, g, A_host, T_b, tau, lambda_f, lambda_r, workspace, ws_bytes,
+                   out_host, dA_host, false, stream);
+}
+
+extern "C" int cg_gauge_fit_grad(const cg_shape *shape, const void *kv, int32_t g,
+                                 const double *A_host, int32_t T_b, float tau, float lambda_f,
+                                 float lambda_r, void *workspace, size_t ws_bytes,
+                                 cg_stats *out_host, double *dA_gauge_host, void *stream) {
+  if (g != 0 && !dA_gauge_host) return fail(CG_E_INVAL, "dA is NULL");
+  return fit_stats(shape, kv, g, A_host, T_b, tau, lambda_f, lambda_r, workspace, ws_bytes,
+                   out_host, dA_gauge_host, true, stream);
 }
 
 /* dL/dA from dL/dG for G = exp(A - A^T), per matrix (host, fp64). */

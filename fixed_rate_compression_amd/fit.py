@@ -85,10 +85,10 @@ class GaugeTrainer:
     def step(self, w: int) -> float:
         """One AdamW step on window w; returns the mean objective L before it."""
         o = self.obj
-        st, dA = cg.cg_gauge_fit_stats(self.shape, _window(self.x, w, self.Tw), self.g, self.A, o["T_b"],
-                                       o["tau"], o["lambda_f"], o["lambda_r"], self.ws, grad=True)
-        # fields (l, s, b, h) share the gauge (l, s, h): sum the gradient over b
-        grad = dA.reshape(self.L, self.KV, self.B, self.H, *self.A.shape[3:]).sum(axis=2)
+        # fields (l, s, b, h) share the gauge (l, s, h): the library returns the
+        # gradient of the batch objective per gauge
+        st, grad = cg.cg_gauge_fit_grad(self.shape, _window(self.x, w, self.Tw), self.g, self.A,
+                                         o["T_b"], o["tau"], o["lambda_f"], o["lambda_r"], self.ws)
         self.t += 1
         flat = [np.ascontiguousarray(a).reshape(-1) for a in (self.A, grad, self.m, self.v)]
         cg.cg_adamw_update(flat[0], flat[1], flat[2], flat[3], self.t, **self.hyper)

@@ -281,7 +281,22 @@ int cg_gauge_fit_stats(const cg_shape *shape, const void *kv, int32_t g, const d
                        int32_t T_b, float tau, float lambda_f, float lambda_r, void *workspace,
                        size_t ws_bytes, cg_stats *out_host, double *dA_host, void *stream);
 
-/* Device scratch needed by cg_gauge_fit_stats (host only). */
+/*
+ * cg_gauge_fit_stats with the gradient of the training objective per gauge
+ * (gauge-training paragraph, arXiv page: one gauge per layer, K/V, head and
+ * group, shared by every sequence of the batch and trained with AdamW on the
+ * frequency objective of the cached windows): dA_gauge_host fp64
+ * [layers][kv][heads][d/g][g][g] = sum over b = 0..batch-1 of the gradient of
+ * field (l, s, b, h)'s L with respect to A[l][s][h], i.e. the gradient of
+ * sum_b L(l, s, b, h).  The batch sum is taken on dL/dG before the Frechet
+ * adjoint (a linear map), in b order.  dA_gauge_host must not be NULL when
+ * g != 0 (CG_E_INVAL); everything else as cg_gauge_fit_stats.  Synchronous.
+ */
+int cg_gauge_fit_grad(const cg_shape *shape, const void *kv, int32_t g, const double *A_host,
+                      int32_t T_b, float tau, float lambda_f, float lambda_r, void *workspace,
+                      size_t ws_bytes, cg_stats *out_host, double *dA_gauge_host, void *stream);
+
+/* Device scratch needed by cg_gauge_fit_stats and cg_gauge_fit_grad (host only). */
 int cg_stats_workspace_bytes(const cg_shape *shape, int32_t g, int32_t T_b, size_t *bytes);
 
 /*
