@@ -60,6 +60,51 @@ __device__ __forceinline__ void unstage_block(const uint32_t *os, int b, uint64_
   }
 }
 
+// Even rates: a block's 16R bits are R/2 aligned 32-bit words, so a lane
+// loads or stores its own block's code directly (the 64 lanes of a wave touch
+// 64 consecutive blocks: one contiguous span).  Odd rates stage through LDS.
+template <int R>
+struct BlockCode {
+  static constexpr bool kDirect = R % 2 == 0 && R <= 8;
+  static constexpr int NW = kDirect ? R / 2 : 1;
+  uint32_t w[NW];
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ p) {
+    const uint32_t *q = (const uint32_t *)p;
+    if constexpr (NW == 1) {
+      w[0] = q[0];
+    } else if constexpr (NW == 2) {
+      const uint2 t = *(const uint2 *)q;
+      w[0] = t.x; w[1] = t.y;
+    } else if constexpr (NW == 3) {
+      const uint3 t = *(const uint3 *)q;
+      w[0] = t.x; w[1] = t.y; w[2] = t.z;
+    } else {
+      const uint4 t = *(const uint4 *)q;
+      w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+    }
+  }
+  __device__ __forceinline__ void to_acc(uint64_t (&acc)[cgz::Rate<R>::kAcc]) const {
+#pragma unroll
+    for (int a = 0; a < cgz::Rate<R>::kAcc; a++) acc[a] = 0;
+#pragma unroll
+    for (int h = 0; h < NW; h++) acc[h / 2] |= (uint64_t)w[h] << (32 * (h % 2));
+  }
+};
+
+template <int R>
+__device__ __forceinline__ void store_block_code(uint8_t *__restrict__ p,
+                                                 const uint64_t (&acc)[cgz::Rate<R>::kAcc]) {
+  constexpr int NW = R / 2;
+  uint32_t w[NW];
+#pragma unroll
+  for (int h = 0; h < NW; h++) w[h] = (uint32_t)(acc[h / 2] >> (32 * (h % 2)));
+  uint32_t *q = (uint32_t *)p;
+  if constexpr (NW == 1) q[0] = w[0];
+  else if constexpr (NW == 2) *(uint2 *)q = make_uint2(w[0], w[1]);
+  else if constexpr (NW == 3) *(uint3 *)q = make_uint3(w[0], w[1], w[2]);
+  else *(uint4 *)q = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Gauges g <= 32: a workgroup walks a.chunk_tiles consecutive tiles of
 // one field and loads tile i+1 (KV rows, or code words) into registers while
 // it codes tile i.
@@ -107,6 +152,7 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
       __syncthreads();
     }
     const int nblk = ((nrows + 3) / 4) * 32;
+    uint8_t *dst = payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R;
     for (int b = threadIdx.x; b < nblk; b += NT) {
       const float *src = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
       float v[16];
@@ -117,12 +163,16 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
       }
       uint64_t acc[cgz::Rate<R>::kAcc];
       cgz::encode_block<R>(v, acc, dbl);
-      stage_block<R>(os, b, acc);
+      if constexpr (BlockCode<R>::kDirect)
+        store_block_code<R>(dst + (size_t)b * 2 * R, acc);
+      else
+        stage_block<R>(os, b, acc);
     }
-    __syncthreads();  // codes staged; every thread is done with xs
-    uint4 *dst = (uint4 *)(payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R);
-    const int n16 = nblk * 2 * R / 16;
-    for (int i = threadIdx.x; i < n16; i += NT) dst[i] = ((const uint4 *)os)[i];
+    __syncthreads();  // every thread is done with xs (and the codes are staged)
+    if constexpr (!BlockCode<R>::kDirect) {
+      const int n16 = nblk * 2 * R / 16;
+      for (int i = threadIdx.x; i < n16; i += NT) ((uint4 *)dst)[i] = ((const uint4 *)os)[i];
+    }
   }
 }
 
@@ -165,25 +215,55 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
     return (const uint4 *)(payload + (size_t)(field * (a.tcap / 4) + (a.t0 + (int64_t)tile * TILE_T) / 4) * 32 * 2 * R);
   };
   auto n16 = [&](int tile) { return ((rows(tile) + 3) / 4) * 32 * 2 * R / 16; };
-  CodeFetch<R> pre;
-  if (tile0 < tend) pre.fetch(codes(tile0), n16(tile0));
+  auto nblocks = [&](int tile) { return ((rows(tile) + 3) / 4) * 32; };
+  constexpr bool kDirect = BlockCode<R>::kDirect;
+  constexpr int BPT = TILE_T / 4 * 32 / NT;   // blocks per thread and tile
+  CodeFetch<R> pre;                            // odd rates: the tile's code words
+  BlockCode<R> pc[BPT];                        // even rates: this thread's blocks
+  auto fetch = [&](int tile) {
+    if constexpr (kDirect) {
+      const uint8_t *c = (const uint8_t *)codes(tile);
+      const int nb = nblocks(tile);
+#pragma unroll
+      for (int i = 0; i < BPT; i++) {
+        const int b = threadIdx.x + NT * i;
+        if (b < nb) pc[i].load(c + (size_t)b * 2 * R);
+      }
+    } else {
+      pre.fetch(codes(tile), n16(tile));
+    }
+  };
+  if (tile0 < tend) fetch(tile0);
   ErrAcc err;
   for (int tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
     const int nrows = rows(tile);
     const int nblk = ((nrows + 3) / 4) * 32;
-    pre.put(os, n16(tile));
-    __syncthreads();
-    if (tile + 1 < tend) pre.fetch(codes(tile + 1), n16(tile + 1));
-    for (int b = threadIdx.x; b < nblk; b += NT) {
-      uint64_t acc[cgz::Rate<R>::kAcc];
-      unstage_block<R>(os, b, acc);
-      float v[16];
-      cgz::decode_block<R>(acc, v);
-      float *dst = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
+    BlockCode<R> cur[BPT];
+    if constexpr (kDirect) {
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        *(float4 *)(dst + j * PITCH) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+      for (int i = 0; i < BPT; i++) cur[i] = pc[i];
+    } else {
+      pre.put(os, n16(tile));
+      __syncthreads();
+    }
+    if (tile + 1 < tend) fetch(tile + 1);
+#pragma unroll
+    for (int i = 0; i < BPT; i++) {
+      const int b = threadIdx.x + NT * i;
+      if (b < nblk) {
+        uint64_t acc[cgz::Rate<R>::kAcc];
+        if constexpr (kDirect)
+          cur[i].to_acc(acc);
+        else
+          unstage_block<R>(os, b, acc);
+        float v[16];
+        cgz::decode_block<R>(acc, v);
+        float *dst = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          *(float4 *)(dst + j * PITCH) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+      }
     }
     __syncthreads();
     if constexpr (G != 0) {
@@ -195,7 +275,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
       store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
     else
       store_tile<BF16>((uint8_t *)out + off, nrows, xs);
-    __syncthreads();  // xs and os are rewritten by the next tile
+    __syncthreads();  // xs (and os) are rewritten by the next tile
   }
   if (a.ref) write_err(err, a.epart);
 }
@@ -238,6 +318,7 @@ __global__ __launch_bounds__(NT) void k_zfp_encode128(const void *__restrict__ k
       __syncthreads();
     }
     const int nblk = ((nrows + 3) / 4) * 32;
+    uint8_t *dst = payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R;
     for (int b = threadIdx.x; b < nblk; b += NT) {
       const float *src = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
       float v[16];
@@ -248,12 +329,16 @@ __global__ __launch_bounds__(NT) void k_zfp_encode128(const void *__restrict__ k
       }
       uint64_t acc[cgz::Rate<R>::kAcc];
       cgz::encode_block<R>(v, acc, dbl);
-      stage_block<R>(os, b, acc);
+      if constexpr (BlockCode<R>::kDirect)
+        store_block_code<R>(dst + (size_t)b * 2 * R, acc);
+      else
+        stage_block<R>(os, b, acc);
     }
-    __syncthreads();  // codes staged; every thread is done with xs
-    uint4 *dst = (uint4 *)(payload + (size_t)(field * (a.tcap / 4) + tb / 4) * 32 * 2 * R);
-    const int n16 = nblk * 2 * R / 16;
-    for (int i = threadIdx.x; i < n16; i += NT) dst[i] = ((const uint4 *)os)[i];
+    __syncthreads();  // every thread is done with xs (and the codes are staged)
+    if constexpr (!BlockCode<R>::kDirect) {
+      const int n16 = nblk * 2 * R / 16;
+      for (int i = threadIdx.x; i < n16; i += NT) ((uint4 *)dst)[i] = ((const uint4 *)os)[i];
+    }
   }
 }
 
