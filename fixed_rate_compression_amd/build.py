@@ -4,7 +4,8 @@ Every translation unit under csrc/ is compiled with hipcc in parallel into
 _build/, then linked into fixed_rate_compression_amd/lib/libcodecgauge.so.
 Flags: FMA contraction off (the gauge's fmaf chains and the quantizers'
 separate multiply/add must round as written), correctly rounded fp32
-division (hipcc default), packed-FP32 instruction selection disabled.
+division (hipcc default), packed-FP32 instruction selection disabled,
+matrix-core accumulators in VGPRs (no AGPR copies around each product).
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 

@@ -78,8 +78,8 @@ __host__ __device__ __forceinline__ void fwd_xform4(int32_t &a, int32_t &b, int3
 // exact inverse of every lifting step, in reverse order (mod 2^32).  Each
 // undone rotation pair (u += v; v = 2v - u) is written as u' = u + v,
 // v' = v - u (old u), which is the same value mod 2^32 in two operations.
-__host__ __device__ __forceinline__ void inv_xform4(int32_t &a, int32_t &b, int32_t &c,
-                                                    int32_t &d) {
+__host__ __device__ __forceinline__ constexpr void inv_xform4(int32_t &a, int32_t &b, int32_t &c,
+                                                              int32_t &d) {
   uint32_t A = (uint32_t)a, B = (uint32_t)b, C = (uint32_t)c, Dd = (uint32_t)d;
   B = B + (uint32_t)(d >> 1);
   Dd = Dd - (uint32_t)((int32_t)B >> 1);
@@ -455,16 +455,21 @@ __host__ __device__ __forceinline__ uint32_t decode_plane(const uint64_t (&acc)[
   return x;
 }
 
-// Decode one block of 16R bits into 16 fp32 values v[4j + i].  Plane j (from
-// the top) is bit 31 - s - j of the negabinary coefficient words, held as
-// 16-bit plane words, two per register: Z[i] = plane 2i | plane 2i+1 << 16.
-// GENERAL = true forces the 32-plane reconstruction (both give the same
-// values whenever the 8-plane one applies).
-template <int R, bool GENERAL = false>
-__host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate<R>::kAcc],
-                                                      float (&v)[16]) {
+// A block after its header and planes 0..7.  Plane j (from the top) is bit
+// 31 - s - j of the negabinary coefficient words, held as 16-bit plane
+// words, two per register: Z[i] = plane 2i | plane 2i+1 << 16 (Z[4..15] are
+// filled only by the 32-plane path).  pos < 16R: budget left after plane 7.
+template <int R>
+struct BlockParse {
+  uint32_t Z[16];
+  int emax, s, pos, n;
+};
+
+template <int R>
+__host__ __device__ __forceinline__ void decode_planes8(const uint64_t (&acc)[Rate<R>::kAcc],
+                                                        BlockParse<R> &st) {
   constexpr int LIMIT = Rate<R>::kBits;
-  const int emax = (int)((acc[0] >> 1) & 0xFFu) - 127;
+  st.emax = (int)((acc[0] >> 1) & 0xFFu) - 127;
   const uint32_t win = window<R>(acc, 9);
   int s = win ? ctz32(win) : 32;        // leading failed group tests
   int pos = 9 + s;
@@ -472,48 +477,73 @@ __host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate
     pos = LIMIT;                                     // every integer is 0
     s = 0;
   }
-  uint32_t Z[16];
   int n = 0;
 #pragma unroll
   for (int j = 0; j < 8; j++) {
     uint32_t x = 0u;
     if (pos < LIMIT) x = decode_plane<R>(acc, pos, n);
-    if (j & 1) Z[j >> 1] |= x << 16; else Z[j >> 1] = x;
+    if (j & 1) st.Z[j >> 1] |= x << 16; else st.Z[j >> 1] = x;
   }
+  st.s = s;
+  st.pos = pos;
+  st.n = n;
+}
+
+// Planes 0..7 (s <= 24) as one byte per coefficient: byte k & 3 of T[k >> 2]
+// holds coefficient k (sequency order) with plane 0 in bit 7, XORed with the
+// negabinary mask of its parity, so that its value is (byte - m) << (24 - s)
+// with m = 0xAA for even s and 0x55 for odd s.  Rows r = 0..7 of two 8x8
+// bit matrices are the low (coefficients 0..7) and high (8..15) bytes of
+// plane 7 - r; transposed, byte c of a matrix holds coefficient c's planes.
+__host__ __device__ __forceinline__ void plane_bytes(const uint32_t (&Z)[16], int s,
+                                                     uint32_t (&T)[4]) {
+  uint32_t a0 = byte_perm(Z[3], Z[2], 0x00020406u), a1 = byte_perm(Z[1], Z[0], 0x00020406u);
+  uint32_t b0 = byte_perm(Z[3], Z[2], 0x01030507u), b1 = byte_perm(Z[1], Z[0], 0x01030507u);
+  transpose8x8(a0, a1);
+  transpose8x8(b0, b1);
+  const uint32_t m4 = 0xAAAAAAAAu >> (s & 1);
+  T[0] = a0 ^ m4;
+  T[1] = a1 ^ m4;
+  T[2] = b0 ^ m4;
+  T[3] = b1 ^ m4;
+}
+
+// The remaining planes (if the budget lasts past plane 7), the reconstruction
+// of the 16 integers, the inverse transform and the scaling.  GENERAL = true
+// forces the 32-plane reconstruction (both give the same values whenever the
+// 8-plane one applies).
+template <int R, bool GENERAL = false>
+__host__ __device__ __forceinline__ void decode_finish(const uint64_t (&acc)[Rate<R>::kAcc],
+                                                       BlockParse<R> &st, float (&v)[16]) {
+  constexpr int LIMIT = Rate<R>::kBits;
+  const int s = st.s;
   int32_t q[16];
-  if (!GENERAL && !wave_any(pos < LIMIT || s > 24)) {
-    // Planes 0..7 only, s <= 24.  Rows r = 0..7 of two 8x8 bit matrices are
-    // the low (coefficients 0..7) and high (8..15) bytes of plane 7 - r;
-    // transposed, byte c of a matrix holds coefficient c's planes with plane
-    // 0 in bit 7, i.e. the top byte of its shifted word.
-    uint32_t a0 = byte_perm(Z[3], Z[2], 0x00020406u), a1 = byte_perm(Z[1], Z[0], 0x00020406u);
-    uint32_t b0 = byte_perm(Z[3], Z[2], 0x01030507u), b1 = byte_perm(Z[1], Z[0], 0x01030507u);
-    transpose8x8(a0, a1);
-    transpose8x8(b0, b1);
-    // negabinary digits of a byte at bit 24 - s + r weigh +-2^(24 - s + r),
-    // negative where 24 - s + r is odd: value = ((byte ^ m) - m) << (24 - s)
-    // with m the bits r of that parity (0xAA for even s, 0x55 for odd s)
-    const uint32_t m4 = 0xAAAAAAAAu >> (s & 1);
+  if (!GENERAL && !wave_any(st.pos < LIMIT || s > 24)) {
+    // Planes 0..7 only, s <= 24: negabinary digits of a byte at bit 24 - s + r
+    // weigh +-2^(24 - s + r), negative where 24 - s + r is odd:
+    // value = ((byte ^ m) - m) << (24 - s)
+    uint32_t T[4];
+    plane_bytes(st.Z, s, T);
     const uint32_t sh = (uint32_t)(24 - s);
-    const uint32_t negm = 0u - ((m4 & 0xFFu) << sh);
-    const uint32_t T[4] = {a0 ^ m4, a1 ^ m4, b0 ^ m4, b1 ^ m4};
+    const uint32_t negm = 0u - (((0xAAAAAAAAu >> (s & 1)) & 0xFFu) << sh);
 #pragma unroll
     for (int k = 0; k < 16; k++)
       q[seq_index(k)] = (int32_t)((((T[k >> 2] >> (8 * (k & 3))) & 0xFFu) << sh) + negm);
   } else {
     // the remaining planes, then all 32 planes: w[15 - j] high half = plane j,
     // w[31 - j] low half = plane j, and the 16x16 transposes
+    int pos = st.pos, n = st.n;
 #pragma unroll
     for (int j = 8; j < 32; j++) {
       uint32_t x = 0u;
       if (pos < LIMIT) x = decode_plane<R>(acc, pos, n);
-      if (j & 1) Z[j >> 1] |= x << 16; else Z[j >> 1] = x;
+      if (j & 1) st.Z[j >> 1] |= x << 16; else st.Z[j >> 1] = x;
     }
     uint32_t w[16];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      w[15 - 2 * i] = byte_perm(Z[i], Z[8 + i], 0x05040100u);
-      w[14 - 2 * i] = byte_perm(Z[i], Z[8 + i], 0x07060302u);
+      w[15 - 2 * i] = byte_perm(st.Z[i], st.Z[8 + i], 0x05040100u);
+      w[14 - 2 * i] = byte_perm(st.Z[i], st.Z[8 + i], 0x07060302u);
     }
     transpose16x2(w);
     // planes past the last one (j > 31 - s) lie below bit s of the shifted
@@ -526,8 +556,124 @@ __host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate
   for (int i = 0; i < 4; i++) inv_xform4(q[i], q[4 + i], q[8 + i], q[12 + i]);
 #pragma unroll
   for (int j = 0; j < 4; j++) inv_xform4(q[4 * j], q[4 * j + 1], q[4 * j + 2], q[4 * j + 3]);
+  const int emax = st.emax;
 #pragma unroll
   for (int k = 0; k < 16; k++) v[k] = ldexpf((float)q[k], emax - 30);
+}
+
+// Decode one block of 16R bits into 16 fp32 values v[4j + i].
+template <int R, bool GENERAL = false>
+__host__ __device__ __forceinline__ void decode_block(const uint64_t (&acc)[Rate<R>::kAcc],
+                                                      float (&v)[16]) {
+  BlockParse<R> st;
+  decode_planes8<R>(acc, st);
+  decode_finish<R, GENERAL>(acc, st, v);
+}
+
+// ---------------------------------------------------------------------------
+// Lifted reconstruction of the 8-plane case.
+//
+// With planes 0..7 only and s <= 20 the integers entering the inverse
+// transform are d_k * 2^(24 - s), d_k = (byte_k ^ m) - m in [-170, 170]; on
+// 16 d_k every halving of the lifting steps meets an even value, so the
+// transform is the exact linear map  out = (A d) * 2^(20 - s)  with the
+// integer matrix A[p][k] = L4[p >> 2][q >> 2] * L4[p & 3][q & 3]  (q the
+// position of sequency coefficient k, L4 = 4 x the 4-point inverse lifting,
+// |A| <= 36), as long as no value of the 32-bit lifting leaves the int32
+// range.  Every intermediate value of the lifting is bounded in magnitude by
+// the largest output (each is a partial forward transform of the outputs,
+// whose rows have absolute sum <= 1), so the condition is |out| < 2^31, i.e.
+// |decoded value| < 2^(emax + 1).  A d is one int8 matrix-core product per
+// wave on the GPU: d_k = int8(byte_k ^ 0x80) + beta, beta = 128 - m, whose
+// constant part beta * rowsum(A) is preset in the accumulator together with
+// 0x4B400000 (1.5 * 2^23), so that the float with the accumulator's bits is
+// 1.5 * 2^23 + (A d)_p exactly and one fma with 2^e and -1.5 * 2^(23+e)
+// (e = emax - 10 - s) yields the decoded value.
+
+// 4 x entry (a, b) of the 4-point inverse lifting, computed by the lifting
+// itself on 4 e_b (no halving there meets an odd value)
+__host__ __device__ constexpr int lift4(int a, int b) {
+  int32_t x[4] = {0, 0, 0, 0};
+  x[b] = 4;
+  inv_xform4(x[0], x[1], x[2], x[3]);
+  return x[a];
+}
+
+__host__ __device__ constexpr int lift_coef(int p, int k) {
+  const int q = seq_index(k);
+  return lift4(p >> 2, q >> 2) * lift4(p & 3, q & 3);
+}
+
+// A and its row sums, evaluated at compile time
+struct LiftTable {
+  int8_t a[16][16];
+  int32_t rowsum[16];
+};
+
+__host__ __device__ constexpr LiftTable make_lift_table() {
+  LiftTable t{};
+  for (int p = 0; p < 16; p++) {
+    int sum = 0;
+    for (int k = 0; k < 16; k++) {
+      t.a[p][k] = (int8_t)lift_coef(p, k);
+      sum += lift_coef(p, k);
+    }
+    t.rowsum[p] = sum;
+  }
+  return t;
+}
+
+constexpr LiftTable kLift = make_lift_table();
+
+constexpr int32_t kLiftMagic = 0x4B400000;  // bits of 1.5 * 2^23
+
+// per-block constants of the lifted reconstruction; ok = false where it
+// does not apply (budget left after plane 7, s > 20, or scales out of the
+// normal float range)
+struct LiftScale {
+  int beta;       // 128 - m
+  float scale;    // 2^e
+  float offset;   // -1.5 * 2^(23 + e)
+  float limit;    // 2^(emax + 1): every |value| must stay below it
+  bool ok;
+};
+
+template <int R>
+__host__ __device__ __forceinline__ LiftScale lift_scale(const BlockParse<R> &st) {
+  LiftScale ls;
+  // no digit set (empty block, or no plane reached): every value is +0
+  const bool empty = (st.Z[0] | st.Z[1] | st.Z[2] | st.Z[3]) == 0u;
+  const int e = empty ? 0 : st.emax - 10 - st.s;
+  const int lim = empty ? 0 : st.emax + 1;
+  ls.beta = (st.s & 1) ? 43 : -42;
+  ls.ok = st.pos >= Rate<R>::kBits && (empty || (st.s <= 20 && e >= -126 && e <= 104 && lim <= 127));
+  const int ec = ls.ok ? e : 0, lc = ls.ok ? lim : 0;
+  ls.scale = __builtin_bit_cast(float, (uint32_t)(ec + 127) << 23);
+  ls.offset = __builtin_bit_cast(float, 0x80400000u | ((uint32_t)(ec + 150) << 23));
+  ls.limit = __builtin_bit_cast(float, (uint32_t)(lc + 127) << 23);
+  return ls;
+}
+
+// CPU model of the lifted reconstruction (the sum over k is the matrix-core
+// product on the GPU); returns false where it does not apply, including a
+// value at or beyond the limit.
+template <int R>
+__host__ bool decode_block_lifted(const uint64_t (&acc)[Rate<R>::kAcc], float (&v)[16]) {
+  BlockParse<R> st;
+  decode_planes8<R>(acc, st);
+  const LiftScale ls = lift_scale<R>(st);
+  if (!ls.ok) return false;
+  uint32_t T[4];
+  plane_bytes(st.Z, st.s, T);
+  bool inside = true;
+  for (int p = 0; p < 16; p++) {
+    int32_t a = kLiftMagic + ls.beta * kLift.rowsum[p];
+    for (int k = 0; k < 16; k++)
+      a += kLift.a[p][k] * (int32_t)(int8_t)(uint8_t)(((T[k >> 2] >> (8 * (k & 3))) & 0xFFu) ^ 0x80u);
+    v[p] = fmaf(__builtin_bit_cast(float, a), ls.scale, ls.offset);
+    inside = inside && fabsf(v[p]) < ls.limit;
+  }
+  return inside;
 }
 
 }  // namespace cgz

@@ -105,6 +105,73 @@ __device__ __forceinline__ void store_block_code(uint8_t *__restrict__ p,
   else *(uint4 *)q = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Lifted reconstruction on the matrix cores (zfp_block.hpp, "Lifted
+// reconstruction"): one v_mfma_i32_32x32x32_i8 per wave computes A d for the
+// wave's 64 blocks.  B operand: lane l = (n = l % 32, g = l / 32) gives its
+// own block's 16 digit bytes as k-group g.  Result D[m][n] lands in lane
+// n + 32 ((m >> 2) & 1), register (m >> 3) * 4 + (m & 3); rows m with
+// ((m >> 2) & 1) == g take block (n, g)'s coefficients, as output
+// p = ((m >> 3) << 2) | (m & 3), so each lane receives its own block's 16
+// values with register r = output position r.  A operand: lane l holds row
+// m = l % 32, k-group l / 32.
+typedef int cg_v4i __attribute__((ext_vector_type(4)));
+typedef int cg_v16i __attribute__((ext_vector_type(16)));
+
+struct LiftRows {
+  uint32_t w[16][4];  // row p of A as 16 int8, k = 4 * word + byte
+};
+
+__host__ __device__ constexpr LiftRows make_lift_rows() {
+  LiftRows t{};
+  for (int p = 0; p < 16; p++)
+    for (int k = 0; k < 16; k++)
+      t.w[p][k >> 2] |= (uint32_t)(uint8_t)cgz::kLift.a[p][k] << (8 * (k & 3));
+  return t;
+}
+
+__constant__ LiftRows kLiftRows = make_lift_rows();
+
+__device__ __forceinline__ cg_v4i lift_operand() {
+  const int l = threadIdx.x & 63, m = l & 31;
+  const bool mine = (l >> 5) == ((m >> 2) & 1);
+  const int p = ((m >> 3) << 2) | (m & 3);
+  cg_v4i a;
+#pragma unroll
+  for (int j = 0; j < 4; j++) a[j] = mine ? (int)kLiftRows.w[p][j] : 0;
+  return a;
+}
+
+// Wave-uniform: false (nothing stored) unless every lane's block takes the
+// lifted reconstruction; then the 16 values are stored at dst (row pitch
+// PITCH).  Called with all 64 lanes active.
+template <int R>
+__device__ __forceinline__ bool lifted_tail(const cg_v4i &liftA, const cgz::BlockParse<R> &st,
+                                            float *dst) {
+  const cgz::LiftScale ls = cgz::lift_scale<R>(st);
+  if (cgz::wave_any(!ls.ok)) return false;
+  uint32_t T[4];
+  cgz::plane_bytes(st.Z, st.s, T);
+  cg_v4i B;
+#pragma unroll
+  for (int j = 0; j < 4; j++) B[j] = (int)(T[j] ^ 0x80808080u);
+  cg_v16i C;
+#pragma unroll
+  for (int r = 0; r < 16; r++) C[r] = cgz::kLiftMagic + ls.beta * cgz::kLift.rowsum[r];
+  const cg_v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(liftA, B, C, 0, 0, 0);
+  float v[16];
+  float mx = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    v[r] = fmaf(__int_as_float(D[r]), ls.scale, ls.offset);
+    mx = fmaxf(mx, fabsf(v[r]));
+  }
+  if (cgz::wave_any(!(mx < ls.limit))) return false;
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    *(float4 *)(dst + j * PITCH) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+  return true;
+}
+
 // Gauges g <= 32: a workgroup walks a.chunk_tiles consecutive tiles of
 // one field and loads tile i+1 (KV rows, or code words) into registers while
 // it codes tile i.
@@ -234,6 +301,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
     }
   };
   if (tile0 < tend) fetch(tile0);
+  const cg_v4i liftA = lift_operand();
   ErrAcc err;
   for (int tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
@@ -248,18 +316,27 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
       __syncthreads();
     }
     if (tile + 1 < tend) fetch(tile + 1);
+    // every lane takes part (the lifted reconstruction is a wave-wide
+    // product): lanes past the tile's blocks decode an empty block into
+    // rows the gauge and the store do not read
 #pragma unroll
     for (int i = 0; i < BPT; i++) {
       const int b = threadIdx.x + NT * i;
-      if (b < nblk) {
-        uint64_t acc[cgz::Rate<R>::kAcc];
-        if constexpr (kDirect)
-          cur[i].to_acc(acc);
-        else
-          unstage_block<R>(os, b, acc);
+      uint64_t acc[cgz::Rate<R>::kAcc];
+      if constexpr (kDirect)
+        cur[i].to_acc(acc);
+      else
+        unstage_block<R>(os, b, acc);
+      if (b >= nblk) {
+#pragma unroll
+        for (int a2 = 0; a2 < cgz::Rate<R>::kAcc; a2++) acc[a2] = 0;
+      }
+      float *dst = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
+      cgz::BlockParse<R> st;
+      cgz::decode_planes8<R>(acc, st);
+      if (!lifted_tail<R>(liftA, st, dst)) {
         float v[16];
-        cgz::decode_block<R>(acc, v);
-        float *dst = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
+        cgz::decode_finish<R>(acc, st, v);
 #pragma unroll
         for (int j = 0; j < 4; j++)
           *(float4 *)(dst + j * PITCH) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);

@@ -72,3 +72,32 @@ extern "C" int hc_decode_block_general(const unsigned char *in, int R, float *v)
   }
   return -1;
 }
+
+template <int R>
+static int dec_lifted(const unsigned char *in, float *v) {
+  uint64_t acc[cgz::Rate<R>::kAcc];
+  for (int a = 0; a < cgz::Rate<R>::kAcc; a++) acc[a] = 0;
+  for (int i = 0; i < 2 * R; i++) acc[i / 8] |= (uint64_t)in[i] << (8 * (i % 8));
+  float b[16];
+  const bool applied = cgz::decode_block_lifted<R>(acc, b);
+  memcpy(v, b, sizeof b);
+  return applied ? 1 : 0;
+}
+
+// the lifted (matrix-core) reconstruction's arithmetic on the CPU: 1 where it
+// applies to the block (v written), 0 where the kernels take another path
+extern "C" int hc_decode_block_lifted(const unsigned char *in, int R, float *v) {
+  switch (R) {
+#define C(r) case r: return dec_lifted<r>(in, v);
+    RATES(C)
+#undef C
+  }
+  return -1;
+}
+
+// the integer matrix of the lifted reconstruction, A[p][k] (row p = output
+// position 4j + i, column k = sequency index)
+extern "C" void hc_lift_matrix(int *a) {
+  for (int p = 0; p < 16; p++)
+    for (int k = 0; k < 16; k++) a[16 * p + k] = cgz::kLift.a[p][k];
+}

@@ -26,6 +26,8 @@ def hc():
     L.hc_encode_block_general.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.hc_decode_block.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.hc_decode_block_general.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.hc_decode_block_lifted.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.hc_lift_matrix.argtypes = [ctypes.c_void_p]
     return L
 
 
@@ -83,3 +85,58 @@ def test_random_streams(hc, R):
         ref = oracle.zfp_decode_block(b, R).view(np.uint32)
         assert np.array_equal(dec(hc, b, R).view(np.uint32), ref)
         assert np.array_equal(dec(hc, b, R, general=True).view(np.uint32), ref)
+
+
+def dec_lifted(L, b, R):
+    b = np.ascontiguousarray(b, np.uint8)
+    o = np.zeros(16, np.float32)
+    applied = L.hc_decode_block_lifted(b.ctypes.data, R, o.ctypes.data)
+    assert applied in (0, 1)
+    return o if applied else None
+
+
+def test_lift_matrix_inverts_the_forward_transform(hc):
+    """The integer matrix of the lifted reconstruction, divided by 16, is the
+    inverse of the separable forward transform F (x) F with Lindstrom's
+    F = 1/16 [[4,4,4,4],[5,1,-1,-5],[-4,4,4,-4],[-2,6,-6,2]] (zfp paper,
+    decorrelating transform), columns in total-sequency order."""
+    a = np.zeros(256, np.int32)
+    hc.hc_lift_matrix(a.ctypes.data)
+    a = a.reshape(16, 16).astype(np.float64)
+    F = np.array([[4, 4, 4, 4], [5, 1, -1, -5], [-4, 4, 4, -4], [-2, 6, -6, 2]], np.float64) / 16
+    seq = [0, 1, 4, 5, 2, 8, 6, 9, 3, 12, 10, 7, 13, 11, 14, 15]
+    a_pos = np.zeros_like(a)
+    a_pos[:, seq] = a
+    Fi = np.linalg.inv(F)
+    assert np.abs(a_pos / 16 - np.kron(Fi, Fi)).max() < 1e-12
+    assert np.abs(a).max() <= 127
+
+
+@pytest.mark.parametrize("R", RATES)
+def test_lifted_reconstruction_bit_exact(hc, R):
+    """Where the lifted (matrix-core) reconstruction applies, it gives the
+    oracle's values bit for bit; on KV data at 2-8 bits/value it applies to
+    almost every block."""
+    x = synth.kv_field_cpu(1, R, 128, 128, 0.95, 4)
+    applied = total = 0
+    for t in range(0, 128, 4):
+        for c in range(0, 128, 4):
+            b = oracle.zfp_encode_block(x[t:t + 4, c:c + 4].reshape(16), R)
+            got = dec_lifted(hc, b, R)
+            total += 1
+            if got is not None:
+                applied += 1
+                assert np.array_equal(got.view(np.uint32), oracle.zfp_decode_block(b, R).view(np.uint32))
+    if 2 <= R <= 4:
+        assert applied > 0.9 * total, (applied, total)
+    rng = np.random.default_rng(300 + R)
+    blocks = [(rng.standard_normal(16) * np.exp(4 * rng.standard_normal(16))).astype(np.float32)
+              for _ in range(400)]
+    blocks += [np.zeros(16, np.float32), np.full(16, 1e-42, np.float32), np.full(16, 3.0e38, np.float32),
+               np.full(16, 1e-37, np.float32), np.eye(4, dtype=np.float32).reshape(16)]
+    streams = [oracle.zfp_encode_block(v, R) for v in blocks]
+    streams += [rng.integers(0, 256, 2 * R).astype(np.uint8) for _ in range(1500)]
+    for b in streams:
+        got = dec_lifted(hc, b, R)
+        if got is not None:
+            assert np.array_equal(got.view(np.uint32), oracle.zfp_decode_block(b, R).view(np.uint32))
