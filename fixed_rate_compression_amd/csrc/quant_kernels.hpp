@@ -29,6 +29,7 @@
 #include "cg_quant.hpp"
 #include "cg_tile.hpp"
 #include "gauge128.hpp"
+#include "split_gauge.hpp"
 
 namespace cgq {
 
@@ -37,6 +38,16 @@ using namespace cgk;
 // full-head gauge with bf16 storage: split-precision bf16 matrix-core path
 template <int G, bool BF16>
 constexpr bool kDense = G == 128 && BF16;
+
+// decoders with bf16 storage and g = 16 / 32: inverse gauge as
+// split-precision bf16 matrix-core products (split_gauge.hpp)
+template <int G, bool BF16>
+constexpr bool kSplitInv = BF16 && (G == 16 || G == 32);
+
+// the fp32 fmaf-chain inverse gauge a decoder keeps (none where another
+// path applies it)
+template <int G, bool BF16>
+constexpr int kChainInv = (kDense<G, BF16> || kSplitInv<G, BF16>) ? 0 : G;
 
 struct QK {
   int64_t tcap, tokens, t0, nt;
@@ -212,7 +223,8 @@ struct GaugedTiles {
 template <int G, bool BF16>
 __device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, int j,
                                                     const float (&v)[32], int nrows,
-                                                    const TileGauge<G, true> &tg,
+                                                    const TileGauge<kChainInv<G, BF16>, true> &tg,
+                                                    const SplitGaugeFrags<kSplitInv<G, BF16> ? G : 16> &sg,
                                                     const G128Frags &fr) {
   float *xs = (float *)lds;
   if constexpr (kDense<G, BF16>) {
@@ -220,6 +232,11 @@ __device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, i
     split32(sh, sl, t, j, v);
     __syncthreads();
     gauge128_tile<false>(sh, sl, xs, fr);
+  } else if constexpr (kSplitInv<G, BF16>) {
+    split_store32(lds, t, j, v);
+    __syncthreads();
+    gauge_tile_split<G>(lds, nrows, sg);
+    __syncthreads();
   } else {
     write32(xs, t, j, v);
     __syncthreads();
@@ -370,8 +387,12 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
       csum[threadIdx.x] = c;
     }
   }
-  TileGauge<G, true> tg;
-  if constexpr (G != 0 && !kDense<G, BF16>) tg.load(Gf);
+  TileGauge<kChainInv<G, BF16>, true> tg;
+  SplitGaugeFrags<kSplitInv<G, BF16> ? G : 16> sg;
+  if constexpr (kSplitInv<G, BF16>)
+    load_split_gauge<G>(Gf, sg);
+  else if constexpr (kChainInv<G, BF16> != 0)
+    tg.load(Gf);
   const int BT = a.block;
   const int64_t nblk_f = a.tcap / BT;
   const int t = threadIdx.x >> 2, j = threadIdx.x & 3;
@@ -430,7 +451,7 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
         for (int k = 0; k < 32; k++) v[k] = 0.0f;
       }
       if (tile + 1 < tend) fetch(tile + 1);
-      inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, fr);
+      inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, sg, fr);
     }
     const size_t off = (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
     if (a.ref)
@@ -560,8 +581,12 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
   if constexpr (kDense<G, BF16>) load_g128<true>(Gf, fr);
-  TileGauge<G, true> tg;
-  if constexpr (G != 0 && !kDense<G, BF16>) tg.load(Gf);
+  TileGauge<kChainInv<G, BF16>, true> tg;
+  SplitGaugeFrags<kSplitInv<G, BF16> ? G : 16> sg;
+  if constexpr (kSplitInv<G, BF16>)
+    load_split_gauge<G>(Gf, sg);
+  else if constexpr (kChainInv<G, BF16> != 0)
+    tg.load(Gf);
   const int64_t Tq = a.tokens - a.residual, Tcq = a.tcap - a.residual;
   const size_t Pf = (size_t)Tcq * 16 * BITS + (size_t)a.residual * D * ESZ;
   const uint8_t *pf = payload + (size_t)f * Pf;
@@ -627,7 +652,7 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
     if (tile + 1 < tend) fetch(tile + 1);
-    inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, fr);
+    inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, sg, fr);
     const size_t off = (size_t)(f * a.tcap + tb) * D * ESZ;
     if (a.ref)
       store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);

@@ -27,6 +27,7 @@
 #include "cg_launch.hpp"
 #include "cg_tile.hpp"
 #include "gauge128.hpp"
+#include "split_gauge.hpp"
 #include "zfp_block.hpp"
 
 namespace cgk {
@@ -141,12 +142,12 @@ __device__ __forceinline__ cg_v4i lift_operand() {
   return a;
 }
 
-// Wave-uniform: false (nothing stored) unless every lane's block takes the
-// lifted reconstruction; then the 16 values are stored at dst (row pitch
-// PITCH).  Called with all 64 lanes active.
+// Wave-uniform: false unless every lane's block takes the lifted
+// reconstruction; then v holds the block's 16 values (v[4j + i]: token row
+// j, channel i).  Called with all 64 lanes active.
 template <int R>
 __device__ __forceinline__ bool lifted_tail(const cg_v4i &liftA, const cgz::BlockParse<R> &st,
-                                            float *dst) {
+                                            float (&v)[16]) {
   const cgz::LiftScale ls = cgz::lift_scale<R>(st);
   if (cgz::wave_any(!ls.ok)) return false;
   uint32_t T[4];
@@ -158,18 +159,13 @@ __device__ __forceinline__ bool lifted_tail(const cg_v4i &liftA, const cgz::Bloc
 #pragma unroll
   for (int r = 0; r < 16; r++) C[r] = cgz::kLiftMagic + ls.beta * cgz::kLift.rowsum[r];
   const cg_v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(liftA, B, C, 0, 0, 0);
-  float v[16];
   float mx = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     v[r] = fmaf(__int_as_float(D[r]), ls.scale, ls.offset);
     mx = fmaxf(mx, fabsf(v[r]));
   }
-  if (cgz::wave_any(!(mx < ls.limit))) return false;
-#pragma unroll
-  for (int j = 0; j < 4; j++)
-    *(float4 *)(dst + j * PITCH) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-  return true;
+  return !cgz::wave_any(!(mx < ls.limit));
 }
 
 // Gauges g <= 32: a workgroup walks a.chunk_tiles consecutive tiles of
@@ -275,8 +271,15 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
   const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * a.chunk_tiles;
   const int tend = min(a.tiles, tile0 + a.chunk_tiles);
   const size_t esz = BF16 ? 2 : 4;
-  TileGauge<G, true> tg;
-  if constexpr (G != 0) tg.load(gauges + gauge_index(field, a.batch, a.heads) * D * G);
+  // bf16 storage, g = 16 / 32: split-precision bf16 matrix cores; otherwise
+  // the fp32 fmaf-chain form (or nothing, g = 0)
+  constexpr bool kSplit = BF16 && (G == 16 || G == 32);
+  TileGauge<kSplit ? 0 : G, true> tg;
+  SplitGaugeFrags<kSplit ? G : 16> sg;
+  if constexpr (kSplit)
+    load_split_gauge<G>(gauges + gauge_index(field, a.batch, a.heads) * D * G, sg);
+  else if constexpr (G != 0)
+    tg.load(gauges + gauge_index(field, a.batch, a.heads) * D * G);
   auto rows = [&](int tile) { return (int)min((int64_t)TILE_T, a.nt - (int64_t)tile * TILE_T); };
   auto codes = [&](int tile) {
     return (const uint4 *)(payload + (size_t)(field * (a.tcap / 4) + (a.t0 + (int64_t)tile * TILE_T) / 4) * 32 * 2 * R);
@@ -331,19 +334,27 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
 #pragma unroll
         for (int a2 = 0; a2 < cgz::Rate<R>::kAcc; a2++) acc[a2] = 0;
       }
-      float *dst = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
       cgz::BlockParse<R> st;
       cgz::decode_planes8<R>(acc, st);
-      if (!lifted_tail<R>(liftA, st, dst)) {
-        float v[16];
-        cgz::decode_finish<R>(acc, st, v);
+      float v[16];
+      if (!lifted_tail<R>(liftA, st, v)) cgz::decode_finish<R>(acc, st, v);
+      if constexpr (kSplit) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          split_store4((unsigned char *)xs, (b >> 5) * 4 + j, (b & 31) * 4, v[4 * j], v[4 * j + 1],
+                       v[4 * j + 2], v[4 * j + 3]);
+      } else {
+        float *dst = xs + (b >> 5) * 4 * PITCH + (b & 31) * 4;
 #pragma unroll
         for (int j = 0; j < 4; j++)
           *(float4 *)(dst + j * PITCH) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
       }
     }
     __syncthreads();
-    if constexpr (G != 0) {
+    if constexpr (kSplit) {
+      gauge_tile_split<G>((unsigned char *)xs, nrows, sg);
+      __syncthreads();
+    } else if constexpr (G != 0) {
       tg.apply(xs, nrows);
       __syncthreads();
     }

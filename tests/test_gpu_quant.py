@@ -1,8 +1,11 @@
 """GPU parity of the fused gauge + block-uniform / KIVI-style quantizers and
 their decoders against the oracle ("Codec-Gauge", arXiv HTML,
-evaluation-protocol paragraph).  Bar: bit-exact codes and metadata; for
-g <= 32, and for the full-head gauge with fp32 storage (fp32 matrix-core
-fmaf chains), the decoded cache is bit-exact too.  For the full-head gauge
+evaluation-protocol paragraph).  Bar: bit-exact codes and metadata.  The
+decoded cache is bit-exact wherever the decoder evaluates the inverse gauge
+as the oracle's fmaf chains (fp32 storage, including the full-head gauge on
+fp32 matrix-core chains; bf16 storage at g = 0 and 8); with bf16 storage at
+g = 16 / 32 (split-precision bf16 matrix cores) every element is held to
+that arithmetic's error bound (gpu_util.check_decoded).  For the full-head gauge
 with bf16 storage (split-precision bf16 matrix cores, an accumulation order
 the CPU does not reproduce) parity is staged: the oracle quantizes the
 library's own gauged field (cg_gauge_apply, the same device routine as the
@@ -13,7 +16,8 @@ import pytest
 
 import oracle
 from fixed_rate_compression_amd import binding as cg
-from gpu_util import D, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu, n_fields, to_dev, to_host
+from gpu_util import (D, check_decoded, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu, n_fields,
+                      to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,8 +74,7 @@ def test_block_uniform_bit_exact(bits, Bt, g):
         p_ref, m_ref = oracle.bu_encode_field(xg, Bt, bits)
         assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f
         assert np.array_equal(meta[f].view(np.uint32), m_ref.view(np.uint32)), f
-        y = oracle.gauge_inverse(oracle.bu_decode_field(p_ref, m_ref, T, D, Bt, bits), Gf, g)
-        assert np.array_equal(out[f], oracle.f32_to_bf16(y)), f
+        check_decoded(out[f], oracle.bu_decode_field(p_ref, m_ref, T, D, Bt, bits), Gf, g, f)
 
 
 def test_block_uniform_past_4gib_offsets():
@@ -106,8 +109,8 @@ def test_block_uniform_past_4gib_offsets():
             mbase = 2 * (f * nb + r0 // Bt)
             assert np.array_equal(to_host(meta[mbase:mbase + 2 * (n // Bt)]).view(np.uint32),
                                   m_ref.reshape(-1).view(np.uint32)), (f, r0)
-            y = oracle.gauge_inverse(oracle.bu_decode_field(p_ref, m_ref, n, D, Bt, bits), Gf, g)
-            assert np.array_equal(to_host(out[f, r0:r0 + n]), oracle.f32_to_bf16(y)), (f, r0)
+            check_decoded(to_host(out[f, r0:r0 + n]), oracle.bu_decode_field(p_ref, m_ref, n, D, Bt, bits),
+                          Gf, g, (f, r0))
     del x, out, pay, meta
     t.cuda.empty_cache()
 
@@ -160,8 +163,7 @@ def test_kivi_bit_exact(bits, g, bf16):
         tail_st = oracle.from_f32(tail, x.dtype)
         assert np.array_equal(pt, tail_st.view(np.uint8).reshape(-1)), f
         yq = oracle.kivi_decode_field(p_ref, m_ref, oracle.to_f32(tail_st), T, D, kind, 32, bits, res)
-        y = oracle.from_f32(oracle.gauge_inverse(yq, Gf, g), x.dtype)
-        assert np.array_equal(bits_view(out[f]), bits_view(y)), f
+        check_decoded(out[f], yq, Gf, g, f)
 
 
 def test_kivi_all_tail_and_constant_groups():

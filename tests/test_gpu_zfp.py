@@ -1,18 +1,21 @@
 """GPU parity of the fused gauge + zfp-style encode and decode + inverse gauge
 against the oracle ("Codec-Gauge", arXiv HTML, evaluation-protocol
 paragraph: gauge -> fixed-rate zfp on the FP32-transformed field -> decode ->
-inverse gauge).  Bar: bit-exact codec streams; for g <= 32, and for the
-full-head gauge with fp32 storage, the decoded cache is bit-exact too,
-because both sides evaluate the gauge as the same fmaf chains, decode the
-same integers and round to bf16 the same way.  The full-head gauge with bf16
-storage (split-precision bf16 matrix cores) is checked staged."""
+inverse gauge).  Bar: bit-exact codec streams.  The decoded cache is
+bit-exact wherever the decoder evaluates the inverse gauge as the oracle's
+fmaf chains (fp32 storage at every group size; bf16 storage at g = 0 and 8),
+because both sides decode the same integers, chain the same fmafs and round
+the same way.  With bf16 storage at g = 16 / 32 the inverse gauge runs as
+split-precision bf16 matrix-core products: every element is held to the
+error bound of that arithmetic (gpu_util.check_decoded) and the 1e-2 bf16
+bar.  The full-head gauge with bf16 storage is checked staged."""
 import numpy as np
 import pytest
 
 import oracle
 from fixed_rate_compression_amd import binding as cg
-from gpu_util import (D, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu, n_fields,
-                      to_dev, to_host, zfp_oracle_field)
+from gpu_util import (D, check_decoded, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu,
+                      n_fields, to_dev, to_host, zfp_oracle_decoded)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,11 +52,10 @@ def check_against_oracle(x, G, g, R, L, KV, B, H, T, Tcap, pay, out, fields=None
     F = n_fields(L, KV, B, H)
     per = Tcap * D * R // 8
     for f in (range(F) if fields is None else fields):
-        p_ref, y_ref = zfp_oracle_field(x[f], gauge_of_field(G, f, KV, B, H), g, R, T, Tcap)
+        Gf = gauge_of_field(G, f, KV, B, H)
+        p_ref, yg = zfp_oracle_decoded(x[f], Gf, g, R, T, Tcap)
         assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f"payload mismatch in field {f}"
-        assert np.array_equal(out[f, :T].view(np.uint32 if out.dtype == np.float32 else np.uint16),
-                              y_ref.view(np.uint32 if y_ref.dtype == np.float32 else np.uint16)), \
-            f"decoded mismatch in field {f}"
+        check_decoded(out[f, :T], yg, Gf, g, f"decoded rows of field {f}")
 
 
 def test_small_config_fp32_g16_rate4():
@@ -236,9 +238,10 @@ def test_llama8b_class_full_size_sampled_fields():
                 fields.append((l * KV + s) * H + h)
     for f in fields:
         xf = to_host(x[f])
-        p_ref, y_ref = zfp_oracle_field(xf, gauge_of_field(G, f, KV, B, H), g, R, T, T)
+        Gf = gauge_of_field(G, f, KV, B, H)
+        p_ref, yg = zfp_oracle_decoded(xf, Gf, g, R, T, T)
         assert np.array_equal(to_host(pay[f * per:(f + 1) * per]), p_ref), f
-        assert np.array_equal(to_host(out[f]), y_ref), f
+        check_decoded(to_host(out[f]), yg, Gf, g, f)
 
 
 def test_fields_past_4gib_offsets():
@@ -269,10 +272,10 @@ def test_fields_past_4gib_offsets():
         for r0, n in ((0, 64), ((1 << 24) - 32, 96), (r_end, T - r_end)):
             xs = to_host(x[f, r0:r0 + n])
             n4 = (n + 3) // 4 * 4
-            p_ref, y_ref = zfp_oracle_field(xs, Gf, g, R, n, n4)
+            p_ref, yg = zfp_oracle_decoded(xs, Gf, g, R, n, n4)
             base = f * per + (r0 // 4) * 32 * 2 * R
             assert np.array_equal(to_host(pay[base:base + n4 // 4 * 32 * 2 * R]), p_ref), (f, r0)
-            assert np.array_equal(to_host(out[f, r0:r0 + n]), y_ref), (f, r0)
+            check_decoded(to_host(out[f, r0:r0 + n]), yg, Gf, g, (f, r0))
         assert not torch.any(out[f, T:].view(torch.int16) != 0)
     del x, out, pay
     torch.cuda.empty_cache()
@@ -303,9 +306,10 @@ def test_27b_class_full_size_sampled_fields():
     fields.append(n_fields(L, KV, B, H) - 1)
     for f in sorted(set(fields)):
         xf = to_host(x[f])
-        p_ref, y_ref = zfp_oracle_field(xf, gauge_of_field(G, f, KV, B, H), g, R, T, T)
+        Gf = gauge_of_field(G, f, KV, B, H)
+        p_ref, yg = zfp_oracle_decoded(xf, Gf, g, R, T, T)
         assert np.array_equal(to_host(pay[f * per:(f + 1) * per]), p_ref), f
-        assert np.array_equal(to_host(out[f]), y_ref), f
+        check_decoded(to_host(out[f]), yg, Gf, g, f)
 
 
 @pytest.mark.parametrize("R", [3, 4, 8])
