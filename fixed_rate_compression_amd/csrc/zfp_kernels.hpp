@@ -460,6 +460,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
     }
   };
   if (tile0 < tend) fetch(tile0);
+  const cg_v4i liftA = lift_operand();
   ErrAcc err;
   for (int tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
@@ -473,14 +474,23 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
     }
     __syncthreads();
     if (tile + 1 < tend) fetch(tile + 1);
-    // decoded blocks go straight into the split operand tiles (rows past
-    // nrows keep stale values: output rows depend on their own row only and
-    // are not stored)
-    for (int b = threadIdx.x; b < nblk; b += NT) {
+    // decoded blocks go straight into the split operand tiles; every lane
+    // takes part (the lifted reconstruction is a wave-wide product), lanes
+    // past the tile's blocks decode an empty block into rows that are not
+    // stored (output rows depend on their own row only)
+#pragma unroll
+    for (int i = 0; i < TILE_T / 4 * 32 / NT; i++) {
+      const int b = threadIdx.x + NT * i;
       uint64_t acc[cgz::Rate<R>::kAcc];
       unstage_block<R>(os, b, acc);
+      if (b >= nblk) {
+#pragma unroll
+        for (int a2 = 0; a2 < cgz::Rate<R>::kAcc; a2++) acc[a2] = 0;
+      }
+      cgz::BlockParse<R> st;
+      cgz::decode_planes8<R>(acc, st);
       float v[16];
-      cgz::decode_block<R>(acc, v);
+      if (!lifted_tail<R>(liftA, st, v)) cgz::decode_finish<R>(acc, st, v);
       const int off = (b >> 5) * 4 * HP + (b & 31) * 4;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
