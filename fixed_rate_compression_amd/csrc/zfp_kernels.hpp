@@ -305,6 +305,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
   };
   if (tile0 < tend) fetch(tile0);
   const cg_v4i liftA = lift_operand();
+  const cgz::ParseConsts kc = cgz::parse_consts();
   ErrAcc err;
   for (int tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
@@ -335,9 +336,9 @@ __global__ __launch_bounds__(NT) void k_zfp_decode(const uint8_t *__restrict__ p
         for (int a2 = 0; a2 < cgz::Rate<R>::kAcc; a2++) acc[a2] = 0;
       }
       cgz::BlockParse<R> st;
-      cgz::decode_planes8<R>(acc, st);
+      cgz::decode_planes8<R>(acc, st, kc);
       float v[16];
-      if (!lifted_tail<R>(liftA, st, v)) cgz::decode_finish<R>(acc, st, v);
+      if (!lifted_tail<R>(liftA, st, v)) cgz::decode_finish<R>(acc, st, v, kc);
       if constexpr (kSplit) {
 #pragma unroll
         for (int j = 0; j < 4; j++)
@@ -461,6 +462,7 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
   };
   if (tile0 < tend) fetch(tile0);
   const cg_v4i liftA = lift_operand();
+  const cgz::ParseConsts kc = cgz::parse_consts();
   ErrAcc err;
   for (int tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + (int64_t)tile * TILE_T;
@@ -488,9 +490,9 @@ __global__ __launch_bounds__(NT) void k_zfp_decode128(const uint8_t *__restrict_
         for (int a2 = 0; a2 < cgz::Rate<R>::kAcc; a2++) acc[a2] = 0;
       }
       cgz::BlockParse<R> st;
-      cgz::decode_planes8<R>(acc, st);
+      cgz::decode_planes8<R>(acc, st, kc);
       float v[16];
-      if (!lifted_tail<R>(liftA, st, v)) cgz::decode_finish<R>(acc, st, v);
+      if (!lifted_tail<R>(liftA, st, v)) cgz::decode_finish<R>(acc, st, v, kc);
       const int off = (b >> 5) * 4 * HP + (b & 31) * 4;
 #pragma unroll
       for (int j = 0; j < 4; j++) {

@@ -1,7 +1,11 @@
-"""Streaming HBM kernels (libcgprobe.so) that move bytes in the codec
-kernels' read : write proportions with no other work: the practical memory
-ceiling the zfp kernels are quoted against next to the 8 TB/s peak.
-Measurement only; nothing on the codec path uses them."""
+"""Measurement kernels (libcgprobe.so); nothing on the codec path uses them.
+
+- Streaming HBM kernels that move bytes in the codec kernels' read : write
+  proportions with no other work: the practical memory ceiling the zfp
+  kernels are quoted against next to the 8 TB/s peak (stream.hip).
+- Instruction-issue probes (issue.hip): the rate of single VALU instruction
+  forms (which ones pair up in one issue slot), and whether matrix-core and
+  VALU work overlap.  `python3 -m fixed_rate_compression_amd.probe issue`."""
 from __future__ import annotations
 
 import ctypes
@@ -9,7 +13,7 @@ import os
 import subprocess
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "stream.hip")
+_SRC = [os.path.join(_HERE, "stream.hip"), os.path.join(_HERE, "issue.hip")]
 _LIB = os.path.join(_HERE, "libcgprobe.so")
 
 MODES = {"copy": (0, 1, 1), "enc": (1, 4, 1), "dec": (2, 1, 4)}   # name: (mode, read, write)
@@ -21,7 +25,7 @@ def build(force: bool = True) -> str:
         subprocess.check_call([
             "hipcc", "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-o", tmp, _SRC])
+            "-o", tmp, *_SRC])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -39,6 +43,10 @@ def lib():
         L.cgprobe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                      ctypes.c_uint64, ctypes.c_void_p]
         L.cgprobe_stream.restype = ctypes.c_int
+        for fn in (L.cgprobe_issue, L.cgprobe_overlap):
+            fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                           ctypes.POINTER(ctypes.c_float)]
+            fn.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -91,3 +99,46 @@ def ceilings(kv, steps: int = 10, warmup: int = 2) -> dict:
         del dst
         torch.cuda.empty_cache()
     return out
+
+
+# the instruction forms of issue.hip, in its kernel order
+ISSUE_FORMS = ("v_xor_b32, VGPR operands", "v_xor_b32, an SGPR operand", "v_xor_b32, a literal",
+               "v_add_u32", "v_bitop3_b32, VGPR operands", "v_bitop3_b32, an SGPR operand",
+               "v_lshrrev_b32 by 1", "v_lshlrev_b32 by 1", "v_bfe_u32", "v_perm_b32", "v_lshl_or_b32",
+               "v_bcnt_u32_b32", "v_ffbh_u32", "v_min_u32", "v_fma_f32, VGPR operands",
+               "v_fma_f32, an SGPR operand", "v_cvt_f32_i32")
+OVERLAP_MODES = ("fp32 16x16x4 alone", "VALU alone (fp32 case)", "fp32 16x16x4 + VALU in one wave",
+                 "fp32 16x16x4 and VALU in separate waves", "bf16 16x16x32 alone", "VALU alone (bf16 case)",
+                 "bf16 16x16x32 + VALU in one wave", "bf16 16x16x32 and VALU in separate waves")
+
+
+def issue_rates(iters: int = 2000) -> dict:
+    """G wave64 instructions/s of each form of ISSUE_FORMS (2048 x 256 threads,
+    32 instructions per trip)."""
+    import torch
+    L = lib()
+    assert L.cgprobe_issue_kinds() == len(ISSUE_FORMS)
+    out = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for k, name in enumerate(ISSUE_FORMS):
+        ms = ctypes.c_float()
+        if L.cgprobe_issue(k, iters, out.data_ptr(), s, ctypes.byref(ms)) != 0:
+            raise RuntimeError(f"cgprobe_issue({k}) failed")
+        res[name] = round(2048 * 4 * iters * 32 / (ms.value * 1e-3) / 1e9, 1)
+    return res
+
+
+def overlap_times(iters: int = 2000) -> dict:
+    """ms of each mode of OVERLAP_MODES."""
+    import torch
+    L = lib()
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for m, name in enumerate(OVERLAP_MODES):
+        ms = ctypes.c_float()
+        if L.cgprobe_overlap(m, iters, out.data_ptr(), s, ctypes.byref(ms)) != 0:
+            raise RuntimeError(f"cgprobe_overlap({m}) failed")
+        res[name] = round(ms.value, 3)
+    return res

@@ -1,0 +1,21 @@
+"""python3 -m fixed_rate_compression_amd.probe issue: print the instruction-issue
+rates and the matrix-core / VALU overlap times of issue.hip (one line each)."""
+import sys
+
+from fixed_rate_compression_amd import probe
+
+
+def main() -> int:
+    if len(sys.argv) < 2 or sys.argv[1] != "issue":
+        print(__doc__)
+        return 2
+    for name, gps in probe.issue_rates().items():
+        print(f"{name:34s} {gps:8.1f} G wave64 instr/s  ({gps / 614.4:.2f} per SIMD issue slot at 2.4 GHz)",
+              flush=True)
+    for name, ms in probe.overlap_times().items():
+        print(f"{name:44s} {ms:.3f} ms", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
