@@ -10,8 +10,11 @@
 // when it is not already a bf16 value, so that
 //   X G^T ~= X_hi G_hi^T + X_hi G_lo^T + X_lo G_hi^T
 // carries ~16 significand bits of every product (the dropped X_lo G_lo term
-// is ~2^-16 of the smallest kept one).  A bf16 input has X_lo = 0 and takes
-// two passes.
+// is ~2^-16 of the smallest kept one).  Decoders take these three passes (or
+// two, for exact integer codes).  The forward gauge of bf16 tiles (the
+// encoders and the bf16 gauge routine) takes one: X is exact in bf16 and
+// the codes are decided on bf16-precision data anyway, so X G_hi^T, within
+// 2^-9 sum |G||X| of X G^T, is the gauged field (HI_ONLY).
 //
 // Work split: wave w owns output channels [32w, 32w+32) (two 16-wide column
 // tiles) for all 64 rows; its B fragments (G_hi, G_lo: 2 column tiles x 4
@@ -163,7 +166,8 @@ __device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j
 
 // X G^T (forward fragments) or X G (inverse fragments) of the split tile into
 // the fp32 tile xs, which may overlay sh/sl.  EXACT: every tile value is a
-// bf16 number (no lo part: two passes instead of three).  Each accumulator
+// bf16 number (no lo part: two passes instead of three).  HI_ONLY (with
+// EXACT): one pass, against G_hi only.  Each accumulator
 // takes its products in the order ks = 0..3, and within a ks hi*G_hi,
 // hi*G_lo, lo*G_hi, so results depend on the tile only.  Contains two
 // workgroup barriers; the caller has synchronized after writing sh/sl.
@@ -171,10 +175,11 @@ __device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j
 // scale_r (q G)[r][n] + min_r cs[n], with (min_r, scale_r) = rowp[r] and
 // cs[n] the column sums of the matrix (the dequantized tile min + q scale
 // times the matrix, with the range applied after the product).
-template <bool EXACT, bool AFFINE = false>
+template <bool EXACT, bool AFFINE = false, bool HI_ONLY = false>
 __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t *sl, float *xs,
                                               const G128Frags &f, const float2 *rowp = nullptr,
                                               const float *cs = nullptr) {
+  static_assert(!HI_ONLY || EXACT, "one pass needs bf16 tile values");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   f32x4_t acc[4][2];
@@ -199,11 +204,13 @@ __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t
 #pragma unroll
       for (int ntl = 0; ntl < 2; ntl++)
         acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mt], f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
+    if (!HI_ONLY) {
 #pragma unroll
-    for (int mt = 0; mt < 4; mt++)
+      for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-      for (int ntl = 0; ntl < 2; ntl++)
-        acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mt], f.lo[ntl][ks], acc[mt][ntl], 0, 0, 0);
+        for (int ntl = 0; ntl < 2; ntl++)
+          acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mt], f.lo[ntl][ks], acc[mt][ntl], 0, 0, 0);
+    }
     if (!EXACT) {
 #pragma unroll
       for (int mt = 0; mt < 4; mt++)

@@ -204,7 +204,7 @@ struct GaugedTiles {
       pre.put(sh, sl);
       __syncthreads();
       if (next_rows > 0) pre.fetch(next_src, next_rows);
-      gauge128_tile<BF16>(sh, sl, xs, fr);
+      gauge128_tile<BF16, false, BF16>(sh, sl, xs, fr);
     } else {
       (void)src;
       pre.put_f32(xs);
@@ -290,7 +290,7 @@ __device__ __forceinline__ void load32_storage(const uint8_t *p, float (&v)[32])
 // ---------------------------------------------------------------------------
 
 template <int BITS, bool BF16, int G>
-__global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
+__device__ __forceinline__ void bu_encode_body(const void *__restrict__ kv,
                                                   const float *__restrict__ gauges,
                                                   uint8_t *__restrict__ payload,
                                                   float *__restrict__ meta, QK a) {
@@ -363,7 +363,25 @@ __global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
 }
 
 template <int BITS, bool BF16, int G>
-__global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ payload,
+__global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
+                                                  const float *__restrict__ gauges,
+                                                  uint8_t *__restrict__ payload,
+                                                  float *__restrict__ meta, QK a) {
+  bu_encode_body<BITS, BF16, G>(kv, gauges, payload, meta, a);
+}
+
+// the same with three waves per SIMD (launched for the full-head gauge with
+// bf16 storage, which fits in 168 VGPRs; other instances would spill)
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void k_bu_encode_w3(const void *__restrict__ kv,
+                                                  const float *__restrict__ gauges,
+                                                  uint8_t *__restrict__ payload,
+                                                  float *__restrict__ meta, QK a) {
+  bu_encode_body<BITS, BF16, G>(kv, gauges, payload, meta, a);
+}
+
+template <int BITS, bool BF16, int G>
+__device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ payload,
                                                   const float *__restrict__ meta,
                                                   const float *__restrict__ gauges,
                                                   void *__restrict__ out, QK a) {
@@ -463,6 +481,24 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
   if (a.ref) write_err(err, a.epart);
 }
 
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ payload,
+                                                  const float *__restrict__ meta,
+                                                  const float *__restrict__ gauges,
+                                                  void *__restrict__ out, QK a) {
+  bu_decode_body<BITS, BF16, G>(payload, meta, gauges, out, a);
+}
+
+// the same with three waves per SIMD (launched for the full-head gauge with
+// bf16 storage, which fits in 168 VGPRs; other instances would spill)
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void k_bu_decode_w3(const uint8_t *__restrict__ payload,
+                                                  const float *__restrict__ meta,
+                                                  const float *__restrict__ gauges,
+                                                  void *__restrict__ out, QK a) {
+  bu_decode_body<BITS, BF16, G>(payload, meta, gauges, out, a);
+}
+
 // ---------------------------------------------------------------------------
 // KIVI-style: keys one range per channel per 32 tokens, values one range per
 // token per 32 channels; the last `residual` rows stay in the storage format.
@@ -472,7 +508,7 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
 // ---------------------------------------------------------------------------
 
 template <int BITS, bool BF16, int G>
-__global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
+__device__ __forceinline__ void kivi_encode_body(const void *__restrict__ kv,
                                                     const float *__restrict__ gauges,
                                                     uint8_t *__restrict__ payload,
                                                     float *__restrict__ meta, QK a) {
@@ -567,7 +603,25 @@ __global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
 }
 
 template <int BITS, bool BF16, int G>
-__global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ payload,
+__global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
+                                                    const float *__restrict__ gauges,
+                                                    uint8_t *__restrict__ payload,
+                                                    float *__restrict__ meta, QK a) {
+  kivi_encode_body<BITS, BF16, G>(kv, gauges, payload, meta, a);
+}
+
+// the same with three waves per SIMD (launched for the full-head gauge with
+// bf16 storage, which fits in 168 VGPRs; other instances would spill)
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void k_kivi_encode_w3(const void *__restrict__ kv,
+                                                    const float *__restrict__ gauges,
+                                                    uint8_t *__restrict__ payload,
+                                                    float *__restrict__ meta, QK a) {
+  kivi_encode_body<BITS, BF16, G>(kv, gauges, payload, meta, a);
+}
+
+template <int BITS, bool BF16, int G>
+__device__ __forceinline__ void kivi_decode_body(const uint8_t *__restrict__ payload,
                                                     const float *__restrict__ meta,
                                                     const float *__restrict__ gauges,
                                                     void *__restrict__ out, QK a) {
@@ -663,6 +717,24 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
   if (a.ref) write_err(err, a.epart);
 }
 
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ payload,
+                                                    const float *__restrict__ meta,
+                                                    const float *__restrict__ gauges,
+                                                    void *__restrict__ out, QK a) {
+  kivi_decode_body<BITS, BF16, G>(payload, meta, gauges, out, a);
+}
+
+// the same with three waves per SIMD (launched for the full-head gauge with
+// bf16 storage, which fits in 168 VGPRs; other instances would spill)
+template <int BITS, bool BF16, int G>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void k_kivi_decode_w3(const uint8_t *__restrict__ payload,
+                                                    const float *__restrict__ meta,
+                                                    const float *__restrict__ gauges,
+                                                    void *__restrict__ out, QK a) {
+  kivi_decode_body<BITS, BF16, G>(payload, meta, gauges, out, a);
+}
+
 // dense-gauge rows kernel behind cg_gauge_apply(g = 128) with bf16 storage:
 // same tiles, same fragments, same MFMA sequence as the fused quantizer
 // kernels (fp32 storage uses the fmaf-chain rows kernel of the smaller groups)
@@ -691,7 +763,7 @@ __global__ __launch_bounds__(NT) void k_gauge128_rows(const void *__restrict__ s
     pre.put(sh, sl);
     __syncthreads();
     if (tile + 1 < tend) pre.fetch(src_f + (size_t)(tb + TILE_T) * D * ESZ, tile_rows(a, tile + 1));
-    gauge128_tile<BF16>(sh, sl, xs, fr);
+    gauge128_tile<BF16, false, BF16 && !INV>(sh, sl, xs, fr);
     store_tile<false>(out + (size_t)(f * a.tcap + tb) * D, nrows, xs);
     __syncthreads();
   }

@@ -94,6 +94,24 @@ def zfp_oracle_field(field, Gf, g, R, T, Tcap):
     return payload, oracle.from_f32(oracle.gauge_inverse(yg, Gf, g), field.dtype)
 
 
+def check_dense_forward(xg, x, Gf, where=None):
+    """The full-head gauge of bf16 tiles (one pass of bf16 matrix-core products
+    against the round-to-nearest bf16 part of the gauge: the tile values are
+    bf16 already) against fp64: every element within 2^-8 sum_k |G_ck| |x_k|
+    (the bf16 rounding of G contributes at most 2^-9 of it, the fp32 sums
+    about 2^-17), and the 1e-2 bar of bf16 I/O as max|err| / max|ref|.
+    Returns that relative error."""
+    x64 = np.asarray(x, np.float64)
+    G64 = np.asarray(Gf, np.float64)
+    ref = oracle.gauge_forward_f64(x64, G64, 128)
+    mag = oracle.gauge_forward_f64(np.abs(x64), np.abs(G64), 128)
+    err = np.abs(np.asarray(xg, np.float64) - ref)
+    assert np.all(err <= 2.0 ** -8 * mag), (where, float(np.max(err / np.maximum(mag, 1e-300))))
+    rel = float(np.max(err) / max(np.max(np.abs(ref)), 1e-30))
+    assert rel <= 1e-2, (where, rel)
+    return rel
+
+
 def split_inverse(storage_dtype, g):
     """True where the library's decoders apply the inverse gauge as
     split-precision bf16 matrix-core products: bf16 storage with g = 16 or

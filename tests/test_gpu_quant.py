@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from fixed_rate_compression_amd import binding as cg
-from gpu_util import (D, check_decoded, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu, n_fields,
+from gpu_util import (D, check_decoded, check_dense_forward, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu, n_fields,
                       to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -199,8 +199,7 @@ def test_dense_gauge_staged(backend, bits, blk, res):
     worst_g, worst_o = 0.0, 0.0
     for f in range(n_fields(L, KV, B, H)):
         Gf = gauge_of_field(G, f, KV, B, H).astype(np.float64)
-        ref_g = oracle.gauge_forward_f64(oracle.to_f32(x[f]), Gf, 128)
-        worst_g = max(worst_g, rel_err(xg[f], ref_g))
+        worst_g = max(worst_g, check_dense_forward(xg[f], oracle.to_f32(x[f]), Gf, f))
         if backend == cg.CG_BACKEND_BLOCK_UNIFORM:
             p_ref, m_ref = oracle.bu_encode_field(xg[f], blk, bits)
             per = T * D * bits // 8
@@ -219,7 +218,6 @@ def test_dense_gauge_staged(backend, bits, blk, res):
         ref_o = oracle.gauge_inverse_f64(deq, Gf, 128)
         worst_o = max(worst_o, rel_err(oracle.to_f32(out[f]), ref_o))
     print(f"dense gauge max rel err {worst_g:.3e}; decoded (bf16) max rel err {worst_o:.3e}")
-    assert worst_g <= 1e-4       # bf16 I/O bar is 1e-2; measured ~1e-5
     assert worst_o <= 1e-2
 
 
@@ -313,9 +311,9 @@ def test_full_head_config_sampled_fields(backend, bits, blk, res):
     encoded and decoded by the same launches the bench times.  Fields of
     layers 0, 15 and 31 (the last field among them) are checked staged:
     codes, metadata and tail bit-exact against the oracle applied to the
-    library's gauged field; the gauge within 1e-4 of fp64; the decoded bf16
-    cache within the 1e-2 bf16 bar of the fp64 inverse gauge of the oracle's
-    dequantized codes."""
+    library's gauged field; the gauge within the one-pass bound of
+    gpu_util.check_dense_forward; the decoded bf16 cache within the 1e-2 bf16
+    bar of the fp64 inverse gauge of the oracle's dequantized codes."""
     t = torch()
     L, KV, B, H, T = 32, 2, 1, 8, 131072
     print(f"full-head config: backend {backend}, {bits} bits", flush=True)
@@ -345,7 +343,7 @@ def test_full_head_config_sampled_fields(backend, bits, blk, res):
         t.cuda.synchronize()
         xg = to_host(xg_d)[0]
         xf = oracle.to_f32(to_host(x[f]))
-        worst_g = max(worst_g, rel_err(xg, oracle.gauge_forward_f64(xf, Gf.astype(np.float64), 128)))
+        worst_g = max(worst_g, check_dense_forward(xg, xf, Gf, (l, s, h)))
         pf = to_host(pay[f * per:(f + 1) * per])
         mf = to_host(meta[f * mper:(f + 1) * mper]).reshape(-1, 2)
         if kivi:
@@ -363,6 +361,6 @@ def test_full_head_config_sampled_fields(backend, bits, blk, res):
         worst_o = max(worst_o, rel_err(oracle.to_f32(to_host(out[f])), ref))
         print(f"  field (layer {l}, kv {s}, head {h}) ok", flush=True)
     print(f"gauge rel err {worst_g:.3e}; decoded cache vs fp64 inverse {worst_o:.3e}")
-    assert worst_g <= 1e-4 and worst_o <= 1e-2
+    assert worst_o <= 1e-2
     del x, out, pay, meta
     t.cuda.empty_cache()

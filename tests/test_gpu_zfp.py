@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from fixed_rate_compression_amd import binding as cg
-from gpu_util import (D, check_decoded, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu,
+from gpu_util import (D, check_decoded, check_dense_forward, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu,
                       n_fields, to_dev, to_host, zfp_oracle_decoded)
 
 pytestmark = pytest.mark.gpu
@@ -344,10 +344,11 @@ def test_full_head_gauge_zfp_fp32_bit_exact(R):
 
 @pytest.mark.parametrize("R", [3, 4, 8])
 def test_dense_gauge_zfp_bf16_staged(R):
-    """Full-head gauge (g = 128) with bf16 storage: the split-precision bf16
-    matrix-core gauge is not an fmaf chain, so parity is staged.  (1) The
-    gauge, through cg_gauge_apply (the routine the fused kernels run),
-    against the fp64 oracle; (2) the codes bit-exact against the oracle's
+    """Full-head gauge (g = 128) with bf16 storage: the bf16 matrix-core
+    gauge (one pass against the bf16 part of G) is not an fmaf chain, so
+    parity is staged.  (1) The gauge, through cg_gauge_apply (the routine the
+    fused kernels run), against the fp64 oracle within the one-pass bound of
+    gpu_util.check_dense_forward; (2) the codes bit-exact against the oracle's
     coder applied to those gauged values; (3) the decoded cache within the
     bf16 bar (1e-2) of the oracle's fp64 inverse gauge of the oracle's decode
     of the same codes."""
@@ -368,12 +369,11 @@ def test_dense_gauge_zfp_bf16_staged(R):
     worst_g, worst_o = 0.0, 0.0
     for f in range(F):
         Gf = gauge_of_field(G, f, KV, B, H).astype(np.float64)
-        worst_g = max(worst_g, rel_err(xg[f], oracle.gauge_forward_f64(oracle.to_f32(x[f]), Gf, 128)))
+        worst_g = max(worst_g, check_dense_forward(xg[f], oracle.to_f32(x[f]), Gf, f))
         p_ref = oracle.zfp_encode_field(xg[f], R)
         assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f"payload mismatch in field {f}"
         dec[f] = oracle.zfp_decode_field(p_ref, T, D, R)
         ref = oracle.gauge_inverse_f64(dec[f], Gf, 128)
         worst_o = max(worst_o, rel_err(oracle.to_f32(out[f]), ref))
     print(f"bf16 dense gauge rel err {worst_g:.3e}; decoded cache vs fp64 inverse {worst_o:.3e}")
-    assert worst_g <= 1e-4          # the bf16 I/O bar is 1e-2
     assert worst_o <= 1e-2
