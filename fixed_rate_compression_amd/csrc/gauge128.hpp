@@ -52,6 +52,8 @@ __device__ __forceinline__ bf16x8_t pack8(const uint32_t (&h)[8]) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+
 struct G128Frags {
   bf16x8_t hi[2][4];
   bf16x8_t lo[2][4];
@@ -76,6 +78,32 @@ __device__ __forceinline__ void load_g128(const float *__restrict__ Gf, G128Frag
       }
       f.hi[ntl][ks] = pack8(h);
       f.lo[ntl][ks] = pack8(l);
+    }
+  }
+}
+
+// fp16 B fragments (one round-to-nearest part, bit patterns held in f.hi;
+// f.lo unused), for tiles of small integer codes: the codes are exact in
+// fp16 and G's fp16 part is within 2^-11 |G| (2^-25 absolute below fp16's
+// normal range), so one fp16 pass beats two bf16 passes' worth of accuracy
+// needs for a bf16 result
+template <bool INV>
+__device__ __forceinline__ void load_g128_f16(const float *__restrict__ Gf, G128Frags &f) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int ntl = 0; ntl < 2; ntl++) {
+    const int n = 32 * wave + 16 * ntl + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      const int k0 = 32 * ks + 8 * (lane >> 4);
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float gv = INV ? Gf[(k0 + e) * D + n] : Gf[n * D + k0 + e];
+        h[e] = __builtin_bit_cast(uint16_t, (_Float16)gv);
+      }
+      f.hi[ntl][ks] = pack8(h);
     }
   }
 }
@@ -150,6 +178,33 @@ struct TileFetch {
   }
 };
 
+// The 32 values of row t, channels 32 j .. 32 j + 31 (thread 4t + j, the four
+// threads of a row adjacent lanes) as fp16 in sh, after a power-of-two scale
+// 2^k of the row that puts its largest magnitude in [2^13, 2^14) (exact, and
+// far from fp16's limits); rsc[t] = 2^-k undoes it after the product.  fp16
+// keeps 11 significant bits of every value of the row's top 2^-13 of range:
+// each value within 2^-12 of itself, or 2^-25 of the row maximum.
+__device__ __forceinline__ void scaled_f16_32(uint16_t *sh, float *rsc, int t, int j, const float (&v)[32]) {
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < 32; k++) m = fmaxf(m, fabsf(v[k]));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  const int e = (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127;   // m = 0 or subnormal: -127
+  const int k = m > 0.f ? min(13 - e, 127) : 0;
+  const float sc = __uint_as_float((uint32_t)(k + 127) << 23);
+  if (j == 0) rsc[t] = __uint_as_float((uint32_t)(127 - k) << 23);
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t h[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; e2++)
+      h[e2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[8 * q + 2 * e2] * sc)) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[8 * q + 2 * e2 + 1] * sc)) << 16);
+    *(uint4 *)(sh + t * HP + 32 * j + 8 * q) = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+}
+
 // the 32 values of row t, channels 32 j .. 32 j + 31 -> split tiles
 __device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j, const float (&v)[32]) {
 #pragma unroll
@@ -167,7 +222,8 @@ __device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j
 // X G^T (forward fragments) or X G (inverse fragments) of the split tile into
 // the fp32 tile xs, which may overlay sh/sl.  EXACT: every tile value is a
 // bf16 number (no lo part: two passes instead of three).  HI_ONLY (with
-// EXACT): one pass, against G_hi only.  Each accumulator
+// EXACT): one pass, against G_hi only.  F16 (with HI_ONLY): the tile and the
+// fragments hold fp16 values (load_g128_f16).  Each accumulator
 // takes its products in the order ks = 0..3, and within a ks hi*G_hi,
 // hi*G_lo, lo*G_hi, so results depend on the tile only.  Contains two
 // workgroup barriers; the caller has synchronized after writing sh/sl.
@@ -175,11 +231,12 @@ __device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j
 // scale_r (q G)[r][n] + min_r cs[n], with (min_r, scale_r) = rowp[r] and
 // cs[n] the column sums of the matrix (the dequantized tile min + q scale
 // times the matrix, with the range applied after the product).
-template <bool EXACT, bool AFFINE = false, bool HI_ONLY = false>
+template <bool EXACT, bool AFFINE = false, bool HI_ONLY = false, bool F16 = false>
 __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t *sl, float *xs,
                                               const G128Frags &f, const float2 *rowp = nullptr,
-                                              const float *cs = nullptr) {
+                                              const float *cs = nullptr, const float *rsc = nullptr) {
   static_assert(!HI_ONLY || EXACT, "one pass needs bf16 tile values");
+  static_assert(!F16 || HI_ONLY, "the fp16 form is one pass over fp16 tile values and load_g128_f16 fragments");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   f32x4_t acc[4][2];
@@ -202,8 +259,14 @@ __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-      for (int ntl = 0; ntl < 2; ntl++)
-        acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mt], f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
+      for (int ntl = 0; ntl < 2; ntl++) {
+        if constexpr (F16)
+          acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, ah[mt]),
+                                                                __builtin_bit_cast(f16x8_t, f.hi[ntl][ks]),
+                                                                acc[mt][ntl], 0, 0, 0);
+        else
+          acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mt], f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
+      }
     if (!HI_ONLY) {
 #pragma unroll
       for (int mt = 0; mt < 4; mt++)
@@ -233,6 +296,20 @@ __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t
         const float c = ntl ? c1 : c0;
 #pragma unroll
         for (int i = 0; i < 4; i++) xs[(m0 + i) * PITCH + n] = fmaf(sc[i], acc[mt][ntl][i], mn[i] * c);
+      }
+    }
+  } else if (rsc) {  // rows scaled before the product: undo the scale
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+      const int m0 = 16 * mt + 4 * (lane >> 4);
+      const float4 r = *(const float4 *)(rsc + m0);
+#pragma unroll
+      for (int ntl = 0; ntl < 2; ntl++) {
+        const int n = 32 * wave + 16 * ntl + (lane & 15);
+        xs[(m0 + 0) * PITCH + n] = acc[mt][ntl].x * r.x;
+        xs[(m0 + 1) * PITCH + n] = acc[mt][ntl].y * r.y;
+        xs[(m0 + 2) * PITCH + n] = acc[mt][ntl].z * r.z;
+        xs[(m0 + 3) * PITCH + n] = acc[mt][ntl].w * r.w;
       }
     }
   } else {

@@ -225,13 +225,14 @@ __device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, i
                                                     const float (&v)[32], int nrows,
                                                     const TileGauge<kChainInv<G, BF16>, true> &tg,
                                                     const SplitGaugeFrags<kSplitInv<G, BF16> ? G : 16> &sg,
-                                                    const G128Frags &fr) {
+                                                    const G128Frags &fr, float *rsc = nullptr) {
   float *xs = (float *)lds;
   if constexpr (kDense<G, BF16>) {
-    uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
-    split32(sh, sl, t, j, v);
+    // rows scaled into fp16, one fp16 pass against load_g128_f16 fragments
+    uint16_t *sh = (uint16_t *)lds;
+    scaled_f16_32(sh, rsc, t, j, v);
     __syncthreads();
-    gauge128_tile<false>(sh, sl, xs, fr);
+    gauge128_tile<true, false, true, true>(sh, sh, xs, fr, nullptr, nullptr, rsc);
   } else if constexpr (kSplitInv<G, BF16>) {
     split_store32(lds, t, j, v);
     __syncthreads();
@@ -397,7 +398,7 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
   if constexpr (kDense<G, BF16>) {
-    load_g128<true>(Gf, fr);
+    load_g128_f16<true>(Gf, fr);
     // inverse matrix B[k][n] = G[k][n]: column sums in a fixed order
     if (threadIdx.x < D) {
       float c = 0.0f;
@@ -435,7 +436,7 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
     const int nrows = tile_rows(a, tile);
     if constexpr (kDense<G, BF16>) {
       // block-uniform ranges are one per block: (min + q step) G = step (q G) + min colsum(G),
-      // and the codes (at most 8 bits) are exact bf16 values: two passes, no split
+      // and the codes (at most 8 bits) are exact fp16 values: one fp16 pass
       uint32_t q[32];
       if (t < nrows) {
         unpack32<BITS>(wd, q);
@@ -449,14 +450,14 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
         uint32_t h[4];
 #pragma unroll
         for (int e = 0; e < 4; e++)
-          h[e] = (__float_as_uint((float)q[8 * k4 + 2 * e]) >> 16) |
-                 (__float_as_uint((float)q[8 * k4 + 2 * e + 1]) & 0xFFFF0000u);
+          h[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(uint16_t)q[8 * k4 + 2 * e]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(uint16_t)q[8 * k4 + 2 * e + 1]) << 16);
         *(uint4 *)(sh + t * HP + 32 * j + 8 * k4) = make_uint4(h[0], h[1], h[2], h[3]);
       }
       if (j == 0) rowp[t] = t < nrows ? make_float2(mn, sc) : make_float2(0.0f, 0.0f);
       if (tile + 1 < tend) fetch(tile + 1);
       __syncthreads();
-      gauge128_tile<true, true>(sh, sh, xs, fr, rowp, csum);
+      gauge128_tile<true, true, true, true>(sh, sh, xs, fr, rowp, csum);
     } else {
       float v[32];
       if (t < nrows) {
@@ -634,7 +635,8 @@ __device__ __forceinline__ void kivi_decode_body(const uint8_t *__restrict__ pay
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
-  if constexpr (kDense<G, BF16>) load_g128<true>(Gf, fr);
+  if constexpr (kDense<G, BF16>) load_g128_f16<true>(Gf, fr);
+  __shared__ __align__(16) float rsc[kDense<G, BF16> ? TILE_T : 1];
   TileGauge<kChainInv<G, BF16>, true> tg;
   SplitGaugeFrags<kSplitInv<G, BF16> ? G : 16> sg;
   if constexpr (kSplitInv<G, BF16>)
@@ -706,7 +708,7 @@ __device__ __forceinline__ void kivi_decode_body(const uint8_t *__restrict__ pay
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
     if (tile + 1 < tend) fetch(tile + 1);
-    inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, sg, fr);
+    inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, sg, fr, rsc);
     const size_t off = (size_t)(f * a.tcap + tb) * D * ESZ;
     if (a.ref)
       store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);

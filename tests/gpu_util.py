@@ -112,6 +112,36 @@ def check_dense_forward(xg, x, Gf, where=None):
     return rel
 
 
+def check_dense_inverse(got, deq, Gf, where=None, row_min=None):
+    """Decoded bf16 rows of the full-head decoders against the fp64 inverse
+    gauge of the oracle's dequantized values `deq`.  The decoders form the
+    product in fp16 with fp32 sums: KIVI-style rows scaled by a power of two
+    into fp16's range (each value and each gauge entry within 2^-11 of
+    itself), so the unrounded result is within 2^-10 sum_k |G_kc| |x_k|.
+    Block-uniform rows (`row_min`: the minimum of each row's block) multiply
+    the exact codes q = (x - min) / step and add min * colsum(G) after the
+    product, so there the gauge rounding scales with sum |G| |x - min| and
+    the fp32 sums with |min| sum |G|: the sums of the bound run over
+    |x| + |x - min|.  The bf16 rounding adds at most 2^-8 of the value.
+    Every element must satisfy |got - ref| <= 2^-8 |ref| + 2^-9 sum |G| m
+    (m = |x|, or |x| + |x - min|), and the 1e-2 bar as max|err| / max|ref|.
+    Returns that relative error."""
+    x64 = np.asarray(deq, np.float64)
+    G64 = np.asarray(Gf, np.float64)
+    ref = oracle.gauge_inverse_f64(x64, G64, 128)
+    m = np.abs(x64)
+    if row_min is not None:
+        m = m + np.abs(x64 - np.asarray(row_min, np.float64).reshape(-1, 1))
+    mag = oracle.gauge_inverse_f64(m, np.abs(G64), 128)
+    val = oracle.to_f32(got).astype(np.float64)
+    err = np.abs(val - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -9 * mag
+    assert np.all(err <= bound), (where, float(np.max(err / np.maximum(bound, 1e-300))))
+    rel = float(np.max(err) / max(np.max(np.abs(ref)), 1e-30))
+    assert rel <= 1e-2, (where, rel)
+    return rel
+
+
 def split_inverse(storage_dtype, g):
     """True where the library's decoders apply the inverse gauge as
     split-precision bf16 matrix-core products: bf16 storage with g = 16 or

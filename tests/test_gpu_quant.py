@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from fixed_rate_compression_amd import binding as cg
-from gpu_util import (D, check_decoded, check_dense_forward, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu, n_fields,
+from gpu_util import (D, check_decoded, check_dense_forward, check_dense_inverse, empty_u8, gauge_of_field, gauges_for, kv_cpu, kv_gpu, n_fields,
                       to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -206,7 +206,9 @@ def test_dense_gauge_staged(backend, bits, blk, res):
             assert np.array_equal(pay[f * per:(f + 1) * per], p_ref)
             assert np.array_equal(meta.reshape(-1, T // blk, 2)[f].view(np.uint32), m_ref.view(np.uint32))
             deq = oracle.bu_decode_field(p_ref, m_ref, T, D, blk, bits)
+            rmin = np.repeat(m_ref.reshape(-1, 2)[:, 0], blk)
         else:
+            rmin = None
             kind = (f // (B * H)) % KV
             p_ref, m_ref, tail = oracle.kivi_encode_field(xg[f], kind, 32, bits, res)
             pq, pt, mf = kivi_split(pay, meta, f, T, res, bits, 2)
@@ -215,8 +217,7 @@ def test_dense_gauge_staged(backend, bits, blk, res):
             tail_st = oracle.f32_to_bf16(tail)
             assert np.array_equal(pt, tail_st.view(np.uint8).reshape(-1))
             deq = oracle.kivi_decode_field(p_ref, m_ref, oracle.to_f32(tail_st), T, D, kind, 32, bits, res)
-        ref_o = oracle.gauge_inverse_f64(deq, Gf, 128)
-        worst_o = max(worst_o, rel_err(oracle.to_f32(out[f]), ref_o))
+        worst_o = max(worst_o, check_dense_inverse(out[f], deq, Gf, f, rmin))
     print(f"dense gauge max rel err {worst_g:.3e}; decoded (bf16) max rel err {worst_o:.3e}")
     assert worst_o <= 1e-2
 
@@ -352,13 +353,14 @@ def test_full_head_config_sampled_fields(backend, bits, blk, res):
             tail_st = oracle.f32_to_bf16(tail)
             assert np.array_equal(pf[Tq * D * bits // 8:], tail_st.view(np.uint8).reshape(-1)), (l, s, h)
             deq = oracle.kivi_decode_field(p_ref, m_ref, oracle.to_f32(tail_st), T, D, s, 32, bits, res)
+            rmin = None
         else:
             p_ref, m_ref = oracle.bu_encode_field(xg, blk, bits)
             assert np.array_equal(pf, p_ref), (l, s, h)
             deq = oracle.bu_decode_field(p_ref, m_ref, T, D, blk, bits)
+            rmin = np.repeat(m_ref.reshape(-1, 2)[:, 0], blk)
         assert np.array_equal(mf.view(np.uint32), m_ref.reshape(-1, 2).view(np.uint32)), (l, s, h)
-        ref = oracle.gauge_inverse_f64(deq, Gf.astype(np.float64), 128)
-        worst_o = max(worst_o, rel_err(oracle.to_f32(to_host(out[f])), ref))
+        worst_o = max(worst_o, check_dense_inverse(to_host(out[f]), deq, Gf, (l, s, h), rmin))
         print(f"  field (layer {l}, kv {s}, head {h}) ok", flush=True)
     print(f"gauge rel err {worst_g:.3e}; decoded cache vs fp64 inverse {worst_o:.3e}")
     assert worst_o <= 1e-2
