@@ -53,6 +53,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, cg_bf16x2_t));
 }
 
+// Marks registers that global loads fill as read at this point (an empty
+// asm statement, no instruction), so the wait for those loads is placed
+// here.  The wait counter of vector memory operations drains in issue order
+// and also counts stores; where a prefetch is followed by a run of predicated
+// row stores, the compiler's wait at the data's first real use is counted
+// from the path without the stores and so also waits for the stores to be
+// acknowledged.  Calling this after the work that hides the loads and before
+// the stores puts the wait where only the loads are outstanding.
+__device__ __forceinline__ void loads_done(uint32_t x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void loads_done(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void loads_done(const uint4 &x) {
+  asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+}
+template <typename T, int N>
+__device__ __forceinline__ void loads_done(const T (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; i++) loads_done(x[i]);
+}
+
 // rows [0, nrows) of a [rows][128] storage-format array -> LDS fp32 tile
 template <bool BF16>
 __device__ __forceinline__ void load_tile(const void *__restrict__ src, int nrows, float *xs) {

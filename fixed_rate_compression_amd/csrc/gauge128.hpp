@@ -82,27 +82,24 @@ __device__ __forceinline__ void load_g128(const float *__restrict__ Gf, G128Frag
   }
 }
 
-// fp16 B fragments (one round-to-nearest part, bit patterns held in f.hi;
-// f.lo unused), for tiles of small integer codes: the codes are exact in
-// fp16 and G's fp16 part is within 2^-11 |G| (2^-25 absolute below fp16's
-// normal range), so one fp16 pass beats two bf16 passes' worth of accuracy
-// needs for a bf16 result
-template <bool INV>
+// Inverse-gauge fragments for the full-head decoders (fp16, one
+// round-to-nearest part held in f.hi, f.lo unused; G's fp16 part is within
+// 2^-11 |G|, 2^-25 absolute below fp16's normal range).  Wave w computes
+// channels 32 w .. + 31 as two 16-channel blocks ntl; fragment column i of
+// block ntl stands for channel 32 w + 8 (i / 4) + 4 ntl + i % 4, so that
+// after gauge128_f16_rows each lane holds 8 consecutive channels of a row.
 __device__ __forceinline__ void load_g128_f16(const float *__restrict__ Gf, G128Frags &f) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, i = lane & 15;
 #pragma unroll
   for (int ntl = 0; ntl < 2; ntl++) {
-    const int n = 32 * wave + 16 * ntl + (lane & 15);
+    const int n = 32 * wave + 8 * (i >> 2) + 4 * ntl + (i & 3);
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
       const int k0 = 32 * ks + 8 * (lane >> 4);
       uint32_t h[8];
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const float gv = INV ? Gf[(k0 + e) * D + n] : Gf[n * D + k0 + e];
-        h[e] = __builtin_bit_cast(uint16_t, (_Float16)gv);
-      }
+      for (int e = 0; e < 8; e++) h[e] = __builtin_bit_cast(uint16_t, (_Float16)Gf[(k0 + e) * D + n]);
       f.hi[ntl][ks] = pack8(h);
     }
   }
@@ -222,21 +219,14 @@ __device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j
 // X G^T (forward fragments) or X G (inverse fragments) of the split tile into
 // the fp32 tile xs, which may overlay sh/sl.  EXACT: every tile value is a
 // bf16 number (no lo part: two passes instead of three).  HI_ONLY (with
-// EXACT): one pass, against G_hi only.  F16 (with HI_ONLY): the tile and the
-// fragments hold fp16 values (load_g128_f16).  Each accumulator
+// EXACT): one pass, against G_hi only.  Each accumulator
 // takes its products in the order ks = 0..3, and within a ks hi*G_hi,
 // hi*G_lo, lo*G_hi, so results depend on the tile only.  Contains two
 // workgroup barriers; the caller has synchronized after writing sh/sl.
-// AFFINE: the tile holds integer codes q and the result is written as
-// scale_r (q G)[r][n] + min_r cs[n], with (min_r, scale_r) = rowp[r] and
-// cs[n] the column sums of the matrix (the dequantized tile min + q scale
-// times the matrix, with the range applied after the product).
-template <bool EXACT, bool AFFINE = false, bool HI_ONLY = false, bool F16 = false>
+template <bool EXACT, bool HI_ONLY = false>
 __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t *sl, float *xs,
-                                              const G128Frags &f, const float2 *rowp = nullptr,
-                                              const float *cs = nullptr, const float *rsc = nullptr) {
+                                              const G128Frags &f) {
   static_assert(!HI_ONLY || EXACT, "one pass needs bf16 tile values");
-  static_assert(!F16 || HI_ONLY, "the fp16 form is one pass over fp16 tile values and load_g128_f16 fragments");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   f32x4_t acc[4][2];
@@ -259,14 +249,8 @@ __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-      for (int ntl = 0; ntl < 2; ntl++) {
-        if constexpr (F16)
-          acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, ah[mt]),
-                                                                __builtin_bit_cast(f16x8_t, f.hi[ntl][ks]),
-                                                                acc[mt][ntl], 0, 0, 0);
-        else
-          acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mt], f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
-      }
+      for (int ntl = 0; ntl < 2; ntl++)
+        acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mt], f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
     if (!HI_ONLY) {
 #pragma unroll
       for (int mt = 0; mt < 4; mt++)
@@ -283,49 +267,52 @@ __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t
     }
   }
   __syncthreads();  // every wave has read its operands: xs may overwrite them
-  if constexpr (AFFINE) {
-    const float c0 = cs[32 * wave + (lane & 15)], c1 = cs[32 * wave + 16 + (lane & 15)];
 #pragma unroll
-    for (int mt = 0; mt < 4; mt++) {
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int ntl = 0; ntl < 2; ntl++) {
+      const int n = 32 * wave + 16 * ntl + (lane & 15);
       const int m0 = 16 * mt + 4 * (lane >> 4);
-      const float4 pa = *(const float4 *)(rowp + m0), pb = *(const float4 *)(rowp + m0 + 2);
-      const float mn[4] = {pa.x, pa.z, pb.x, pb.z}, sc[4] = {pa.y, pa.w, pb.y, pb.w};
-#pragma unroll
-      for (int ntl = 0; ntl < 2; ntl++) {
-        const int n = 32 * wave + 16 * ntl + (lane & 15);
-        const float c = ntl ? c1 : c0;
-#pragma unroll
-        for (int i = 0; i < 4; i++) xs[(m0 + i) * PITCH + n] = fmaf(sc[i], acc[mt][ntl][i], mn[i] * c);
-      }
+      xs[(m0 + 0) * PITCH + n] = acc[mt][ntl].x;
+      xs[(m0 + 1) * PITCH + n] = acc[mt][ntl].y;
+      xs[(m0 + 2) * PITCH + n] = acc[mt][ntl].z;
+      xs[(m0 + 3) * PITCH + n] = acc[mt][ntl].w;
     }
-  } else if (rsc) {  // rows scaled before the product: undo the scale
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++) {
-      const int m0 = 16 * mt + 4 * (lane >> 4);
-      const float4 r = *(const float4 *)(rsc + m0);
-#pragma unroll
-      for (int ntl = 0; ntl < 2; ntl++) {
-        const int n = 32 * wave + 16 * ntl + (lane & 15);
-        xs[(m0 + 0) * PITCH + n] = acc[mt][ntl].x * r.x;
-        xs[(m0 + 1) * PITCH + n] = acc[mt][ntl].y * r.y;
-        xs[(m0 + 2) * PITCH + n] = acc[mt][ntl].z * r.z;
-        xs[(m0 + 3) * PITCH + n] = acc[mt][ntl].w * r.w;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-      for (int ntl = 0; ntl < 2; ntl++) {
-        const int n = 32 * wave + 16 * ntl + (lane & 15);
-        const int m0 = 16 * mt + 4 * (lane >> 4);
-        xs[(m0 + 0) * PITCH + n] = acc[mt][ntl].x;
-        xs[(m0 + 1) * PITCH + n] = acc[mt][ntl].y;
-        xs[(m0 + 2) * PITCH + n] = acc[mt][ntl].z;
-        xs[(m0 + 3) * PITCH + n] = acc[mt][ntl].w;
-      }
-  }
   __syncthreads();
+}
+
+// X G for rows 16 MT0 .. 16 (MT0 + NMT) - 1 of the fp16 tile sh (row pitch
+// HP) and the fragments of load_g128_f16, as the transposed product: the
+// fragment is the first operand and the tile the second, so that
+//   acc[m][ntl][e] = (X G)[16 (MT0 + m) + lane % 16][32 wave + 8 (lane / 16) + 4 ntl + e]
+// (a 16x16x32 product leaves D[4 (lane / 16) + e][lane % 16] in lane; with
+// the operands swapped D is the transpose of the output block).  No
+// barrier here; the caller has synchronized after writing sh and must not
+// overwrite it before every wave has returned.
+template <int MT0, int NMT>
+__device__ __forceinline__ void gauge128_f16_rows(const uint16_t *sh, const G128Frags &f,
+                                                  f32x4_t (&acc)[NMT][2]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 0; m < NMT; m++) {
+    acc[m][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // k-step outermost: the 2 NMT accumulators advance together
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) {
+    bf16x8_t ah[NMT];
+#pragma unroll
+    for (int m = 0; m < NMT; m++)
+      ah[m] = *(const bf16x8_t *)(sh + (16 * (MT0 + m) + (lane & 15)) * HP + 8 * (lane >> 4) + 32 * ks);
+#pragma unroll
+    for (int m = 0; m < NMT; m++)
+#pragma unroll
+      for (int ntl = 0; ntl < 2; ntl++)
+        acc[m][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, f.hi[ntl][ks]),
+                                                             __builtin_bit_cast(f16x8_t, ah[m]),
+                                                             acc[m][ntl], 0, 0, 0);
+  }
 }
 
 }  // namespace cgk

@@ -193,6 +193,10 @@ struct GaugedTiles {
     pre.fetch(src, nrows);
   }
 
+  // the wait for the prefetched tile, placed by the caller after the work
+  // that hides it and before the tile's stores (see loads_done)
+  __device__ __forceinline__ void arrived() const { loads_done(pre.r); }
+
   // next_src/next_rows: the tile after this one (next_rows = 0: none)
   __device__ __forceinline__ void next(const void *__restrict__ src, int nrows,
                                        const void *__restrict__ next_src, int next_rows,
@@ -204,7 +208,7 @@ struct GaugedTiles {
       pre.put(sh, sl);
       __syncthreads();
       if (next_rows > 0) pre.fetch(next_src, next_rows);
-      gauge128_tile<BF16, false, BF16>(sh, sl, xs, fr);
+      gauge128_tile<BF16, BF16>(sh, sl, xs, fr);
     } else {
       (void)src;
       pre.put_f32(xs);
@@ -219,21 +223,17 @@ struct GaugedTiles {
 };
 
 // Every thread hands over its 32 decoded values (row t, channels 32 j ..);
-// apply the inverse gauge to the whole tile, result in the tile view of lds.
+// apply the inverse gauge to the whole tile, result in the tile view of lds
+// (every path but the full-head gauge with bf16 storage, which the decoders
+// run on fp16 operands with direct row stores).
 template <int G, bool BF16>
 __device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, int j,
                                                     const float (&v)[32], int nrows,
                                                     const TileGauge<kChainInv<G, BF16>, true> &tg,
-                                                    const SplitGaugeFrags<kSplitInv<G, BF16> ? G : 16> &sg,
-                                                    const G128Frags &fr, float *rsc = nullptr) {
+                                                    const SplitGaugeFrags<kSplitInv<G, BF16> ? G : 16> &sg) {
+  static_assert(!kDense<G, BF16>, "full-head bf16 decoders use gauge128_f16_rows");
   float *xs = (float *)lds;
-  if constexpr (kDense<G, BF16>) {
-    // rows scaled into fp16, one fp16 pass against load_g128_f16 fragments
-    uint16_t *sh = (uint16_t *)lds;
-    scaled_f16_32(sh, rsc, t, j, v);
-    __syncthreads();
-    gauge128_tile<true, false, true, true>(sh, sh, xs, fr, nullptr, nullptr, rsc);
-  } else if constexpr (kSplitInv<G, BF16>) {
+  if constexpr (kSplitInv<G, BF16>) {
     split_store32(lds, t, j, v);
     __syncthreads();
     gauge_tile_split<G>(lds, nrows, sg);
@@ -244,6 +244,109 @@ __device__ __forceinline__ void inverse_gauged_tile(unsigned char *lds, int t, i
     if constexpr (G != 0) {
       tg.apply(xs, nrows);
       __syncthreads();
+    }
+  }
+}
+
+// Full-head decoders: the product leaves each lane 16 B of one row (8
+// channels), so a wave could store only 64 B of each of 16 rows per
+// instruction, and such stores, with two waves completing each 128-byte
+// line, stream markedly slower than whole rows.  The bf16 results are
+// therefore staged in LDS as the tile's 64 rows x 256 B and stored as whole
+// rows, 4 rows per wave instruction (wave w: rows 16 w .. + 15).  The
+// 16-byte pieces of a staged row are swizzled, piece ^ (row % 16), so that
+// the writes (16 rows, one piece each) and the row reads both hit 64
+// distinct banks.
+constexpr int STAGE_BYTES = TILE_T * D * 2;
+
+__device__ __forceinline__ int stage_off(int r, int piece) { return r * 256 + 16 * (piece ^ (r & 15)); }
+
+// row blocks MT0 .. MT0 + NMT - 1 of the accumulators of gauge128_f16_rows
+// as bf16 into the staged tile.  AFFINE: value = scale_r acc + min_r cs[c]
+// with (min_r, scale_r) = rowp[r]; otherwise acc rsc[r].
+template <bool AFFINE, int MT0, int NMT>
+__device__ __forceinline__ void stage_rows(unsigned char *stage, const f32x4_t (&acc)[NMT][2],
+                                           const float *rsc, const float2 *rowp, const float *cs) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4;
+  const int c0 = 32 * wave + 8 * g;
+  float c[8];
+  if constexpr (AFFINE) {
+    const float4 ca = *(const float4 *)(cs + c0), cb = *(const float4 *)(cs + c0 + 4);
+    c[0] = ca.x; c[1] = ca.y; c[2] = ca.z; c[3] = ca.w;
+    c[4] = cb.x; c[5] = cb.y; c[6] = cb.z; c[7] = cb.w;
+  }
+#pragma unroll
+  for (int m = 0; m < NMT; m++) {
+    const int r = 16 * (MT0 + m) + (lane & 15);
+    float v[8];
+    if constexpr (AFFINE) {
+      const float2 pr = rowp[r];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        v[q] = fmaf(pr.y, acc[m][0][q], pr.x * c[q]);
+        v[4 + q] = fmaf(pr.y, acc[m][1][q], pr.x * c[4 + q]);
+      }
+    } else {
+      const float sr = rsc[r];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        v[q] = acc[m][0][q] * sr;
+        v[4 + q] = acc[m][1][q] * sr;
+      }
+    }
+    *(uint4 *)(stage + stage_off(r, 4 * wave + g)) =
+        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+  }
+}
+
+// the inverse gauge of the fp16 tile into the staged tile, in two halves of
+// 32 rows (fewer live accumulators)
+template <bool AFFINE>
+__device__ __forceinline__ void gauge_stage_tile(const uint16_t *sh, unsigned char *stage, const G128Frags &fr,
+                                                 const float *rsc, const float2 *rowp, const float *cs) {
+  {
+    f32x4_t acc[2][2];
+    gauge128_f16_rows<0, 2>(sh, fr, acc);
+    stage_rows<AFFINE, 0, 2>(stage, acc, rsc, rowp, cs);
+  }
+  {
+    f32x4_t acc[2][2];
+    gauge128_f16_rows<2, 2>(sh, fr, acc);
+    stage_rows<AFFINE, 2, 2>(stage, acc, rsc, rowp, cs);
+  }
+}
+
+// the reference rows the lanes store in store_staged (zeros past nrows)
+__device__ __forceinline__ void load_ref_rows(const uint8_t *__restrict__ ref, int nrows, uint4 (&rq)[4]) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int r = 16 * wave + 4 * k + (lane >> 4);
+    rq[k] = r < nrows ? *(const uint4 *)(ref + (size_t)r * D * 2 + 16 * (lane & 15)) : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// the staged tile's rows [0, nrows) -> bf16 rows at dst (the tile's first
+// row); with_ref: also the error sums against the rows rq of load_ref_rows
+__device__ __forceinline__ void store_staged(uint8_t *__restrict__ dst, int nrows, const unsigned char *stage,
+                                             bool with_ref, const uint4 (&rq)[4], ErrAcc &e) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int r = 16 * wave + 4 * k + (lane >> 4);
+    const uint4 w = *(const uint4 *)(stage + stage_off(r, lane & 15));
+    if (r < nrows) {
+      *(uint4 *)(dst + (size_t)r * D * 2 + 16 * (lane & 15)) = w;
+      if (with_ref) {
+        const uint4 q = rq[k];
+        e.add(bf16lo(w.x), bf16lo(q.x)); e.add(bf16hi(w.x), bf16hi(q.x));
+        e.add(bf16lo(w.y), bf16lo(q.y)); e.add(bf16hi(w.y), bf16hi(q.y));
+        e.add(bf16lo(w.z), bf16lo(q.z)); e.add(bf16hi(w.z), bf16hi(q.z));
+        e.add(bf16lo(w.w), bf16lo(q.w)); e.add(bf16hi(w.w), bf16hi(q.w));
+      }
     }
   }
 }
@@ -316,6 +419,7 @@ __device__ __forceinline__ void bu_encode_body(const void *__restrict__ kv,
   const int64_t tend = min(ntiles, (chunk + 1) * a.tiles_per_chunk);
   GaugedTiles<G, BF16> tiles;
   if (tile0 < tend) tiles.prefetch(src_f + (size_t)(a.t0 + tile0 * TILE_T) * D * ESZ, tile_rows(a, tile0));
+  tiles.arrived();
   for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
     const int nrows = tile_rows(a, tile);
@@ -339,6 +443,7 @@ __device__ __forceinline__ void bu_encode_body(const void *__restrict__ kv,
       red[2 * w + 1] = mx;
     }
     __syncthreads();
+    tiles.arrived();
     if (active) {
       const int wpb = BT / 16, w0 = (t / BT) * wpb;
       mn = red[2 * w0];
@@ -390,7 +495,7 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
   // dense gauge: (min, step) of each tile row and the column sums of the
   // inverse matrix, for the range applied after the product
   __shared__ __align__(16) float2 rowp[kDense<G, BF16> ? TILE_T : 1];
-  __shared__ float csum[kDense<G, BF16> ? D : 1];
+  __shared__ __align__(16) float csum[kDense<G, BF16> ? D : 1];
   float *xs = (float *)lds;
   const int64_t f = launch_field((int64_t)blockIdx.x / a.chunks, a.fsel, a.fstep, a.fbase);
   const int64_t chunk = (int64_t)blockIdx.x % a.chunks;
@@ -398,7 +503,7 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
   if constexpr (kDense<G, BF16>) {
-    load_g128_f16<true>(Gf, fr);
+    load_g128_f16(Gf, fr);
     // inverse matrix B[k][n] = G[k][n]: column sums in a fixed order
     if (threadIdx.x < D) {
       float c = 0.0f;
@@ -430,13 +535,21 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
     }
   };
   if (tile0 < tend) fetch(tile0);
+  if constexpr (kDense<G, BF16>) {
+    loads_done(wd);
+    loads_done(mn);
+    loads_done(sc);
+  }
   ErrAcc err;
   for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
     const int nrows = tile_rows(a, tile);
+    const size_t off = (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
     if constexpr (kDense<G, BF16>) {
       // block-uniform ranges are one per block: (min + q step) G = step (q G) + min colsum(G),
-      // and the codes (at most 8 bits) are exact fp16 values: one fp16 pass
+      // and the codes (at most 8 bits) are exact fp16 values: one fp16 pass.  The
+      // fp16 tile and the staged bf16 rows share lds; the barrier after the
+      // staging also orders this tile's reads of sh before the next tile's writes.
       uint32_t q[32];
       if (t < nrows) {
         unpack32<BITS>(wd, q);
@@ -445,6 +558,7 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
         for (int k = 0; k < 32; k++) q[k] = 0u;
       }
       uint16_t *sh = (uint16_t *)lds;
+      unsigned char *stage = lds + TILE_T * HP * 2;
 #pragma unroll
       for (int k4 = 0; k4 < 4; k4++) {
         uint32_t h[4];
@@ -457,7 +571,17 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
       if (j == 0) rowp[t] = t < nrows ? make_float2(mn, sc) : make_float2(0.0f, 0.0f);
       if (tile + 1 < tend) fetch(tile + 1);
       __syncthreads();
-      gauge128_tile<true, true, true, true>(sh, sh, xs, fr, rowp, csum);
+      gauge_stage_tile<true>(sh, stage, fr, nullptr, rowp, csum);
+      uint4 rq[4];
+      if (a.ref) load_ref_rows((const uint8_t *)a.ref + off, nrows, rq);
+      // the next tile's codes and ranges and the reference rows have arrived
+      // behind the products: wait for them before the stores (see loads_done)
+      loads_done(wd);
+      loads_done(mn);
+      loads_done(sc);
+      if (a.ref) loads_done(rq);
+      __syncthreads();
+      store_staged((uint8_t *)out + off, nrows, stage, a.ref != nullptr, rq, err);
     } else {
       float v[32];
       if (t < nrows) {
@@ -470,14 +594,13 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
         for (int k = 0; k < 32; k++) v[k] = 0.0f;
       }
       if (tile + 1 < tend) fetch(tile + 1);
-      inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, sg, fr);
+      inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, sg);
+      if (a.ref)
+        store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
+      else
+        store_tile<BF16>((uint8_t *)out + off, nrows, xs);
+      __syncthreads();
     }
-    const size_t off = (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
-    if (a.ref)
-      store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
-    else
-      store_tile<BF16>((uint8_t *)out + off, nrows, xs);
-    __syncthreads();
   }
   if (a.ref) write_err(err, a.epart);
 }
@@ -490,10 +613,10 @@ __global__ __launch_bounds__(NT) void k_bu_decode(const uint8_t *__restrict__ pa
   bu_decode_body<BITS, BF16, G>(payload, meta, gauges, out, a);
 }
 
-// the same with three waves per SIMD (launched for the full-head gauge with
-// bf16 storage, which fits in 168 VGPRs; other instances would spill)
+// the same with four waves per SIMD (launched for the full-head gauge with
+// bf16 storage below 8-bit codes, which fits in 128 VGPRs)
 template <int BITS, bool BF16, int G>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void k_bu_decode_w3(const uint8_t *__restrict__ payload,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_bu_decode_w4(const uint8_t *__restrict__ payload,
                                                   const float *__restrict__ meta,
                                                   const float *__restrict__ gauges,
                                                   void *__restrict__ out, QK a) {
@@ -538,31 +661,33 @@ __device__ __forceinline__ void kivi_encode_body(const void *__restrict__ kv,
   const int64_t tend = min(ntiles, (chunk + 1) * a.tiles_per_chunk);
   GaugedTiles<G, BF16> tiles;
   if (tile0 < tend) tiles.prefetch(src_f + (size_t)(a.t0 + tile0 * TILE_T) * D * ESZ, tile_rows(a, tile0));
+  tiles.arrived();
   for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
     const int nrows = tile_rows(a, tile);
     tiles.next(src_f + (size_t)tb * D * ESZ, nrows, src_f + (size_t)(tb + TILE_T) * D * ESZ,
                tile + 1 < tend ? tile_rows(a, tile + 1) : 0, lds, tg, fr);
+    // keys: this thread's column range (stored after the codes, so that no
+    // store precedes the wait for the prefetched tile)
+    const int gi = threadIdx.x >> 7, c = threadIdx.x & 127, r0 = 32 * gi;
+    const bool kcol = keys && r0 < nrows && tb + r0 < Tq;
+    Range krg{};
     if (keys) {
-      const int gi = threadIdx.x >> 7, c = threadIdx.x & 127;
-      const int r0 = 32 * gi;
-      if (r0 < nrows && tb + r0 < Tq) {
+      if (kcol) {
         float mn = INFINITY, mx = -INFINITY;
         for (int r = 0; r < 32; r++) {
           const float x = xs[(r0 + r) * PITCH + c];
           mn = fminf(mn, x);
           mx = fmaxf(mx, x);
         }
-        const Range rg = make_range(mn, mx, L);
-        pmn[threadIdx.x] = rg.mn;
-        pinv[threadIdx.x] = rg.inv;
-        pzero[threadIdx.x] = rg.zero;
-        float *m = mf + 2 * (((tb + r0) / 32) * D + c);
-        m[0] = rg.mn;
-        m[1] = rg.scale;
+        krg = make_range(mn, mx, L);
+        pmn[threadIdx.x] = krg.mn;
+        pinv[threadIdx.x] = krg.inv;
+        pzero[threadIdx.x] = krg.zero;
       }
       __syncthreads();
     }
+    tiles.arrived();
     if (t < nrows) {
       const int64_t row = tb + t;
       float v[32];
@@ -598,6 +723,11 @@ __device__ __forceinline__ void kivi_encode_body(const void *__restrict__ kv,
       } else {
         store32_storage<BF16>(pf + (size_t)Tcq * 16 * BITS + ((size_t)(row - Tq) * D + 32 * j) * ESZ, v);
       }
+    }
+    if (kcol) {
+      float *m = mf + 2 * (((tb + r0) / 32) * D + c);
+      m[0] = krg.mn;
+      m[1] = krg.scale;
     }
     __syncthreads();
   }
@@ -635,7 +765,8 @@ __device__ __forceinline__ void kivi_decode_body(const uint8_t *__restrict__ pay
   const int64_t ntiles = (a.nt + TILE_T - 1) / TILE_T;
   const float *Gf = G ? gauges + gauge_index(f, a.batch, a.heads) * D * (G ? G : 1) : nullptr;
   G128Frags fr;
-  if constexpr (kDense<G, BF16>) load_g128_f16<true>(Gf, fr);
+  if constexpr (kDense<G, BF16>) load_g128_f16(Gf, fr);
+  // dense gauge: the power-of-two row scales of the fp16 tile
   __shared__ __align__(16) float rsc[kDense<G, BF16> ? TILE_T : 1];
   TileGauge<kChainInv<G, BF16>, true> tg;
   SplitGaugeFrags<kSplitInv<G, BF16> ? G : 16> sg;
@@ -675,6 +806,13 @@ __device__ __forceinline__ void kivi_decode_body(const uint8_t *__restrict__ pay
     }
   };
   if (tile0 < tend) fetch(tile0);
+  if constexpr (kDense<G, BF16>) {
+    loads_done(wd);
+    loads_done(mn);
+    loads_done(sc);
+    loads_done(kmn);
+    loads_done(ksc);
+  }
   ErrAcc err;
   for (int64_t tile = tile0; tile < tend; tile++) {
     const int64_t tb = a.t0 + tile * TILE_T;
@@ -708,13 +846,37 @@ __device__ __forceinline__ void kivi_decode_body(const uint8_t *__restrict__ pay
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
     if (tile + 1 < tend) fetch(tile + 1);
-    inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, sg, fr, rsc);
     const size_t off = (size_t)(f * a.tcap + tb) * D * ESZ;
-    if (a.ref)
-      store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
-    else
-      store_tile<BF16>((uint8_t *)out + off, nrows, xs);
-    __syncthreads();
+    if constexpr (kDense<G, BF16>) {
+      // rows scaled into fp16, one fp16 pass, bf16 rows staged in lds beside
+      // the fp16 tile and stored whole; the barrier after the staging also
+      // orders this tile's reads of sh (and of the key ranges) before the
+      // next tile's writes.
+      uint16_t *sh = (uint16_t *)lds;
+      unsigned char *stage = lds + TILE_T * HP * 2;
+      scaled_f16_32(sh, rsc, t, j, v);
+      __syncthreads();
+      uint4 rq[4];
+      if (a.ref) load_ref_rows((const uint8_t *)a.ref + off, nrows, rq);
+      gauge_stage_tile<false>(sh, stage, fr, rsc, nullptr, nullptr);
+      // the next tile's codes and ranges and the reference rows have arrived
+      // behind the products: wait for them before the stores (see loads_done)
+      loads_done(wd);
+      loads_done(mn);
+      loads_done(sc);
+      loads_done(kmn);
+      loads_done(ksc);
+      if (a.ref) loads_done(rq);
+      __syncthreads();
+      store_staged((uint8_t *)out + off, nrows, stage, a.ref != nullptr, rq, err);
+    } else {
+      inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, sg);
+      if (a.ref)
+        store_tile_err<BF16>((uint8_t *)out + off, nrows, xs, (const uint8_t *)a.ref + off, err);
+      else
+        store_tile<BF16>((uint8_t *)out + off, nrows, xs);
+      __syncthreads();
+    }
   }
   if (a.ref) write_err(err, a.epart);
 }
@@ -765,7 +927,7 @@ __global__ __launch_bounds__(NT) void k_gauge128_rows(const void *__restrict__ s
     pre.put(sh, sl);
     __syncthreads();
     if (tile + 1 < tend) pre.fetch(src_f + (size_t)(tb + TILE_T) * D * ESZ, tile_rows(a, tile + 1));
-    gauge128_tile<BF16, false, BF16 && !INV>(sh, sl, xs, fr);
+    gauge128_tile<BF16, BF16 && !INV>(sh, sl, xs, fr);
     store_tile<false>(out + (size_t)(f * a.tcap + tb) * D, nrows, xs);
     __syncthreads();
   }

@@ -36,25 +36,35 @@ hipError_t quant_launch_bits(bool encode, bool bf16, int g, int backend, const v
   const QK a = make_qk(q, quant_chunk_tiles(g, q.fields, (q.nt + TILE_T - 1) / TILE_T));
   const dim3 grid((unsigned)(q.fields * a.chunks)), block(NT);
   const bool bu = backend == 2;
-  // W3: the kernels' three-waves-per-SIMD instances (full-head gauge, bf16 storage)
-#define CG_Q(BF, GG, W3)                                                                             \
+  // BE, BD, KE, KD: the instance suffixes of the block-uniform encoder and
+  // decoder and the KIVI-style encoder and decoder (_w3 / _w4: three / four
+  // waves per SIMD)
+#define CG_Q(BF, GG, BE, BD, KE, KD)                                                                 \
   if (bf16 == BF && g == GG) {                                                                       \
     if (bu && encode)                                                                                \
-      hipLaunchKernelGGL((k_bu_encode##W3<BITS, BF, GG>), grid, block, 0, s, src, gauges,           \
+      hipLaunchKernelGGL((k_bu_encode##BE<BITS, BF, GG>), grid, block, 0, s, src, gauges,           \
                          (uint8_t *)dst, meta_out, a);                                               \
     else if (bu)                                                                                     \
-      hipLaunchKernelGGL((k_bu_decode##W3<BITS, BF, GG>), grid, block, 0, s, (const uint8_t *)src,  \
+      hipLaunchKernelGGL((k_bu_decode##BD<BITS, BF, GG>), grid, block, 0, s, (const uint8_t *)src,  \
                          (const float *)meta_in, gauges, dst, a);                                    \
     else if (encode)                                                                                 \
-      hipLaunchKernelGGL((k_kivi_encode##W3<BITS, BF, GG>), grid, block, 0, s, src, gauges,         \
+      hipLaunchKernelGGL((k_kivi_encode##KE<BITS, BF, GG>), grid, block, 0, s, src, gauges,         \
                          (uint8_t *)dst, meta_out, a);                                               \
     else                                                                                             \
-      hipLaunchKernelGGL((k_kivi_decode##W3<BITS, BF, GG>), grid, block, 0, s, (const uint8_t *)src,\
+      hipLaunchKernelGGL((k_kivi_decode##KD<BITS, BF, GG>), grid, block, 0, s, (const uint8_t *)src,\
                          (const float *)meta_in, gauges, dst, a);                                    \
     return hipGetLastError();                                                                        \
   }
-  CG_Q(true, 0, ) CG_Q(true, 8, ) CG_Q(true, 16, ) CG_Q(true, 32, ) CG_Q(true, 128, _w3)
-  CG_Q(false, 0, ) CG_Q(false, 8, ) CG_Q(false, 16, ) CG_Q(false, 32, ) CG_Q(false, 128, )
+  CG_Q(true, 0, , , , ) CG_Q(true, 8, , , , ) CG_Q(true, 16, , , , ) CG_Q(true, 32, , , , )
+  // full-head gauge with bf16 storage: the instances with more waves per SIMD
+  // fit their registers below 8-bit codes
+  if constexpr (BITS < 8) {
+    CG_Q(true, 128, _w3, _w4, _w3, _w3)
+  } else {
+    CG_Q(true, 128, , , , )
+  }
+  CG_Q(false, 0, , , , ) CG_Q(false, 8, , , , ) CG_Q(false, 16, , , , ) CG_Q(false, 32, , , , )
+  CG_Q(false, 128, , , , )
 #undef CG_Q
   return hipErrorInvalidValue;
 }

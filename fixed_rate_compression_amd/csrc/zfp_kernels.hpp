@@ -401,7 +401,7 @@ __global__ __launch_bounds__(NT) void k_zfp_encode128(const void *__restrict__ k
     pre.put(sh, sl);
     __syncthreads();
     if (tile + 1 < tend) pre.fetch(src_f + (size_t)(tb + TILE_T) * D * esz, rows(tile + 1));
-    gauge128_tile<BF16, false, BF16>(sh, sl, xs, fr);
+    gauge128_tile<BF16, BF16>(sh, sl, xs, fr);
     if (nrows & 3) {
       pad_block_row(xs, nrows);
       __syncthreads();

@@ -5,7 +5,9 @@
   kernels are quoted against next to the 8 TB/s peak (stream.hip).
 - Instruction-issue probes (issue.hip): the rate of single VALU instruction
   forms (which ones pair up in one issue slot), and whether matrix-core and
-  VALU work overlap.  `python3 -m fixed_rate_compression_amd.probe issue`."""
+  VALU work overlap.  `python3 -m fixed_rate_compression_amd.probe issue`;
+  `... probe stream` prints the streaming kernels' rates on a 4.29 GB
+  tensor, with the decode-shaped kernel in both store patterns."""
 from __future__ import annotations
 
 import ctypes
@@ -16,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = [os.path.join(_HERE, "stream.hip"), os.path.join(_HERE, "issue.hip")]
 _LIB = os.path.join(_HERE, "libcgprobe.so")
 
-MODES = {"copy": (0, 1, 1), "enc": (1, 4, 1), "dec": (2, 1, 4)}   # name: (mode, read, write)
+MODES = {"copy": (0, 1, 1), "enc": (1, 4, 1), "dec": (2, 1, 4), "dec_rows": (3, 1, 4), "dec_rows_nt": (4, 1, 4),
+         "dec_rows128": (5, 1, 4)}   # name: (mode, read, write)
 
 
 def build(force: bool = True) -> str:
@@ -64,19 +67,19 @@ def stream(name: str, src, dst, stream=None) -> None:
         raise RuntimeError(f"cgprobe_stream({name}) failed with {rc}")
 
 
-def ceilings(kv, steps: int = 10, warmup: int = 2) -> dict:
+def ceilings(kv, steps: int = 10, warmup: int = 2, names=("copy", "enc", "dec")) -> dict:
     """HBM GB/s (bytes read + written per second, median over `steps` timed
-    launches) of the three kernels on the tensor `kv` (the copy and the
-    encode-shaped kernel read it; the decode-shaped kernel reads a quarter
-    of its size and writes its full size)."""
+    launches) of the kernels `names` (keys of MODES) on the tensor `kv` (the
+    copy and the encode-shaped kernel read it; the decode-shaped kernels
+    read a quarter of its size and write its full size)."""
     import numpy as np
     import torch
     nb = kv.numel() * kv.element_size()
     flat = kv.view(torch.uint8).view(-1)
     out = {}
-    for name in ("copy", "enc", "dec"):
+    for name in names:
         _, rin, rout = MODES[name]
-        if name == "dec":
+        if rout > rin:
             src = flat[: nb // 4]
             dst = torch.empty(nb, dtype=torch.uint8, device=kv.device)
         else:
