@@ -115,6 +115,9 @@ constexpr int HP = 136;
 constexpr int SPLIT_BYTES = 2 * TILE_T * HP * 2;                 // hi + lo tiles
 constexpr int TILE_BYTES = TILE_T * PITCH * 4;                   // fp32 tile
 constexpr int LDS_TILE_BYTES = SPLIT_BYTES > TILE_BYTES ? SPLIT_BYTES : TILE_BYTES;
+// the fp32 tile and, after it, one bf16 operand tile (tiles of bf16 values
+// need no lo part) in separate LDS
+constexpr int APART_TILE_BYTES = TILE_BYTES + TILE_T * HP * 2;
 
 // two values -> packed bf16 hi parts and packed bf16 remainders (each part
 // round-to-nearest-even, as split_bf16)
@@ -222,8 +225,10 @@ __device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j
 // EXACT): one pass, against G_hi only.  Each accumulator
 // takes its products in the order ks = 0..3, and within a ks hi*G_hi,
 // hi*G_lo, lo*G_hi, so results depend on the tile only.  Contains two
-// workgroup barriers; the caller has synchronized after writing sh/sl.
-template <bool EXACT, bool HI_ONLY = false>
+// workgroup barriers (one with APART: xs does not overlay sh/sl, so the
+// results need not wait for the other waves' operand reads); the caller has
+// synchronized after writing sh/sl.
+template <bool EXACT, bool HI_ONLY = false, bool APART = false>
 __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t *sl, float *xs,
                                               const G128Frags &f) {
   static_assert(!HI_ONLY || EXACT, "one pass needs bf16 tile values");
@@ -266,7 +271,7 @@ __device__ __forceinline__ void gauge128_tile(const uint16_t *sh, const uint16_t
           acc[mt][ntl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mt], f.hi[ntl][ks], acc[mt][ntl], 0, 0, 0);
     }
   }
-  __syncthreads();  // every wave has read its operands: xs may overwrite them
+  if (!APART) __syncthreads();  // every wave has read its operands: xs may overwrite them
 #pragma unroll
   for (int mt = 0; mt < 4; mt++)
 #pragma unroll

@@ -184,7 +184,17 @@ __device__ __forceinline__ void write32(float *xs, int t, int j, const float (&v
 // tile (rows [0, nrows); rows past nrows are zero) and applies the forward
 // gauge; the fp32 result is in the tile view of `lds` (PITCH floats per row).
 // The global loads of the following tile are issued before the gauge, so
-// they are in flight during the gauge and the quantizer work.
+// they are in flight during the gauge and the quantizer work.  Full-head
+// gauge: `lds` holds kEncLds<G, BF16> bytes, the fp32 tile apart from the
+// bf16 operand tile, so next() needs no barrier between the products and
+// their results, and the caller none after its reads of the fp32 tile (the
+// next call's barrier after the operand writes orders them).  Otherwise the
+// caller synchronizes after its reads of the fp32 tile before calling next()
+// again.
+// LDS bytes of the encoders' tile
+template <int G, bool BF16>
+constexpr int kEncLds = kDense<G, BF16> ? APART_TILE_BYTES : LDS_TILE_BYTES;
+
 template <int G, bool BF16>
 struct GaugedTiles {
   TileFetch<BF16> pre;
@@ -204,11 +214,11 @@ struct GaugedTiles {
                                        const G128Frags &fr) {
     float *xs = (float *)lds;
     if constexpr (kDense<G, BF16>) {
-      uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
-      pre.put(sh, sl);
+      uint16_t *sh = (uint16_t *)(lds + TILE_BYTES);
+      pre.put(sh, sh);
       __syncthreads();
       if (next_rows > 0) pre.fetch(next_src, next_rows);
-      gauge128_tile<BF16, BF16>(sh, sl, xs, fr);
+      gauge128_tile<true, true, true>(sh, sh, xs, fr);
     } else {
       (void)src;
       pre.put_f32(xs);
@@ -398,7 +408,7 @@ __device__ __forceinline__ void bu_encode_body(const void *__restrict__ kv,
                                                   const float *__restrict__ gauges,
                                                   uint8_t *__restrict__ payload,
                                                   float *__restrict__ meta, QK a) {
-  __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  __shared__ __align__(16) unsigned char lds[kEncLds<G, BF16>];
   float *xs = (float *)lds;
   __shared__ float red[8];
   constexpr int L = (1 << BITS) - 1;
@@ -464,7 +474,7 @@ __device__ __forceinline__ void bu_encode_body(const void *__restrict__ kv,
         m[1] = r.scale;
       }
     }
-    __syncthreads();
+    if constexpr (!kDense<G, BF16>) __syncthreads();  // see GaugedTiles
   }
 }
 
@@ -636,7 +646,7 @@ __device__ __forceinline__ void kivi_encode_body(const void *__restrict__ kv,
                                                     const float *__restrict__ gauges,
                                                     uint8_t *__restrict__ payload,
                                                     float *__restrict__ meta, QK a) {
-  __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
+  __shared__ __align__(16) unsigned char lds[kEncLds<G, BF16>];
   float *xs = (float *)lds;
   __shared__ float pmn[2 * D], pinv[2 * D];
   __shared__ uint8_t pzero[2 * D];
@@ -729,7 +739,7 @@ __device__ __forceinline__ void kivi_encode_body(const void *__restrict__ kv,
       m[0] = krg.mn;
       m[1] = krg.scale;
     }
-    __syncthreads();
+    if constexpr (!kDense<G, BF16>) __syncthreads();  // see GaugedTiles
   }
 }
 
