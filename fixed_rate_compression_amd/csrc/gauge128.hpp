@@ -178,31 +178,46 @@ struct TileFetch {
   }
 };
 
-// The 32 values of row t, channels 32 j .. 32 j + 31 (thread 4t + j, the four
-// threads of a row adjacent lanes) as fp16 in sh, after a power-of-two scale
-// 2^k of the row that puts its largest magnitude in [2^13, 2^14) (exact, and
-// far from fp16's limits); rsc[t] = 2^-k undoes it after the product.  fp16
-// keeps 11 significant bits of every value of the row's top 2^-13 of range:
-// each value within 2^-12 of itself, or 2^-25 of the row maximum.
-__device__ __forceinline__ void scaled_f16_32(uint16_t *sh, float *rsc, int t, int j, const float (&v)[32]) {
-  float m = 0.f;
-#pragma unroll
-  for (int k = 0; k < 32; k++) m = fmaxf(m, fabsf(v[k]));
+// The power-of-two scale 2^k of row t that puts m, the largest magnitude of
+// the row's values, in [2^13, 2^14) (exact, and far from fp16's limits),
+// from each of the row's four threads' part of m (thread 4t + j, the four
+// threads of a row adjacent lanes; every thread of the wave calls this);
+// rsc[t] = 2^-k undoes it after the product.  fp16 keeps 11 significant bits
+// of every value of the row's top 2^-13 of range: each scaled value within
+// 2^-12 of itself, or 2^-25 of the row maximum.
+__device__ __forceinline__ float f16_row_scale(float m, float *rsc, int t, int j) {
   m = fmaxf(m, __shfl_xor(m, 1));
   m = fmaxf(m, __shfl_xor(m, 2));
   const int e = (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127;   // m = 0 or subnormal: -127
   const int k = m > 0.f ? min(13 - e, 127) : 0;
-  const float sc = __uint_as_float((uint32_t)(k + 127) << 23);
   if (j == 0) rsc[t] = __uint_as_float((uint32_t)(127 - k) << 23);
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
+// 32 fp16 values (bit patterns, pairs packed low first) -> row t, channels
+// 32 j .. 32 j + 31 of the fp16 tile
+__device__ __forceinline__ void put_f16_32(uint16_t *sh, int t, int j, const uint32_t (&h)[16]) {
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    uint32_t h[4];
+  for (int q = 0; q < 4; q++)
+    *(uint4 *)(sh + t * HP + 32 * j + 8 * q) = make_uint4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+}
+
+__device__ __forceinline__ uint32_t f16x2_bits(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+// The 32 values of row t, channels 32 j .. 32 j + 31, scaled by the row's
+// f16_row_scale (from their largest magnitude) and stored as fp16 in sh.
+__device__ __forceinline__ void scaled_f16_32(uint16_t *sh, float *rsc, int t, int j, const float (&v)[32]) {
+  float m = 0.f;
 #pragma unroll
-    for (int e2 = 0; e2 < 4; e2++)
-      h[e2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[8 * q + 2 * e2] * sc)) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(v[8 * q + 2 * e2 + 1] * sc)) << 16);
-    *(uint4 *)(sh + t * HP + 32 * j + 8 * q) = make_uint4(h[0], h[1], h[2], h[3]);
-  }
+  for (int k = 0; k < 32; k++) m = fmaxf(m, fabsf(v[k]));
+  const float sc = f16_row_scale(m, rsc, t, j);
+  uint32_t h[16];
+#pragma unroll
+  for (int k = 0; k < 16; k++) h[k] = f16x2_bits(v[2 * k] * sc, v[2 * k + 1] * sc);
+  put_f16_32(sh, t, j, h);
 }
 
 // the 32 values of row t, channels 32 j .. 32 j + 31 -> split tiles

@@ -361,6 +361,32 @@ __device__ __forceinline__ void store_staged(uint8_t *__restrict__ dst, int nrow
   }
 }
 
+// Full-head decoders, after every thread has written its part of the fp16
+// tile (the start of lds, row pitch HP): the inverse gauge, the bf16 rows
+// staged beside the tile (stage_rows) and stored whole.  arrived() places
+// the wait for the prefetched next tile before the stores (see loads_done).
+// Two barriers; the second also orders this tile's reads of the fp16 tile,
+// of rsc / rowp and of the key ranges before the next tile's writes.  The
+// block-uniform decoder (AFFINE) loads the reference rows after the product
+// (it fits four waves' registers that way), the KIVI-style one before it.
+template <bool AFFINE, typename Arrived>
+__device__ __forceinline__ void decode_tile_dense(unsigned char *lds, const G128Frags &fr, const float *rsc,
+                                                  const float2 *rowp, const float *cs, int nrows,
+                                                  uint8_t *__restrict__ dst, const uint8_t *__restrict__ ref,
+                                                  ErrAcc &err, Arrived arrived) {
+  const uint16_t *sh = (const uint16_t *)lds;
+  unsigned char *stage = lds + TILE_T * HP * 2;
+  __syncthreads();
+  uint4 rq[4];
+  if (!AFFINE && ref) load_ref_rows(ref, nrows, rq);
+  gauge_stage_tile<AFFINE>(sh, stage, fr, rsc, rowp, cs);
+  if (AFFINE && ref) load_ref_rows(ref, nrows, rq);
+  arrived();
+  if (ref) loads_done(rq);
+  __syncthreads();
+  store_staged(dst, nrows, stage, ref != nullptr, rq, err);
+}
+
 // storage-format row segment of 32 values <-> fp32
 template <bool BF16>
 __device__ __forceinline__ void store32_storage(uint8_t *p, const float (&v)[32]) {
@@ -557,9 +583,8 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
     const size_t off = (size_t)(f * a.tcap + tb) * D * (BF16 ? 2 : 4);
     if constexpr (kDense<G, BF16>) {
       // block-uniform ranges are one per block: (min + q step) G = step (q G) + min colsum(G),
-      // and the codes (at most 8 bits) are exact fp16 values: one fp16 pass.  The
-      // fp16 tile and the staged bf16 rows share lds; the barrier after the
-      // staging also orders this tile's reads of sh before the next tile's writes.
+      // and the codes (at most 8 bits) are exact fp16 values: one fp16 pass
+      // (decode_tile_dense)
       uint32_t q[32];
       if (t < nrows) {
         unpack32<BITS>(wd, q);
@@ -568,7 +593,6 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
         for (int k = 0; k < 32; k++) q[k] = 0u;
       }
       uint16_t *sh = (uint16_t *)lds;
-      unsigned char *stage = lds + TILE_T * HP * 2;
 #pragma unroll
       for (int k4 = 0; k4 < 4; k4++) {
         uint32_t h[4];
@@ -580,18 +604,9 @@ __device__ __forceinline__ void bu_decode_body(const uint8_t *__restrict__ paylo
       }
       if (j == 0) rowp[t] = t < nrows ? make_float2(mn, sc) : make_float2(0.0f, 0.0f);
       if (tile + 1 < tend) fetch(tile + 1);
-      __syncthreads();
-      gauge_stage_tile<true>(sh, stage, fr, nullptr, rowp, csum);
-      uint4 rq[4];
-      if (a.ref) load_ref_rows((const uint8_t *)a.ref + off, nrows, rq);
-      // the next tile's codes and ranges and the reference rows have arrived
-      // behind the products: wait for them before the stores (see loads_done)
-      loads_done(wd);
-      loads_done(mn);
-      loads_done(sc);
-      if (a.ref) loads_done(rq);
-      __syncthreads();
-      store_staged((uint8_t *)out + off, nrows, stage, a.ref != nullptr, rq, err);
+      decode_tile_dense<true>(lds, fr, nullptr, rowp, csum, nrows, (uint8_t *)out + off,
+                              a.ref ? (const uint8_t *)a.ref + off : nullptr, err,
+                              [&] { loads_done(wd); loads_done(mn); loads_done(sc); });
     } else {
       float v[32];
       if (t < nrows) {
@@ -834,6 +849,7 @@ __device__ __forceinline__ void kivi_decode_body(const uint8_t *__restrict__ pay
       }
       __syncthreads();
     }
+    const size_t off = (size_t)(f * a.tcap + tb) * D * ESZ;
     float v[32];
     if (t < nrows) {
       const int64_t row = tb + t;
@@ -856,29 +872,17 @@ __device__ __forceinline__ void kivi_decode_body(const uint8_t *__restrict__ pay
       for (int k = 0; k < 32; k++) v[k] = 0.0f;
     }
     if (tile + 1 < tend) fetch(tile + 1);
-    const size_t off = (size_t)(f * a.tcap + tb) * D * ESZ;
     if constexpr (kDense<G, BF16>) {
-      // rows scaled into fp16, one fp16 pass, bf16 rows staged in lds beside
-      // the fp16 tile and stored whole; the barrier after the staging also
-      // orders this tile's reads of sh (and of the key ranges) before the
-      // next tile's writes.
-      uint16_t *sh = (uint16_t *)lds;
-      unsigned char *stage = lds + TILE_T * HP * 2;
-      scaled_f16_32(sh, rsc, t, j, v);
-      __syncthreads();
-      uint4 rq[4];
-      if (a.ref) load_ref_rows((const uint8_t *)a.ref + off, nrows, rq);
-      gauge_stage_tile<false>(sh, stage, fr, rsc, nullptr, nullptr);
-      // the next tile's codes and ranges and the reference rows have arrived
-      // behind the products: wait for them before the stores (see loads_done)
-      loads_done(wd);
-      loads_done(mn);
-      loads_done(sc);
-      loads_done(kmn);
-      loads_done(ksc);
-      if (a.ref) loads_done(rq);
-      __syncthreads();
-      store_staged((uint8_t *)out + off, nrows, stage, a.ref != nullptr, rq, err);
+      // rows scaled into fp16 from their largest magnitude
+      scaled_f16_32((uint16_t *)lds, rsc, t, j, v);
+      decode_tile_dense<false>(lds, fr, rsc, nullptr, nullptr, nrows, (uint8_t *)out + off,
+                               a.ref ? (const uint8_t *)a.ref + off : nullptr, err, [&] {
+                                 loads_done(wd);
+                                 loads_done(mn);
+                                 loads_done(sc);
+                                 loads_done(kmn);
+                                 loads_done(ksc);
+                               });
     } else {
       inverse_gauged_tile<G, BF16>(lds, t, j, v, nrows, tg, sg);
       if (a.ref)
