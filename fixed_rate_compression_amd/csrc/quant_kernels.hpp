@@ -663,8 +663,14 @@ __device__ __forceinline__ void kivi_encode_body(const void *__restrict__ kv,
                                                     float *__restrict__ meta, QK a) {
   __shared__ __align__(16) unsigned char lds[kEncLds<G, BF16>];
   float *xs = (float *)lds;
-  __shared__ float pmn[2 * D], pinv[2 * D];
-  __shared__ uint8_t pzero[2 * D];
+  // key column ranges of the tile's two 32-row groups (index 128 group +
+  // channel): the minimum in pmn; the inverse step in the fp32 tile's row
+  // padding (4 unused floats per row, exactly 256: kinv), 0 for a range that
+  // quantizes everything to code 0 (then clamp(rint((x - min) * 0), 0, L) =
+  // 0, as quant1 returns for it).  No flag array and no separate inverse
+  // array: the full-head encoder keeps three workgroups per CU.
+  __shared__ float pmn[2 * D];
+  auto kinv = [&](int i) -> float & { return xs[(i >> 2) * PITCH + D + (i & 3)]; };
   constexpr int L = (1 << BITS) - 1;
   constexpr size_t ESZ = BF16 ? 2 : 4;
   const int64_t f = (int64_t)blockIdx.x / a.chunks;
@@ -707,8 +713,7 @@ __device__ __forceinline__ void kivi_encode_body(const void *__restrict__ kv,
         }
         krg = make_range(mn, mx, L);
         pmn[threadIdx.x] = krg.mn;
-        pinv[threadIdx.x] = krg.inv;
-        pzero[threadIdx.x] = krg.zero;
+        kinv(threadIdx.x) = krg.zero ? 0.0f : krg.inv;
       }
       __syncthreads();
     }
@@ -725,8 +730,8 @@ __device__ __forceinline__ void kivi_encode_body(const void *__restrict__ kv,
           for (int k = 0; k < 32; k++) {
             Range rg;
             rg.mn = pmn[base + k];
-            rg.inv = pinv[base + k];
-            rg.zero = pzero[base + k];
+            rg.inv = kinv(base + k);
+            rg.zero = false;
             q[k] = quant1(v[k], rg, L);
           }
         } else {

@@ -7,7 +7,9 @@
   forms (which ones pair up in one issue slot), and whether matrix-core and
   VALU work overlap.  `python3 -m fixed_rate_compression_amd.probe issue`;
   `... probe stream` prints the streaming kernels' rates on a 4.29 GB
-  tensor, with the decode-shaped kernel in both store patterns."""
+  tensor, with the decode-shaped kernel in its store patterns.
+- LDS read-pattern probe (lds.hip): matrix-operand reads of a 64-row tile at
+  several row pitches and swizzles (`... probe lds`)."""
 from __future__ import annotations
 
 import ctypes
@@ -15,7 +17,7 @@ import os
 import subprocess
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = [os.path.join(_HERE, "stream.hip"), os.path.join(_HERE, "issue.hip")]
+_SRC = [os.path.join(_HERE, "stream.hip"), os.path.join(_HERE, "issue.hip"), os.path.join(_HERE, "lds.hip")]
 _LIB = os.path.join(_HERE, "libcgprobe.so")
 
 MODES = {"copy": (0, 1, 1), "enc": (1, 4, 1), "dec": (2, 1, 4), "dec_rows": (3, 1, 4), "dec_rows_nt": (4, 1, 4),
@@ -46,7 +48,7 @@ def lib():
         L.cgprobe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                      ctypes.c_uint64, ctypes.c_void_p]
         L.cgprobe_stream.restype = ctypes.c_int
-        for fn in (L.cgprobe_issue, L.cgprobe_overlap):
+        for fn in (L.cgprobe_issue, L.cgprobe_overlap, L.cgprobe_lds):
             fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.POINTER(ctypes.c_float)]
             fn.restype = ctypes.c_int
@@ -143,5 +145,25 @@ def overlap_times(iters: int = 2000) -> dict:
         ms = ctypes.c_float()
         if L.cgprobe_overlap(m, iters, out.data_ptr(), s, ctypes.byref(ms)) != 0:
             raise RuntimeError(f"cgprobe_overlap({m}) failed")
+        res[name] = round(ms.value, 3)
+    return res
+
+
+# the read patterns of lds.hip, in its kernel order
+LDS_KINDS = ("pitch 68 dwords", "pitch 76 dwords", "pitch 72 dwords", "pitch 64, chunk ^ (row % 8)",
+             "pitch 64", "pitch 64, chunk ^ ((row / 2) % 8)")
+
+
+def lds_times(iters: int = 2000) -> dict:
+    """ms of each LDS read pattern of LDS_KINDS (16 ds_read_b128 per trip)."""
+    import torch
+    L = lib()
+    out = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for k, name in enumerate(LDS_KINDS):
+        ms = ctypes.c_float()
+        if L.cgprobe_lds(k, iters, out.data_ptr(), s, ctypes.byref(ms)) != 0:
+            raise RuntimeError(f"cgprobe_lds({k}) failed")
         res[name] = round(ms.value, 3)
     return res

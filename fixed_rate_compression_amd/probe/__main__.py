@@ -1,16 +1,22 @@
 """python3 -m fixed_rate_compression_amd.probe issue: print the instruction-issue
 rates and the matrix-core / VALU overlap times of issue.hip (one line each).
 python3 -m fixed_rate_compression_amd.probe stream: print the streaming
-kernels' HBM rates on a 4.29 GB tensor (stream.hip, every mode)."""
+kernels' HBM rates on a 4.29 GB tensor (stream.hip, every mode).
+python3 -m fixed_rate_compression_amd.probe lds: print the times of the LDS
+matrix-operand read patterns (lds.hip)."""
 import sys
 
 from fixed_rate_compression_amd import probe
 
 
 def main() -> int:
-    if len(sys.argv) < 2 or sys.argv[1] not in ("issue", "stream"):
+    if len(sys.argv) < 2 or sys.argv[1] not in ("issue", "stream", "lds"):
         print(__doc__)
         return 2
+    if sys.argv[1] == "lds":
+        for name, ms in probe.lds_times().items():
+            print(f"{name:36s} {ms:.3f} ms", flush=True)
+        return 0
     if sys.argv[1] == "stream":
         import torch
         kv = torch.zeros(1 << 31, dtype=torch.bfloat16, device="cuda")
