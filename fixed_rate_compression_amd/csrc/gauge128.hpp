@@ -10,11 +10,14 @@
 // when it is not already a bf16 value, so that
 //   X G^T ~= X_hi G_hi^T + X_hi G_lo^T + X_lo G_hi^T
 // carries ~16 significand bits of every product (the dropped X_lo G_lo term
-// is ~2^-16 of the smallest kept one).  Decoders take these three passes (or
-// two, for exact integer codes).  The forward gauge of bf16 tiles (the
-// encoders and the bf16 gauge routine) takes one: X is exact in bf16 and
-// the codes are decided on bf16-precision data anyway, so X G_hi^T, within
-// 2^-9 sum |G||X| of X G^T, is the gauged field (HI_ONLY).
+// is ~2^-16 of the smallest kept one).  The zfp decoder takes these three
+// passes and the bf16 inverse gauge routine two (its rows are bf16 values).
+// The forward gauge of bf16 tiles (the encoders and the bf16 gauge routine)
+// takes one: X is exact in bf16 and the codes are decided on bf16-precision
+// data anyway, so X G_hi^T, within 2^-9 sum |G||X| of X G^T, is the gauged
+// field (HI_ONLY).  The quantizer decoders take one fp16 pass
+// (gauge128_f16_rows): their codes are exact in fp16, or their rows are
+// scaled by a power of two into fp16's range.
 //
 // Work split: wave w owns output channels [32w, 32w+32) (two 16-wide column
 // tiles) for all 64 rows; its B fragments (G_hi, G_lo: 2 column tiles x 4

@@ -14,12 +14,13 @@
 //
 // Work layout: a workgroup (256 threads) processes 64-token tiles of one
 // field (a chunk of consecutive tiles when the full-head gauge is used, so
-// its 64 KB matrix is loaded once).  The full-head gauge runs on the bf16
-// matrix cores in split precision with bf16 storage (kDense), and as fp32
+// its 64 KB matrix is loaded once).  With bf16 storage the full-head gauge
+// runs on the matrix cores in reduced precision (kDense: one bf16 pass
+// forward, one fp16 pass inverse, gauge128.hpp); with fp32 storage as fp32
 // matrix-core fmaf chains (TileGauge, the reading order of the smaller
-// groups) with fp32 storage.  After the gauge, thread i owns the 32
-// values (row i/4, channels 32 (i%4) .. +31): exactly `bits` 32-bit words of
-// codes, stored with one vector store, so a wave writes a contiguous span.
+// groups).  After the gauge, thread i owns the 32 values (row i/4, channels
+// 32 (i%4) .. +31): exactly `bits` 32-bit words of codes, stored with one
+// vector store, so a wave writes a contiguous span.
 #pragma once
 
 #include <float.h>
@@ -35,7 +36,7 @@ namespace cgq {
 
 using namespace cgk;
 
-// full-head gauge with bf16 storage: split-precision bf16 matrix-core path
+// full-head gauge with bf16 storage: reduced-precision matrix-core path
 template <int G, bool BF16>
 constexpr bool kDense = G == 128 && BF16;
 
@@ -513,7 +514,8 @@ __global__ __launch_bounds__(NT) void k_bu_encode(const void *__restrict__ kv,
 }
 
 // the same with three waves per SIMD (launched for the full-head gauge with
-// bf16 storage, which fits in 168 VGPRs; other instances would spill)
+// bf16 storage below 8-bit codes, which fits in 168 VGPRs; other instances
+// would spill)
 template <int BITS, bool BF16, int G>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void k_bu_encode_w3(const void *__restrict__ kv,
                                                   const float *__restrict__ gauges,
@@ -772,7 +774,8 @@ __global__ __launch_bounds__(NT) void k_kivi_encode(const void *__restrict__ kv,
 }
 
 // the same with three waves per SIMD (launched for the full-head gauge with
-// bf16 storage, which fits in 168 VGPRs; other instances would spill)
+// bf16 storage below 8-bit codes, which fits in 168 VGPRs; other instances
+// would spill)
 template <int BITS, bool BF16, int G>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void k_kivi_encode_w3(const void *__restrict__ kv,
                                                     const float *__restrict__ gauges,
@@ -909,7 +912,8 @@ __global__ __launch_bounds__(NT) void k_kivi_decode(const uint8_t *__restrict__ 
 }
 
 // the same with three waves per SIMD (launched for the full-head gauge with
-// bf16 storage, which fits in 168 VGPRs; other instances would spill)
+// bf16 storage below 8-bit codes, which fits in 168 VGPRs; other instances
+// would spill)
 template <int BITS, bool BF16, int G>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void k_kivi_decode_w3(const uint8_t *__restrict__ payload,
                                                     const float *__restrict__ meta,
