@@ -222,6 +222,58 @@ def test_dense_gauge_staged(backend, bits, blk, res):
     assert worst_o <= 1e-2
 
 
+@pytest.mark.parametrize("backend,bits,blk,res,T", [
+    (cg.CG_BACKEND_KIVI, 2, 32, 128, 1376),          # last tile 32 rows; the tail spans two tiles
+    (cg.CG_BACKEND_BLOCK_UNIFORM, 3, 32, 0, 1376),   # last tile 32 rows
+    (cg.CG_BACKEND_BLOCK_UNIFORM, 4, 16, 0, 1360),   # last tile 16 rows, 16-token blocks
+])
+def test_dense_gauge_ragged_tiles(backend, bits, blk, res, T):
+    """Full-head gauge with bf16 storage on fields whose last 64-row tile is
+    partial: the decoders' staged row stores must write exactly the valid
+    rows.  Codes, metadata and tail bit-exact on the library's gauged field,
+    decoded rows within the dense inverse bound; for the block-uniform
+    backend also a decode of a row range that starts and ends inside tiles,
+    bit-identical to the same rows of the whole-field decode and leaving the
+    other rows untouched."""
+    t = torch()
+    L, KV, B, H = 1, 2, 1, 2
+    x = kv_cpu(80 + bits, L, KV, B, H, T, T, 0.95, 4, bf16=True)
+    G = gauges_for(90 + bits, L, KV, H, 128)
+    codec = cg.make_codec(backend, bits, blk, res)
+    pay, meta, out, xg = run(x, G, 128, codec, L, KV, B, H, T, True)
+    for f in range(n_fields(L, KV, B, H)):
+        Gf = gauge_of_field(G, f, KV, B, H).astype(np.float64)
+        check_dense_forward(xg[f], oracle.to_f32(x[f]), Gf, f)
+        if backend == cg.CG_BACKEND_BLOCK_UNIFORM:
+            p_ref, m_ref = oracle.bu_encode_field(xg[f], blk, bits)
+            per = T * D * bits // 8
+            assert np.array_equal(pay[f * per:(f + 1) * per], p_ref), f
+            assert np.array_equal(meta.reshape(-1, T // blk, 2)[f].view(np.uint32), m_ref.view(np.uint32)), f
+            deq = oracle.bu_decode_field(p_ref, m_ref, T, D, blk, bits)
+            rmin = np.repeat(m_ref.reshape(-1, 2)[:, 0], blk)
+        else:
+            kind = (f // (B * H)) % KV
+            p_ref, m_ref, tail = oracle.kivi_encode_field(xg[f], kind, 32, bits, res)
+            pq, pt, mf = kivi_split(pay, meta, f, T, res, bits, 2)
+            assert np.array_equal(pq, p_ref), f
+            assert np.array_equal(mf.view(np.uint32), m_ref.view(np.uint32)), f
+            tail_st = oracle.f32_to_bf16(tail)
+            assert np.array_equal(pt, tail_st.view(np.uint8).reshape(-1)), f
+            deq = oracle.kivi_decode_field(p_ref, m_ref, oracle.to_f32(tail_st), T, D, kind, 32, bits, res)
+            rmin = None
+        check_dense_inverse(out[f], deq, Gf, f, rmin)
+    if backend == cg.CG_BACKEND_BLOCK_UNIFORM:
+        t0, nt = 96, T - 96 - 2 * blk                 # starts and ends inside 64-row tiles
+        shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_BF16)
+        sub = t.zeros((n_fields(L, KV, B, H), T, D), dtype=t.bfloat16, device="cuda")
+        cg.cg_decode(shape, to_dev(pay), to_dev(meta), cg.make_gauge(128, to_dev(np.ascontiguousarray(G))),
+                     codec, t0, nt, sub)
+        t.cuda.synchronize()
+        got = to_host(sub)
+        assert np.array_equal(got[:, t0:t0 + nt], out[:, t0:t0 + nt])
+        assert not got[:, :t0].any() and not got[:, t0 + nt:].any()
+
+
 @pytest.mark.parametrize("backend,bits,blk,res", [
     (cg.CG_BACKEND_BLOCK_UNIFORM, 3, 64, 0),
     (cg.CG_BACKEND_BLOCK_UNIFORM, 8, 32, 0),
