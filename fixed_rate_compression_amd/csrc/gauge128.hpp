@@ -225,20 +225,6 @@ __device__ __forceinline__ void scaled_f16_32(uint16_t *sh, float *rsc, int t, i
   put_f16_32(sh, t, j, h);
 }
 
-// the 32 values of row t, channels 32 j .. 32 j + 31 -> split tiles
-__device__ __forceinline__ void split32(uint16_t *sh, uint16_t *sl, int t, int j, const float (&v)[32]) {
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    uint4 h, l;
-    split_pair(v[8 * q], v[8 * q + 1], h.x, l.x);
-    split_pair(v[8 * q + 2], v[8 * q + 3], h.y, l.y);
-    split_pair(v[8 * q + 4], v[8 * q + 5], h.z, l.z);
-    split_pair(v[8 * q + 6], v[8 * q + 7], h.w, l.w);
-    *(uint4 *)(sh + t * HP + 32 * j + 8 * q) = h;
-    *(uint4 *)(sl + t * HP + 32 * j + 8 * q) = l;
-  }
-}
-
 // X G^T (forward fragments) or X G (inverse fragments) of the split tile into
 // the fp32 tile xs, which may overlay sh/sl.  EXACT: every tile value is a
 // bf16 number (no lo part: two passes instead of three).  HI_ONLY (with
