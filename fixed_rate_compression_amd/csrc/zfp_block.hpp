@@ -190,6 +190,11 @@ __host__ __device__ __forceinline__ int clz32(uint32_t x) {  // x != 0
   return __builtin_clz(x);
 }
 
+// index of the lowest set bit of x; all ones for x = 0 (one v_ffbl_b32)
+__host__ __device__ __forceinline__ uint32_t ctz32_or_ones(uint32_t x) {
+  return x ? (uint32_t)__builtin_ctz(x) : ~0u;
+}
+
 // number of significant bits of x (0 for x = 0)
 __host__ __device__ __forceinline__ int bitlen32(uint32_t x) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -300,25 +305,27 @@ __host__ __device__ __forceinline__ void encode_plane(uint64_t (&acc)[Rate<R>::k
                                                       int &pos, int &n,
                                                       const uint16_t *__restrict__ dbl) {
   const uint32_t rest = w >> n;
-  const int hb1 = 32 - clz32(w | 1u);   // highest set bit + 1 (1 when w <= 1)
-  // scanned positions n .. min(hb, 14); when rest == 0 the code below is
-  // replaced by the failed test
+  const int hb1 = bitlen32(w);          // highest set bit + 1 (0 when w = 0)
+  // scanned positions n .. min(hb, 14) (none when rest == 0: then hb1 <= n)
   const int L = max(min(hb1, 15), n) - n;
   const uint32_t S = rest & ((1u << L) - 1u);
   const uint32_t lo = S & 0xFFu, hi = S >> 8;
-  const int pclo = __builtin_popcount(lo), pc = pclo + __builtin_popcount(hi);
+  const int pclo = __builtin_popcount(lo), pc = __builtin_popcount(S);
   const uint32_t D = (uint32_t)dbl[lo] | ((uint32_t)dbl[hi] << (8 + pclo));
-  uint32_t code = 1u | (D << 1);
-  if (hb1 <= 15) code &= ~(1u << (L + pc));
+  // the flag after the highest one (a 1 from the table) becomes the failed
+  // test 0, unless that one is coefficient 15, whose 1 is implied; with
+  // rest == 0 and n < 16 this leaves the single failed test 0 (L = pc = 0)
+  const uint32_t last = ((w >> 15) & 1u) ^ 1u;
+  uint32_t code = (1u | (D << 1)) ^ (last << (L + pc));
   int len = 1 + L + pc;
-  if (rest == 0) {
+  if (n >= 16) {                        // every coefficient significant: no group part
     code = 0u;
-    len = n < 16 ? 1 : 0;
+    len = 0;
   }
   const uint64_t full = (uint64_t)(w & ((1u << n) - 1u)) | ((uint64_t)code << n);
   put64<R>(acc, pos, full);
   pos += n + len;
-  n = rest ? hb1 : n;
+  n = max(n, hb1);                      // hb1 > n exactly when rest != 0
 }
 
 // Encode 16 fp32 values v[4j + i] (j = token row, i = channel) at rate R.
@@ -433,15 +440,18 @@ __host__ __device__ __forceinline__ uint32_t group_part(uint32_t W, int &pos, in
   const uint32_t G1 = (W << 1) | 1u;
   const uint32_t odd_starts = G1 & ~(G1 << 1) & kc.odd;
   const uint32_t D = G1 & (kc.even ^ (G1 & ~(G1 + odd_starts)));
-  const uint32_t fails = D & ~W;                              // tests that read 0
-  const uint32_t ef = fails ? (uint32_t)ctz32(fails) : 32u;  // first failed test
+  const uint32_t fails = D & ~W;              // tests that read 0
+  const uint32_t ef = ctz32_or_ones(fails);   // first failed test (all ones: none)
   const uint32_t room = (uint32_t)(LIMIT - pos);              // >= 1
   const uint32_t m = 15u - (uint32_t)n;                       // index of coefficient 15
-  // a plane's group part never spans more than 2m+1 bits
+  // E: where the part ends unless the scan reaches coefficient 15 first.  A
+  // part ended by a failed test or by the budget spans at most 2m + 1 bits
+  // (one flag per found 1 plus the first test, at most m scanned bits), so
+  // where 2m + 2 is below both ef and room the scan has reached index 15.
   uint32_t E = ef < room ? ef : room;
   E = E < 2u * m + 2u ? E : 2u * m + 2u;                      // <= 32
-  const uint32_t below = (uint32_t)~(~0ull << E);            // E <= 32
-  uint32_t term = (D >> 1) & below;     // found 1s before E
+  const uint32_t above = (uint32_t)(~0ull << E);             // window bits E.. (E <= 32)
+  uint32_t term = (D >> 1) & ~above;    // found 1s before E
   uint32_t y = 0u, bias = 1u;
   while (term) {                        // two newly significant coefficients per step
     const uint32_t low1 = term & (0u - term);
@@ -451,19 +461,21 @@ __host__ __device__ __forceinline__ uint32_t group_part(uint32_t W, int &pos, in
     term = rest ^ low2;
     bias += 2u;
   }
-  const uint32_t cnt = (uint32_t)__builtin_popcount(below & ~D);        // bits scanned before E
+  const uint32_t cnt = (uint32_t)__builtin_popcount(~(above | D));   // bits scanned before E
   // three ways the part ends, selected without branches (lanes diverge here):
-  //  cap    the scan reaches coefficient 15, whose 1 is implicit;
-  //  fail   a failed group test at ef;
-  //  budget the budget ends at room (<= ef <= 32); inside a scan the scanned
-  //         index is set
+  //  cap    the scan reaches coefficient 15 (more than m bits scanned before
+  //         E), whose 1 is implicit;
+  //  fail   a failed group test: E = ef, a flag position;
+  //  budget the budget ends: E = room; inside a scan (E not a flag position)
+  //         the scanned index is set.
+  // Without a cap the part ends at E, and the bit at E is a flag exactly when
+  // the scan is not inside a run, so one test covers both other ends.
   const bool cap = cnt > m;
-  const bool fail = ef < room;
   const uint32_t ycap = (y & (0x7FFFu >> n)) | (0x8000u >> n);   // indices below m, and m
-  const uint32_t inscan = ((D >> (room & 31u)) & 1u) ^ 1u;   // room is not a flag position
-  const uint32_t ybud = y | (inscan << (cnt & 31u));
-  y = cap ? ycap : (fail ? y : ybud);
-  const uint32_t used = cap ? m + (uint32_t)__builtin_popcount(ycap) : (fail ? ef + 1u : room);
+  const uint32_t inscan = ((D >> (E & 31u)) & 1u) ^ 1u;          // (E = 32 only with a cap)
+  const uint32_t yend = y | (inscan << (cnt & 31u));
+  y = cap ? ycap : yend;
+  const uint32_t used = cap ? m + (uint32_t)__builtin_popcount(ycap) : E + (ef < room ? 1u : 0u);
   pos += (int)used;
   n += bitlen32(y);                     // every index up to the last new one is now verbatim
   return y;
