@@ -190,6 +190,15 @@ __host__ __device__ __forceinline__ int clz32(uint32_t x) {  // x != 0
   return __builtin_clz(x);
 }
 
+// bits [off, off + width) of x (off + width <= 32; one v_bfe_u32)
+__host__ __device__ __forceinline__ uint32_t bits32(uint32_t x, uint32_t off, uint32_t width) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ubfe(x, off, width);
+#else
+  return width ? (x >> off) & (~0u >> (32u - width)) : 0u;
+#endif
+}
+
 // index of the lowest set bit of x; all ones for x = 0 (one v_ffbl_b32)
 __host__ __device__ __forceinline__ uint32_t ctz32_or_ones(uint32_t x) {
   return x ? (uint32_t)__builtin_ctz(x) : ~0u;
@@ -304,28 +313,27 @@ template <int R>
 __host__ __device__ __forceinline__ void encode_plane(uint64_t (&acc)[Rate<R>::kAcc], uint32_t w,
                                                       int &pos, int &n,
                                                       const uint16_t *__restrict__ dbl) {
-  const uint32_t rest = w >> n;
   const int hb1 = bitlen32(w);          // highest set bit + 1 (0 when w = 0)
-  // scanned positions n .. min(hb, 14) (none when rest == 0: then hb1 <= n)
+  // scanned positions n .. min(hb, 14) (none when w >> n == 0: then hb1 <= n)
   const int L = max(min(hb1, 15), n) - n;
-  const uint32_t S = rest & ((1u << L) - 1u);
+  const uint32_t S = bits32(w, (uint32_t)n, (uint32_t)L);
   const uint32_t lo = S & 0xFFu, hi = S >> 8;
-  const int pclo = __builtin_popcount(lo), pc = __builtin_popcount(S);
+  const int pclo = __builtin_popcount(lo);
+  const int Lpc = L + __builtin_popcount(S);
   const uint32_t D = (uint32_t)dbl[lo] | ((uint32_t)dbl[hi] << (8 + pclo));
   // the flag after the highest one (a 1 from the table) becomes the failed
   // test 0, unless that one is coefficient 15, whose 1 is implied; with
-  // rest == 0 and n < 16 this leaves the single failed test 0 (L = pc = 0)
+  // w >> n == 0 and n < 16 this leaves the single failed test 0 (L = pc = 0)
   const uint32_t last = ((w >> 15) & 1u) ^ 1u;
-  uint32_t code = (1u | (D << 1)) ^ (last << (L + pc));
-  int len = 1 + L + pc;
-  if (n >= 16) {                        // every coefficient significant: no group part
-    code = 0u;
-    len = 0;
-  }
+  uint32_t code = (1u | (D << 1)) ^ (last << Lpc);
+  // with all 16 coefficients significant (n = 16, where L = pc = 0) the plane
+  // has no group part: no code and a length of 0
+  const bool part = n < 16;
+  if (!part) code = 0u;
   const uint64_t full = (uint64_t)(w & ((1u << n) - 1u)) | ((uint64_t)code << n);
   put64<R>(acc, pos, full);
-  pos += n + len;
-  n = max(n, hb1);                      // hb1 > n exactly when rest != 0
+  pos += n + Lpc + (part ? 1 : 0);
+  n = max(n, hb1);                      // hb1 > n exactly when w >> n != 0
 }
 
 // Encode 16 fp32 values v[4j + i] (j = token row, i = channel) at rate R.
@@ -432,9 +440,9 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
 // (the carry clears exactly the run).  D (bit t = flag at window bit t) marks
 // the tests; the k-th found 1 (k from 0) at window bit t is coefficient
 // n + t - (k + 1).  Returns the new coefficients' bits relative to n;
-// advances pos and n.
+// advances pos.
 template <int R>
-__host__ __device__ __forceinline__ uint32_t group_part(uint32_t W, int &pos, int &n,
+__host__ __device__ __forceinline__ uint32_t group_part(uint32_t W, int &pos, const int n,
                                                     const ParseConsts &kc) {
   constexpr int LIMIT = Rate<R>::kBits;
   const uint32_t G1 = (W << 1) | 1u;
@@ -477,7 +485,6 @@ __host__ __device__ __forceinline__ uint32_t group_part(uint32_t W, int &pos, in
   y = cap ? ycap : yend;
   const uint32_t used = cap ? m + (uint32_t)__builtin_popcount(ycap) : E + (ef < room ? 1u : 0u);
   pos += (int)used;
-  n += bitlen32(y);                     // every index up to the last new one is now verbatim
   return y;
 }
 
@@ -491,7 +498,11 @@ __host__ __device__ __forceinline__ uint32_t decode_plane(const uint64_t (&acc)[
   uint32_t x = W0 & ((1u << n) - 1u);   // verbatim bits (n <= 16)
   const int n0 = n;
   pos += n0;
-  if (n0 < 16 && pos < LIMIT) x |= group_part<R>(W0 >> n0, pos, n, kc) << n0;
+  if (n0 < 16 && pos < LIMIT) {
+    const uint32_t y = group_part<R>(W0 >> n0, pos, n0, kc) << n0;
+    x |= y;
+    n = max(n0, bitlen32(y));  // every index up to the last new one is now verbatim
+  }
   return x;
 }
 
