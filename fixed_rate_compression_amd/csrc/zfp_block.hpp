@@ -445,7 +445,12 @@ template <int R>
 __host__ __device__ __forceinline__ uint32_t group_part(uint32_t W, int &pos, const int n,
                                                     const ParseConsts &kc) {
   constexpr int LIMIT = Rate<R>::kBits;
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t G1;
+  asm("v_lshl_or_b32 %0, %1, 1, 1" : "=v"(G1) : "v"(W));
+#else
   const uint32_t G1 = (W << 1) | 1u;
+#endif
   const uint32_t odd_starts = G1 & ~(G1 << 1) & kc.odd;
   const uint32_t D = G1 & (kc.even ^ (G1 & ~(G1 + odd_starts)));
   const uint32_t fails = D & ~W;              // tests that read 0
@@ -460,15 +465,17 @@ __host__ __device__ __forceinline__ uint32_t group_part(uint32_t W, int &pos, co
   E = E < 2u * m + 2u ? E : 2u * m + 2u;                      // <= 32
   const uint32_t above = (uint32_t)(~0ull << E);             // window bits E.. (E <= 32)
   uint32_t term = (D >> 1) & ~above;    // found 1s before E
+  // two newly significant coefficients per step; a step with no found 1
+  // left adds nothing, so the first one runs unconditionally
   uint32_t y = 0u, bias = 1u;
-  while (term) {                        // two newly significant coefficients per step
+  do {
     const uint32_t low1 = term & (0u - term);
     const uint32_t rest = term ^ low1;
     const uint32_t low2 = rest & (0u - rest);   // 0 when only one was left
     y |= (low1 >> bias) | (low2 >> (bias + 1u));
     term = rest ^ low2;
     bias += 2u;
-  }
+  } while (term);
   const uint32_t cnt = (uint32_t)__builtin_popcount(~(above | D));   // bits scanned before E
   // three ways the part ends, selected without branches (lanes diverge here):
   //  cap    the scan reaches coefficient 15 (more than m bits scanned before
@@ -499,9 +506,10 @@ __host__ __device__ __forceinline__ uint32_t decode_plane(const uint64_t (&acc)[
   const int n0 = n;
   pos += n0;
   if (n0 < 16 && pos < LIMIT) {
-    const uint32_t y = group_part<R>(W0 >> n0, pos, n0, kc) << n0;
-    x |= y;
-    n = max(n0, bitlen32(y));  // every index up to the last new one is now verbatim
+    x |= group_part<R>(W0 >> n0, pos, n0, kc) << n0;
+    // every index up to the last new one is now verbatim (the verbatim bits
+    // of x lie below n0)
+    n = max(n0, bitlen32(x));
   }
   return x;
 }
