@@ -263,6 +263,17 @@ __host__ __device__ constexpr uint16_t dbl8_entry(uint32_t s) {
   return (uint16_t)out;
 }
 
+// The encoder's lookup tables, kPlaneTableHalves 16-bit words at a 4-byte
+// aligned address: the 8-bit expansion (256 halfwords), then, as 256 32-bit
+// words, the same shifted left by one with bit 0 set (the group test that
+// opens a plane's group part precedes the expanded low byte).
+constexpr int kPlaneTableHalves = 256 + 2 * 256;
+
+__host__ __device__ __forceinline__ void plane_tables_entry(uint16_t *t, uint32_t i) {
+  t[i] = dbl8_entry(i);
+  ((uint32_t *)(t + 256))[i] = ((uint32_t)dbl8_entry(i) << 1) | 1u;
+}
+
 // 32 stream bits starting at `pos` (< 16R); bits past 16R read as 0
 template <int R>
 __host__ __device__ __forceinline__ uint32_t window(const uint64_t (&acc)[Rate<R>::kAcc],
@@ -308,24 +319,26 @@ __host__ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo,
 // every 1 among them followed by one more bit -- 1 if another one follows in
 // the plane, 0 after the last one (hb = highest set bit; a one at position 15
 // is implied and not sent).  The "1 after every 1" expansion comes from the
-// 256-entry table `dbl`.  Fixed cost whatever the plane's content.
+// tables `tab` (plane_tables_entry); `last` = 1 when bit 15 of w is clear.
+// Fixed cost whatever the plane's content.
 template <int R>
 __host__ __device__ __forceinline__ void encode_plane(uint64_t (&acc)[Rate<R>::kAcc], uint32_t w,
-                                                      int &pos, int &n,
-                                                      const uint16_t *__restrict__ dbl) {
+                                                      uint32_t last, int &pos, int &n,
+                                                      const uint16_t *__restrict__ tab) {
   const int hb1 = bitlen32(w);          // highest set bit + 1 (0 when w = 0)
   // scanned positions n .. min(hb, 14) (none when w >> n == 0: then hb1 <= n)
-  const int L = max(min(hb1, 15), n) - n;
+  const int L = (int)__builtin_elementwise_sub_sat((uint32_t)min(hb1, 15), (uint32_t)n);
   const uint32_t S = bits32(w, (uint32_t)n, (uint32_t)L);
   const uint32_t lo = S & 0xFFu, hi = S >> 8;
   const int pclo = __builtin_popcount(lo);
   const int Lpc = L + __builtin_popcount(S);
-  const uint32_t D = (uint32_t)dbl[lo] | ((uint32_t)dbl[hi] << (8 + pclo));
+  // the opening test, then the expanded scan bits
+  const uint32_t D1 = ((const uint32_t *)(tab + 256))[lo] | ((uint32_t)tab[hi] << (9 + pclo));
   // the flag after the highest one (a 1 from the table) becomes the failed
-  // test 0, unless that one is coefficient 15, whose 1 is implied; with
-  // w >> n == 0 and n < 16 this leaves the single failed test 0 (L = pc = 0)
-  const uint32_t last = ((w >> 15) & 1u) ^ 1u;
-  uint32_t code = (1u | (D << 1)) ^ (last << Lpc);
+  // test 0 (`last` = 1), unless that one is coefficient 15 (bit 15 of w),
+  // whose 1 is implied; with w >> n == 0 and n < 16 this leaves the single
+  // failed test 0 (L = pc = 0)
+  uint32_t code = D1 ^ (last << Lpc);
   // with all 16 coefficients significant (n = 16, where L = pc = 0) the plane
   // has no group part: no code and a length of 0
   const bool part = n < 16;
@@ -342,11 +355,12 @@ __host__ __device__ __forceinline__ void encode_plane(uint64_t (&acc)[Rate<R>::k
 // has s > 24, planes 0..7 come from two 8x8 bit transposes of the words'
 // bytes at bits 31 - s .. 24 - s; the full 16x16 transposes are formed only
 // when some lane of the wave still has budget after 8 planes.  GENERAL = true
-// forces the full transposes (same stream).
+// forces the full transposes (same stream).  `tab`: kPlaneTableHalves words
+// filled by plane_tables_entry.
 template <int R, bool GENERAL = false>
 __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
                                                       uint64_t (&acc)[Rate<R>::kAcc],
-                                                      const uint16_t *__restrict__ dbl) {
+                                                      const uint16_t *__restrict__ tab) {
   constexpr int NA = Rate<R>::kAcc;
   constexpr int LIMIT = Rate<R>::kBits;
 #pragma unroll
@@ -410,7 +424,11 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
   }
 #pragma unroll
   for (int j = 0; j < 8; j++)           // planes 0..7 (no early exit: keeps the loop unrollable)
-    if (pos < LIMIT) encode_plane<R>(acc, (X[j >> 1] >> (16 * (j & 1))) & 0xFFFFu, pos, n, dbl);
+    if (pos < LIMIT) {
+      const uint32_t nX = ~X[j >> 1];   // shared by the word's two planes
+      encode_plane<R>(acc, (X[j >> 1] >> (16 * (j & 1))) & 0xFFFFu,
+                      (nX >> (16 * (j & 1) + 15)) & 1u, pos, n, tab);
+    }
   if (wave_any(pos < LIMIT)) {
     if (!transposed) {
 #pragma unroll
@@ -419,8 +437,10 @@ __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
     }
 #pragma unroll
     for (int j = 8; j < 32; j++)        // plane 31-j of the shifted words
-      if (pos < LIMIT)
-        encode_plane<R>(acc, j < 16 ? (u[15 - j] >> 16) : (u[31 - j] & 0xFFFFu), pos, n, dbl);
+      if (pos < LIMIT) {
+        const uint32_t w = j < 16 ? (u[15 - j] >> 16) : (u[31 - j] & 0xFFFFu);
+        encode_plane<R>(acc, w, ((w >> 15) & 1u) ^ 1u, pos, n, tab);
+      }
   }
   if (LIMIT % 64) acc[NA - 1] &= (~0ull) >> (64 - LIMIT % 64);
 }

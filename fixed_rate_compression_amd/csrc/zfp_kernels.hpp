@@ -188,14 +188,14 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
                                                    uint8_t *__restrict__ payload, TileArgs a) {
   __shared__ float xs[TILE_T * PITCH];
   __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
-  __shared__ uint16_t dbl[256];
+  __shared__ __align__(4) uint16_t tab[cgz::kPlaneTableHalves];
   const int64_t field = (int64_t)blockIdx.x / a.chunks;
   const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * a.chunk_tiles;
   const int tend = min(a.tiles, tile0 + a.chunk_tiles);
   const size_t esz = BF16 ? 2 : 4;
   TileGauge<G, false> tg;
   if constexpr (G != 0) tg.load(gauges + gauge_index(field, a.batch, a.heads) * D * G);
-  dbl[threadIdx.x] = cgz::dbl8_entry(threadIdx.x);
+  cgz::plane_tables_entry(tab, threadIdx.x);
   const uint8_t *src_f = (const uint8_t *)kv + (size_t)field * a.tcap * D * esz;
   auto rows = [&](int tile) { return (int)min((int64_t)TILE_T, a.nt - (int64_t)tile * TILE_T); };
   TileFetch<BF16> pre;
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
         v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
       }
       uint64_t acc[cgz::Rate<R>::kAcc];
-      cgz::encode_block<R>(v, acc, dbl);
+      cgz::encode_block<R>(v, acc, tab);
       if constexpr (BlockCode<R>::kDirect)
         store_block_code<R>(dst + (size_t)b * 2 * R, acc);
       else
@@ -381,14 +381,14 @@ __global__ __launch_bounds__(NT) void k_zfp_encode128(const void *__restrict__ k
                                                       uint8_t *__restrict__ payload, TileArgs a) {
   __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
   __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
-  __shared__ uint16_t dbl[256];
+  __shared__ __align__(4) uint16_t tab[cgz::kPlaneTableHalves];
   float *xs = (float *)lds;
   uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
   const int64_t field = (int64_t)blockIdx.x / a.chunks;
   const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * ZFP128_CHUNK;
   const int tend = min(a.tiles, tile0 + ZFP128_CHUNK);
   const size_t esz = BF16 ? 2 : 4;
-  dbl[threadIdx.x] = cgz::dbl8_entry(threadIdx.x);
+  cgz::plane_tables_entry(tab, threadIdx.x);
   G128Frags fr;
   load_g128<false>(gauges + gauge_index(field, a.batch, a.heads) * D * 128, fr);
   const uint8_t *src_f = (const uint8_t *)kv + (size_t)field * a.tcap * D * esz;
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(NT) void k_zfp_encode128(const void *__restrict__ k
         v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
       }
       uint64_t acc[cgz::Rate<R>::kAcc];
-      cgz::encode_block<R>(v, acc, dbl);
+      cgz::encode_block<R>(v, acc, tab);
       if constexpr (BlockCode<R>::kDirect)
         store_block_code<R>(dst + (size_t)b * 2 * R, acc);
       else

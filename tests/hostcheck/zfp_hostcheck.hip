@@ -5,19 +5,19 @@
 
 #include "../../fixed_rate_compression_amd/csrc/zfp_block.hpp"
 
-static uint16_t g_dbl[256];
-static bool g_dbl_ready = false;
+alignas(4) static uint16_t g_tab[cgz::kPlaneTableHalves];
+static bool g_tab_ready = false;
 
 template <int R, bool GENERAL>
 static void enc(const float *v, unsigned char *out) {
-  if (!g_dbl_ready) {
-    for (int i = 0; i < 256; i++) g_dbl[i] = cgz::dbl8_entry((uint32_t)i);
-    g_dbl_ready = true;
+  if (!g_tab_ready) {
+    for (uint32_t i = 0; i < 256; i++) cgz::plane_tables_entry(g_tab, i);
+    g_tab_ready = true;
   }
   float b[16];
   memcpy(b, v, sizeof b);
   uint64_t acc[cgz::Rate<R>::kAcc];
-  cgz::encode_block<R, GENERAL>(b, acc, g_dbl);
+  cgz::encode_block<R, GENERAL>(b, acc, g_tab);
   for (int i = 0; i < 2 * R; i++) out[i] = (unsigned char)(acc[i / 8] >> (8 * (i % 8)));
 }
 
