@@ -466,6 +466,8 @@ __host__ __device__ __forceinline__ uint32_t group_part(uint32_t W, int &pos, co
                                                     const ParseConsts &kc) {
   constexpr int LIMIT = Rate<R>::kBits;
 #if defined(__HIP_DEVICE_COMPILE__)
+  // one v_lshl_or_b32: left to itself the compiler keeps W << 1 and the or
+  // as two instructions (an ALU-only asm statement, no memory access)
   uint32_t G1;
   asm("v_lshl_or_b32 %0, %1, 1, 1" : "=v"(G1) : "v"(W));
 #else
