@@ -73,6 +73,30 @@ extern "C" int hc_decode_block_general(const unsigned char *in, int R, float *v)
   return -1;
 }
 
+// n consecutive blocks v[16 b + 4 j + i] into 2R bytes each (GENERAL != 0:
+// the 16x16 transposes forced)
+extern "C" int hc_encode_blocks(const float *v, long n, int R, int general, unsigned char *out) {
+  for (long b = 0; b < n; b++) {
+    const float *p = v + 16 * b;
+    unsigned char *o = out + b * 2 * R;
+    int rc = general ? hc_encode_block_general(p, R, o) : hc_encode_block(p, R, o);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+// n consecutive blocks of 2R bytes each into v[16 b + 4 j + i] (GENERAL != 0:
+// the 32-plane reconstruction forced)
+extern "C" int hc_decode_blocks(const unsigned char *in, long n, int R, int general, float *v) {
+  for (long b = 0; b < n; b++) {
+    const unsigned char *p = in + b * 2 * R;
+    float *o = v + 16 * b;
+    int rc = general ? hc_decode_block_general(p, R, o) : hc_decode_block(p, R, o);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
 template <int R>
 static int dec_lifted(const unsigned char *in, float *v) {
   uint64_t acc[cgz::Rate<R>::kAcc];

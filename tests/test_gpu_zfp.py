@@ -149,22 +149,29 @@ def test_edge_values_zero_constant_denormal_outlier():
 
 
 def test_random_payload_decodes_like_oracle():
+    """Arbitrary streams (every 16R-bit pattern is a valid fixed-rate block)
+    decode exactly like the oracle: uniform random bytes, and bits that are
+    mostly 0 (long runs of failed tests and many planes, the 32-plane path)
+    or mostly 1 (early caps at coefficient 15, all 16 coefficients
+    significant), 32768 blocks per rate and pattern."""
     import torch
-    L, KV, B, H, T = 1, 1, 1, 2, 64
+    L, KV, B, H, T = 1, 1, 1, 2, 2048
     rng = np.random.default_rng(0)
     for R in (2, 3, 4, 6, 8):
         shape = cg.make_shape(L, KV, B, H, T, T, D, cg.CG_DTYPE_F32)
         codec = cg.make_codec(cg.CG_BACKEND_ZFP, R)
-        raw = rng.integers(0, 256, 2 * T * D * R // 8).astype(np.uint8)
-        pay = torch.from_numpy(raw).cuda()
-        out = torch.zeros((2, T, D), dtype=torch.float32, device="cuda")
-        cg.cg_decode(shape, pay, None, cg.make_gauge(0), codec, 0, T, out)
-        torch.cuda.synchronize()
-        got = to_host(out)
-        per = T * D * R // 8
-        for f in range(2):
-            ref = oracle.zfp_decode_field(raw[f * per:(f + 1) * per], T, D, R)
-            assert np.array_equal(got[f].view(np.uint32), ref.view(np.uint32))
+        nbytes = 2 * T * D * R // 8
+        for p_one in (0.5, 0.15, 0.85):
+            raw = np.packbits(rng.random(8 * nbytes) < p_one, bitorder="little")
+            pay = torch.from_numpy(raw).cuda()
+            out = torch.zeros((2, T, D), dtype=torch.float32, device="cuda")
+            cg.cg_decode(shape, pay, None, cg.make_gauge(0), codec, 0, T, out)
+            torch.cuda.synchronize()
+            got = to_host(out)
+            per = T * D * R // 8
+            for f in range(2):
+                ref = oracle.zfp_decode_field(raw[f * per:(f + 1) * per], T, D, R)
+                assert np.array_equal(got[f].view(np.uint32), ref.view(np.uint32)), (R, p_one, f)
 
 
 def test_gauge_apply_and_none_backend_bit_exact():

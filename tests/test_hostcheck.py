@@ -28,6 +28,10 @@ def hc():
     L.hc_decode_block_general.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.hc_decode_block_lifted.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     L.hc_lift_matrix.argtypes = [ctypes.c_void_p]
+    L.hc_decode_blocks.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    L.hc_encode_blocks.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
     return L
 
 
@@ -93,6 +97,48 @@ def dec_lifted(L, b, R):
     applied = L.hc_decode_block_lifted(b.ctypes.data, R, o.ctypes.data)
     assert applied in (0, 1)
     return o if applied else None
+
+
+@pytest.mark.parametrize("R", RATES)
+def test_biased_random_fields(hc, R):
+    """Whole random fields (4096 blocks each) decode like the oracle's field
+    decoder: uniform bits, mostly-0 bits (long runs of failed tests, many
+    planes) and mostly-1 bits (early caps at coefficient 15, all sixteen
+    coefficients significant), with the kernels' reconstruction choice and
+    with the 32-plane one forced."""
+    rng = np.random.default_rng(700 + R)
+    T = 512
+    nb = T // 4 * 32
+    for p_one in (0.5, 0.15, 0.85):
+        raw = np.packbits(rng.random(8 * nb * 2 * R) < p_one, bitorder="little")
+        ref = oracle.zfp_decode_field(raw, T, 128, R)
+        for general in (0, 1):
+            v = np.zeros(16 * nb, np.float32)
+            assert hc.hc_decode_blocks(raw.ctypes.data, nb, R, general, v.ctypes.data) == 0
+            got = v.reshape(T // 4, 32, 4, 4).transpose(0, 2, 1, 3).reshape(T, 128)
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (R, p_one, general)
+
+
+@pytest.mark.parametrize("R", RATES)
+def test_mixed_value_fields_encode(hc, R):
+    """Whole fields (4096 blocks each) encode like the oracle's field
+    encoder, with the kernels' plane-word path and with the 16x16
+    transposes forced: Gaussian values under lognormal channel scales with
+    sparse zeros, subnormal rows and rows near the top of the fp32 range."""
+    rng = np.random.default_rng(900 + R)
+    T = 512
+    x = rng.standard_normal((T, 128)) * np.exp(3 * rng.standard_normal(128))
+    x[rng.random((T, 128)) < 0.1] = 0.0
+    x[32:64] *= 1e-41
+    x[96:128] = x[96:128] / np.max(np.abs(x[96:128])) * 3e38
+    x = x.astype(np.float32)
+    ref = oracle.zfp_encode_field(x, R)
+    v = np.ascontiguousarray(x.reshape(T // 4, 4, 32, 4).transpose(0, 2, 1, 3))
+    nb = T // 4 * 32
+    for general in (0, 1):
+        out = np.zeros(nb * 2 * R, np.uint8)
+        assert hc.hc_encode_blocks(v.ctypes.data, nb, R, general, out.ctypes.data) == 0
+        assert np.array_equal(out, ref), (R, general)
 
 
 def test_lift_matrix_inverts_the_forward_transform(hc):
