@@ -13,7 +13,7 @@ static uint32_t rnd() { rs ^= rs << 13; rs ^= rs >> 7; rs ^= rs << 17; return (u
 static float rndf() { return ((float)(rnd() & 0xFFFFFF) / 8388608.0f) - 1.0f; }
 
 template <int R>
-static void run(const uint16_t *dbl) {
+static void run(const uint16_t *tab) {
   constexpr int NA = cgz::Rate<R>::kAcc;
   for (int it = 0; it < 2000; it++) {
     float v[16], w[16];
@@ -24,7 +24,7 @@ static void run(const uint16_t *dbl) {
     }
     if (it % 7 == 0) for (int i = 0; i < 16; i++) v[i] = v[0];     // constant block
     uint64_t acc[NA];
-    cgz::encode_block<R>(v, acc, dbl);
+    cgz::encode_block<R>(v, acc, tab);
     cgz::decode_block<R>(acc, w);
     for (int a = 0; a < NA; a++) acc[a] = ((uint64_t)rnd() << 32) | rnd();   // corrupted stream
     constexpr int top = 16 * R - 64 * (NA - 1);
@@ -34,11 +34,12 @@ static void run(const uint16_t *dbl) {
 }
 
 int main() {
-  uint16_t *dbl = (uint16_t *)malloc(256 * sizeof(uint16_t));
-  for (int i = 0; i < 256; i++) dbl[i] = cgz::dbl8_entry((uint32_t)i);
-  run<1>(dbl); run<2>(dbl); run<3>(dbl); run<4>(dbl); run<5>(dbl); run<6>(dbl); run<7>(dbl);
-  run<8>(dbl); run<12>(dbl); run<16>(dbl);
-  free(dbl);
+  // the encoder's lookup tables, exactly as large as the coder reads them
+  uint16_t *tab = (uint16_t *)malloc(cgz::kPlaneTableHalves * sizeof(uint16_t));
+  for (uint32_t i = 0; i < 256; i++) cgz::plane_tables_entry(tab, i);
+  run<1>(tab); run<2>(tab); run<3>(tab); run<4>(tab); run<5>(tab); run<6>(tab); run<7>(tab);
+  run<8>(tab); run<12>(tab); run<16>(tab);
+  free(tab);
   printf("block driver done\n");
   return 0;
 }
