@@ -15,26 +15,28 @@
 //
 // GPU formulation (one block per lane, everything in VGPRs):
 //  * the leading all-zero planes cost one 0 bit each, so they are skipped in
-//    one step with a count-leading-zeros of the OR of the 16 words, and the
-//    words are shifted so that the first nonzero plane sits at bit 31;
-//  * all bit planes are produced at once by a 16x16 bit-matrix transpose
-//    applied to both 16-bit halves of the 16 words (4 butterfly stages);
-//  * a plane's verbatim part is one masked shift into the output, and its
-//    group-test/scan part costs one step per coefficient that becomes
-//    significant (each coefficient does so at most once per block);
+//    one step with a count-leading-zeros of the OR of the 16 words;
+//  * encoder: planes 0..7 come from two 8x8 bit transposes of the words'
+//    bytes (the full 16x16 transposes of both 16-bit halves of the shifted
+//    words only when some lane of the wave still has budget after 8
+//    planes); a plane's verbatim part is one masked shift into the output,
+//    and its group part a fixed-cost code from two table lookups (the "1
+//    after every 1" expansion of the scanned bits);
 //  * the block's bits live in ceil(16R/64) 64-bit accumulators; bits past
 //    16R are dropped, which equals stopping at the budget because the code
 //    of a block is a prefix code emitted strictly left to right;
 //  * decoder: a plane's verbatim bits and group part come from one 32-bit
 //    window; the group part's flag positions come from the runs of ones (a
 //    found coefficient's 1 is always followed by a flag, so within a run of
-//    ones counted from a data position, data and flag positions alternate);
+//    ones counted from a data position, data and flag positions alternate),
+//    and the newly significant coefficients are taken two per loop step;
 //    when no lane of the wave has budget left after 8 planes (the common case
 //    at 2-4 bits per value) the planes are turned into integers with two 8x8
 //    bit transposes and a byte-wise negabinary conversion instead of the full
 //    32-plane transpose.
 // The functions are __host__ __device__ so the same code can be checked on
-// the CPU; they use only portable integer operations.
+// the CPU: the device build uses a few AMDGPU builtins (and one ALU-only asm
+// statement) where the host build has the equivalent portable expression.
 #pragma once
 
 #include <hip/hip_runtime.h>
