@@ -148,6 +148,26 @@ def test_edge_values_zero_constant_denormal_outlier():
             check_against_oracle(x, G, g, R, L, KV, B, H, T, T, pay, out)
 
 
+@pytest.mark.parametrize("R", [2, 3, 4, 6, 8])
+def test_mixed_value_fields(R):
+    """Whole fields of mixed magnitudes through the fused kernels, bit-exact
+    streams and decoded rows against the oracle: Gaussian values under
+    lognormal channel scales with 10 % zeros, a band of subnormal-scale rows
+    and a band of rows near 1e37 (below fp32 overflow after any orthogonal
+    16-channel mix), fp32 storage at g = 0 and 16."""
+    L, KV, B, H, T = 1, 1, 1, 2, 512
+    rng = np.random.default_rng(1100 + R)
+    x = rng.standard_normal((2, T, D)) * np.exp(3 * rng.standard_normal((2, 1, D)))
+    x[rng.random((2, T, D)) < 0.1] = 0.0
+    x[:, 32:64] *= 1e-41
+    x[:, 96:128] = x[:, 96:128] / np.max(np.abs(x[:, 96:128])) * 1e37
+    x = x.astype(np.float32)
+    for g in (0, 16):
+        G = gauges_for(1200 + R, L, KV, H, g)
+        pay, out = run_zfp(x, G, g, R, L, KV, B, H, T, T, False)
+        check_against_oracle(x, G, g, R, L, KV, B, H, T, T, pay, out)
+
+
 def test_random_payload_decodes_like_oracle():
     """Arbitrary streams (every 16R-bit pattern is a valid fixed-rate block)
     decode exactly like the oracle: uniform random bytes, and bits that are
