@@ -265,15 +265,17 @@ __host__ __device__ constexpr uint16_t dbl8_entry(uint32_t s) {
   return (uint16_t)out;
 }
 
-// The encoder's lookup tables, kPlaneTableHalves 16-bit words at a 4-byte
-// aligned address: the 8-bit expansion (256 halfwords), then, as 256 32-bit
-// words, the same shifted left by one with bit 0 set (the group test that
-// opens a plane's group part precedes the expanded low byte).
-constexpr int kPlaneTableHalves = 256 + 2 * 256;
+// The encoder's lookup tables: the 8-bit expansion (for the high byte of
+// the scanned bits), and the same shifted left by one with bit 0 set (for
+// the low byte: the group test that opens a plane's group part precedes it).
+struct PlaneTables {
+  uint16_t hi[256];
+  uint32_t lo[256];
+};
 
-__host__ __device__ __forceinline__ void plane_tables_entry(uint16_t *t, uint32_t i) {
-  t[i] = dbl8_entry(i);
-  ((uint32_t *)(t + 256))[i] = ((uint32_t)dbl8_entry(i) << 1) | 1u;
+__host__ __device__ __forceinline__ void plane_tables_entry(PlaneTables &t, uint32_t i) {
+  t.hi[i] = dbl8_entry(i);
+  t.lo[i] = ((uint32_t)dbl8_entry(i) << 1) | 1u;
 }
 
 // 32 stream bits starting at `pos` (< 16R); bits past 16R read as 0
@@ -321,12 +323,13 @@ __host__ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo,
 // every 1 among them followed by one more bit -- 1 if another one follows in
 // the plane, 0 after the last one (hb = highest set bit; a one at position 15
 // is implied and not sent).  The "1 after every 1" expansion comes from the
-// tables `tab` (plane_tables_entry); `last` = 1 when bit 15 of w is clear.
+// tables `tab` (filled by plane_tables_entry); `last` = 1 when bit 15 of w
+// is clear.
 // Fixed cost whatever the plane's content.
 template <int R>
 __host__ __device__ __forceinline__ void encode_plane(uint64_t (&acc)[Rate<R>::kAcc], uint32_t w,
                                                       uint32_t last, int &pos, int &n,
-                                                      const uint16_t *__restrict__ tab) {
+                                                      const PlaneTables &tab) {
   const int hb1 = bitlen32(w);          // highest set bit + 1 (0 when w = 0)
   // scanned positions n .. min(hb, 14) (none when w >> n == 0: then hb1 <= n)
   const int L = (int)__builtin_elementwise_sub_sat((uint32_t)min(hb1, 15), (uint32_t)n);
@@ -335,7 +338,7 @@ __host__ __device__ __forceinline__ void encode_plane(uint64_t (&acc)[Rate<R>::k
   const int pclo = __builtin_popcount(lo);
   const int Lpc = L + __builtin_popcount(S);
   // the opening test, then the expanded scan bits
-  const uint32_t D1 = ((const uint32_t *)(tab + 256))[lo] | ((uint32_t)tab[hi] << (9 + pclo));
+  const uint32_t D1 = tab.lo[lo] | ((uint32_t)tab.hi[hi] << (9 + pclo));
   // the flag after the highest one (a 1 from the table) becomes the failed
   // test 0 (`last` = 1), unless that one is coefficient 15 (bit 15 of w),
   // whose 1 is implied; with w >> n == 0 and n < 16 this leaves the single
@@ -357,12 +360,12 @@ __host__ __device__ __forceinline__ void encode_plane(uint64_t (&acc)[Rate<R>::k
 // has s > 24, planes 0..7 come from two 8x8 bit transposes of the words'
 // bytes at bits 31 - s .. 24 - s; the full 16x16 transposes are formed only
 // when some lane of the wave still has budget after 8 planes.  GENERAL = true
-// forces the full transposes (same stream).  `tab`: kPlaneTableHalves words
-// filled by plane_tables_entry.
+// forces the full transposes (same stream).  `tab`: filled by
+// plane_tables_entry.
 template <int R, bool GENERAL = false>
 __host__ __device__ __forceinline__ void encode_block(const float (&v)[16],
                                                       uint64_t (&acc)[Rate<R>::kAcc],
-                                                      const uint16_t *__restrict__ tab) {
+                                                      const PlaneTables &tab) {
   constexpr int NA = Rate<R>::kAcc;
   constexpr int LIMIT = Rate<R>::kBits;
 #pragma unroll

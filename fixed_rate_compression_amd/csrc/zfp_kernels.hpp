@@ -188,7 +188,7 @@ __global__ __launch_bounds__(NT) void k_zfp_encode(const void *__restrict__ kv,
                                                    uint8_t *__restrict__ payload, TileArgs a) {
   __shared__ float xs[TILE_T * PITCH];
   __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
-  __shared__ __align__(4) uint16_t tab[cgz::kPlaneTableHalves];
+  __shared__ cgz::PlaneTables tab;
   const int64_t field = (int64_t)blockIdx.x / a.chunks;
   const int tile0 = (int)((int64_t)blockIdx.x % a.chunks) * a.chunk_tiles;
   const int tend = min(a.tiles, tile0 + a.chunk_tiles);
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(NT) void k_zfp_encode128(const void *__restrict__ k
                                                       uint8_t *__restrict__ payload, TileArgs a) {
   __shared__ __align__(16) unsigned char lds[LDS_TILE_BYTES];
   __shared__ uint32_t os[TILE_T / 4 * 32 * R / 2];
-  __shared__ __align__(4) uint16_t tab[cgz::kPlaneTableHalves];
+  __shared__ cgz::PlaneTables tab;
   float *xs = (float *)lds;
   uint16_t *sh = (uint16_t *)lds, *sl = sh + TILE_T * HP;
   const int64_t field = (int64_t)blockIdx.x / a.chunks;

@@ -5,7 +5,7 @@
 
 #include "../../fixed_rate_compression_amd/csrc/zfp_block.hpp"
 
-alignas(4) static uint16_t g_tab[cgz::kPlaneTableHalves];
+static cgz::PlaneTables g_tab;
 static bool g_tab_ready = false;
 
 template <int R, bool GENERAL>

@@ -13,7 +13,7 @@ static uint32_t rnd() { rs ^= rs << 13; rs ^= rs >> 7; rs ^= rs << 17; return (u
 static float rndf() { return ((float)(rnd() & 0xFFFFFF) / 8388608.0f) - 1.0f; }
 
 template <int R>
-static void run(const uint16_t *tab) {
+static void run(const cgz::PlaneTables &tab) {
   constexpr int NA = cgz::Rate<R>::kAcc;
   for (int it = 0; it < 2000; it++) {
     float v[16], w[16];
@@ -34,11 +34,11 @@ static void run(const uint16_t *tab) {
 }
 
 int main() {
-  // the encoder's lookup tables, exactly as large as the coder reads them
-  uint16_t *tab = (uint16_t *)malloc(cgz::kPlaneTableHalves * sizeof(uint16_t));
-  for (uint32_t i = 0; i < 256; i++) cgz::plane_tables_entry(tab, i);
-  run<1>(tab); run<2>(tab); run<3>(tab); run<4>(tab); run<5>(tab); run<6>(tab); run<7>(tab);
-  run<8>(tab); run<12>(tab); run<16>(tab);
+  // the encoder's lookup tables on the heap, exactly as large as they are
+  cgz::PlaneTables *tab = (cgz::PlaneTables *)malloc(sizeof(cgz::PlaneTables));
+  for (uint32_t i = 0; i < 256; i++) cgz::plane_tables_entry(*tab, i);
+  run<1>(*tab); run<2>(*tab); run<3>(*tab); run<4>(*tab); run<5>(*tab); run<6>(*tab); run<7>(*tab);
+  run<8>(*tab); run<12>(*tab); run<16>(*tab);
   free(tab);
   printf("block driver done\n");
   return 0;
