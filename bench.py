@@ -55,15 +55,15 @@ ISSUE_SLOTS_PEAK_GPS = 256 * 4 * 2.4 / 4
 # reports null once the hash of those sources differs.
 PMC_SOURCES = ("cg_launch.hpp", "cg_tile.hpp", "gauge128.hpp", "split_gauge.hpp", "zfp_block.hpp",
                "zfp_kernels.hpp", "zfp_r4.hip", "kernels_zfp.hip", "../build.py")
-PMC_TRAFFIC = {"sha256": "42fb25a4a0c4a9b9a0a77f2f87fbcbbab003d999fd7db691593756e85da9a14a",
+PMC_TRAFFIC = {"sha256": "9f8302f9bb9e1c6b5e30de7f1f08e219f0024d257bf2d4b2079f27e162212882",
                # FETCH_SIZE x 2 + WRITE_SIZE x 1 (KiB -> B), per launch
-               "k_zfp_encode": 5402698496, "k_zfp_decode": 5406537003,
+               "k_zfp_encode": 5402689621, "k_zfp_decode": 5406598272,
                # per launch (rocprofv3 --pmc, same sources): SQ_INSTS_VALU,
                # SQ_ACTIVE_INST_VALU2, SQ_VALU_MFMA_BUSY_CYCLES, SQ_VALU_MFMA_COEXEC_CYCLES
-               "valu_k_zfp_encode": 1204511363, "valu2_k_zfp_encode": 182014144,
+               "valu_k_zfp_encode": 1204511363, "valu2_k_zfp_encode": 182045782,
                "mfma_k_zfp_encode": 1073741824, "coexec_k_zfp_encode": 0,
-               "valu_k_zfp_decode": 1373576982, "valu2_k_zfp_decode": 280489615,
-               "mfma_k_zfp_decode": 335495456, "coexec_k_zfp_decode": 173611047}
+               "valu_k_zfp_decode": 1373576982, "valu2_k_zfp_decode": 280576980,
+               "mfma_k_zfp_decode": 335495456, "coexec_k_zfp_decode": 173685605}
 
 CFG = dict(layers=32, kv=2, batch=1, heads=8, tokens=32768, head_dim=128, g=16, rate=4,
            rho=0.95, outliers=4, seed=2)
